@@ -1,0 +1,508 @@
+"""Pins of the fp64 oracle against facts fixed outside the oracle itself.
+
+Each test checks the oracle against one of: a value the source pages print
+(golden files under tests/golden, each citing its page), a closed form, a
+library routine (torch's float8 dtypes, scipy), an invariant, or brute force
+on tiny inputs. The last group plants mistakes in the oracle and checks that
+a pin catches each one.
+"""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+from oracle import mx as omx
+from oracle import moe as omoe
+from workloads import LayerShape, make_inputs, f32_to_bf16_bits
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden_rows(name):
+    rows = []
+    with open(os.path.join(GOLD, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                rows.append(line.split())
+    return rows
+
+
+def _e2m1_table():
+    rows = _golden_rows("e2m1_codes.txt")
+    return np.array([float(r[2]) for r in sorted(rows, key=lambda r: int(r[0]))])
+
+
+# ----------------------------------------------------------------- formats
+
+def test_e2m1_decode_matches_golden_table():
+    want = _e2m1_table()
+    got = oracle.e2m1_decode(np.arange(16))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))  # code 8 is -0.0
+
+
+def test_e2m1_largest_magnitude_and_order():
+    mags = oracle.e2m1_decode(np.arange(8))
+    assert mags.max() == 6.0  # FLOAT4_E2M1_MAX
+    assert np.all(np.diff(mags) > 0)
+    assert np.array_equal(oracle.e2m1_decode(np.arange(8, 16)), -mags)
+
+
+def test_e8m0_decode_matches_torch_float8_e8m0fnu():
+    b = torch.arange(256, dtype=torch.uint8)
+    want = b.view(torch.float8_e8m0fnu).to(torch.float32).double().numpy()
+    got = oracle.e8m0_decode(np.arange(256))
+    assert np.isnan(got[255]) and np.isnan(want[255])
+    assert np.array_equal(got[:255], want[:255])
+
+
+def test_dequant_nibble_order_and_scale_groups():
+    # One row of K = 64: byte j holds elements 2j (low nibble) and 2j+1 (high).
+    packed = np.zeros((1, 32), np.uint8)
+    packed[0, 0] = 0x72      # element 0 = code 2 (1.0), element 1 = code 7 (6.0)
+    packed[0, 16] = 0xA5     # element 32 = code 5 (3.0), element 33 = code 10 (-1.0)
+    scales = np.array([[127, 129]], np.uint8)  # group 0 x1, group 1 x4
+    w = oracle.dequant_mxfp4(packed, scales)[0]
+    assert w[0] == 1.0 and w[1] == 6.0
+    assert w[32] == 12.0 and w[33] == -4.0
+    assert np.count_nonzero(w) == 4
+
+
+def test_mxfp4_values_exact_in_bf16():
+    # Every E2M1 value times 2^(e-127), e in [0, 252], is a bf16 number: the
+    # basis for decoding weights to bf16 without rounding.
+    vals = oracle.e2m1_decode(np.arange(16))[:, None] * np.ldexp(1.0, np.arange(0, 253) - 127)[None, :]
+    t = torch.from_numpy(vals.ravel())
+    assert torch.equal(t.to(torch.bfloat16).double(), t)
+
+
+def test_e4m3_decode_matches_torch():
+    b = torch.arange(256, dtype=torch.uint8)
+    want = b.view(torch.float8_e4m3fn).to(torch.float32).double().numpy()
+    got = oracle.e4m3_decode(np.arange(256))
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def test_e4m3_encode_matches_torch_cast():
+    rng = np.random.default_rng(7)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 40,
+        rng.standard_normal(5000) * 1e-2,          # subnormal range
+        oracle.e4m3_decode(np.arange(126)) * 1.0,  # exact codes
+        # midpoints between neighbouring codes: ties to even
+        0.5 * (oracle.e4m3_decode(np.arange(0, 125)) + oracle.e4m3_decode(np.arange(1, 126))),
+        [448.0, 455.0, 463.9, 1e6, -1e6, 0.0],
+    ])
+    v = np.concatenate([v, -v])
+    got = omx._e4m3_encode(v)
+    clamped = np.clip(v, -448.0, 448.0)
+    want = torch.from_numpy(clamped).float().to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+
+
+def test_mxfp8_shared_exponent_worked_examples():
+    blk = np.zeros((4, 32))
+    blk[0, 5] = 1.0      # amax 1 -> shared exponent -8 -> byte 119; 1.0 -> 256 = code 0x78
+    blk[1, :] = 448.0    # amax 448 -> exponent 0 -> byte 127; 448 -> code 0x7E
+    blk[2, 3] = -500.0   # amax 500 -> exponent 0; 500 saturates to -448 -> 0xFE
+    q, s = oracle.quant_mxfp8(blk)     # row 3 all zero -> byte 0, codes 0
+    assert list(s[:, 0]) == [119, 127, 127, 0]
+    assert q[0, 5] == 0x78 and q[0, 0] == 0
+    assert np.all(q[1] == 0x7E)
+    assert q[2, 3] == 0xFE
+    assert np.all(q[3] == 0)
+
+
+def test_mxfp8_rounding_error_bound():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-6, 6, (64, 1)))
+    q, s = oracle.quant_mxfp8(v)
+    d = oracle.dequant_mxfp8(q, s)
+    scale = np.repeat(oracle.e8m0_decode(s), 32, axis=-1)
+    scaled = np.abs(v) / scale
+    normal = (scaled >= 2.0 ** -6) & (scaled <= 448.0)
+    # nearest rounding with a 3-bit mantissa: error at most 2^-4 of the value
+    assert np.all(np.abs(d - v)[normal] <= np.abs(v)[normal] * 2.0 ** -4)
+    # subnormal elements: absolute error at most half a spacing (2^-10 * scale)
+    sub = scaled < 2.0 ** -6
+    assert np.all(np.abs(d - v)[sub] <= scale[sub] * 2.0 ** -10)
+
+
+# ----------------------------------------------------------------- routing
+
+def test_topk_selection_by_brute_force():
+    rng = np.random.default_rng(11)
+    for _ in range(200):
+        E, k = int(rng.integers(2, 9)), 0
+        k = int(rng.integers(1, E + 1))
+        lg = rng.integers(-3, 4, size=(1, E)).astype(np.float32)  # many ties
+        ids, w = oracle.route_topk_softmax(lg, k)
+        sel = list(ids[0])
+        rest = [i for i in range(E) if i not in sel]
+        l = lg[0]
+        def before(a, b):  # a ranks before b: larger logit, or equal and lower id
+            return l[a] > l[b] or (l[a] == l[b] and a < b)
+        assert len(set(sel)) == k
+        assert all(before(a, b) for a in sel for b in rest)
+        assert all(before(sel[j], sel[j + 1]) for j in range(k - 1))
+
+
+def test_topk_matches_torch_topk_on_distinct_logits():
+    rng = np.random.default_rng(12)
+    lg = rng.standard_normal((50, 896)).astype(np.float32)
+    ids, _ = oracle.route_topk_softmax(lg, 16)
+    want = torch.topk(torch.from_numpy(lg), 16, dim=1, sorted=True).indices.numpy()
+    assert np.array_equal(ids, want)
+
+
+def test_topk_weights_are_softmax_of_selected():
+    rng = np.random.default_rng(13)
+    lg = (rng.standard_normal((40, 64)) * 3).astype(np.float32)
+    ids, w = oracle.route_topk_softmax(lg, 8)
+    sel = np.take_along_axis(lg.astype(np.float64), ids, 1)
+    assert np.allclose(w, scipy.special.softmax(sel, axis=1), rtol=1e-14, atol=0)
+    full = scipy.special.softmax(lg.astype(np.float64), axis=1)
+    renorm = np.take_along_axis(full, ids, 1)
+    assert np.allclose(w, renorm / renorm.sum(1, keepdims=True), rtol=1e-13, atol=0)
+    assert np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
+
+
+def test_local_map_offset_and_masked_ids():
+    ids = np.array([[-1, 0, 447, 448, 449, 895, 896, 1000]])
+    got = oracle.local_map(ids, 448, 448)
+    assert list(got[0]) == [-1, -1, -1, 0, 1, 447, -1, -1]
+
+
+# ----------------------------------------------------------- shared append
+
+def test_shared_append_golden_values():
+    rows = _golden_rows("shared_append.txt")
+    for lg, sc, want in rows:
+        bits = f32_to_bf16_bits(np.array([[float(lg)]], np.float32))
+        ids, w = oracle.shared_append(bits, E=10, S=1, scale=float(sc))
+        assert ids[0, 0] == 10
+        assert math.isclose(w[0, 0], float(want), rel_tol=1e-14, abs_tol=0)
+
+
+def test_shared_append_matches_scipy_expit():
+    rng = np.random.default_rng(5)
+    bits = f32_to_bf16_bits((rng.standard_normal((64, 3)) * 2).astype(np.float32))
+    ids, w = oracle.shared_append(bits, E=7, S=3, scale=0.5)
+    assert np.array_equal(ids, np.broadcast_to([7, 8, 9], (64, 3)))
+    want = scipy.special.expit(oracle.bf16_bits_to_f64(bits)) * 0.5
+    assert np.allclose(w, want, rtol=1e-15, atol=0)
+
+
+# -------------------------------------------------------------------- sort
+
+def test_kmax_v_reproduces_kimi_k31_constant():
+    g = {r[0]: int(r[1]) for r in _golden_rows("kimi_k31_tp8_shape.txt")}
+    assert oracle.kmax_v(g["num_experts"], g["max_tokens"], g["top_k"], g["block_n"]) == g["kmax_v"]
+
+
+def _check_sort(se, Ep, B):
+    m = oracle.sort_align(se, Ep, B)
+    flat = se.reshape(-1)
+    # brute force: rows are the valid slots sorted by (expert, slot)
+    want = [s for _, s in sorted((int(e), s) for s, e in enumerate(flat) if e >= 0)]
+    assert list(m["sorted_slot"]) == want
+    assert m["counts"].sum() == np.count_nonzero(flat >= 0)
+    assert np.array_equal(m["counts"], np.bincount(flat[flat >= 0], minlength=Ep)[:Ep])
+    assert m["offsets"][0] == 0 and np.all(np.diff(m["offsets"]) == m["counts"])
+    R = len(want)
+    ex = m["expanded_idx"]
+    assert np.all(ex[flat < 0] == -1)
+    assert np.array_equal(ex[m["sorted_slot"]], np.arange(R))
+    # every row belongs to its expert's range
+    for e in range(Ep):
+        seg = m["sorted_slot"][m["offsets"][e]:m["offsets"][e + 1]]
+        assert np.all(flat[seg] == e)
+    T, Kp = se.shape
+    assert m["num_v"] <= oracle.kmax_v(Ep, T, Kp, B)
+    # vinfo chunks tile each expert's rows in order
+    covered = np.zeros(R, np.int64)
+    for e, r0, n, c in m["vinfo"]:
+        assert 1 <= n <= B and r0 == m["offsets"][e] + c * B
+        covered[r0:r0 + n] += 1
+        assert np.all(flat[m["sorted_slot"][r0:r0 + n]] == e)
+    assert np.all(covered == 1)
+    return m
+
+
+def test_sort_brute_force_random():
+    rng = np.random.default_rng(21)
+    for _ in range(60):
+        T, Kp, Ep = int(rng.integers(1, 40)), int(rng.integers(1, 9)), int(rng.integers(1, 20))
+        B = int(rng.choice([1, 2, 16, 32]))
+        se = rng.integers(-1, Ep, size=(T, Kp)).astype(np.int32)
+        _check_sort(se, Ep, B)
+
+
+def test_sort_counts_sum_when_all_local():
+    s = LayerShape("t", T=48, E=64, E_g=64, topk=16, H=512, I=128, B=16)
+    inp = make_inputs(s, 9, weights=False)
+    res = oracle.reference_forward(s, inp, compute_out=False)
+    assert res["counts"].sum() == s.T * s.topk
+    _check_sort(res["slot_expert"], s.Ep, s.B)
+
+
+def test_vinfo_bound_is_tight():
+    # every token on its own experts in chunks of exactly B reach the bound's shape
+    T, Kp, B, Ep = 32, 2, 16, 8
+    se = np.tile(np.arange(2, dtype=np.int32), (T, 1))  # two experts, 32 rows each
+    m = _check_sort(se, Ep, B)
+    assert m["num_v"] == 4
+
+
+# -------------------------------------------------------------------- gate
+
+def test_gate_rule_and_force():
+    c = np.zeros(10, np.int32)
+    assert oracle.gate_word(c) == (0, 0, 0, 0)
+    c[:4] = [64, 64, 64, 63]
+    assert oracle.gate_word(c)[:3] == (0, 4, 255)        # 255 < 64*4
+    c[3] = 64
+    assert oracle.gate_word(c) == (1, 4, 256, 4)
+    c[0] = 129
+    assert oracle.gate_word(c) == (1, 4, 321, 5)         # 129 rows -> two 128-row tiles
+    assert oracle.gate_word(c, force_path=0) == (0, 4, 321, 0)
+    c2 = np.array([1, 1, 0], np.int32)
+    assert oracle.gate_word(c2, force_path=1) == (1, 2, 2, 2)
+    t = oracle.dense_tiles(np.array([0, 300, 5]), np.array([0, 0, 300, 305]))
+    assert t.tolist() == [[1, 0, 128, 0], [1, 128, 128, 1], [1, 256, 44, 2], [2, 300, 5, 0]]
+
+
+# ------------------------------------------------- whole layer, closed form
+
+def _pack_rows(codes):
+    """codes [rows, K] (0..15) -> bytes [rows, K/2], low nibble = even k."""
+    codes = np.asarray(codes, np.uint8)
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def _onehot_layer():
+    """A layer whose weights are one-hot rows, so its output has a closed form.
+
+    Expert e: gate row i reads x[pg_e(i)] times cg_e, up row i reads
+    x[pu_e(i)] times cu_e, output row h reads act[h % I] times c2_e.
+    The other scale group of each row holds a different exponent, so a
+    wrong group index changes the result.
+    """
+    H, I, E, S = 64, 32, 3, 1
+    Ep = E + S
+    gcode, gscale = 3, 126   # 1.5 * 2^-1 = 0.75
+    ucode, uscale = 6, 125   # 4.0 * 2^-2 = 1.0
+    dcode, dscale = 5, 128   # 3.0 * 2^1 = 6.0
+    w13c = np.zeros((Ep, 2 * I, H), np.uint8)
+    s13 = np.zeros((Ep, 2 * I, H // 32), np.uint8)
+    w2c = np.zeros((Ep, H, I), np.uint8)
+    s2 = np.zeros((Ep, H, I // 32), np.uint8)
+    pg = lambda e, i: (5 * i + 7 * e + 1) % H
+    pu = lambda e, i: (3 * i + 11 * e + 2) % H
+    for e in range(Ep):
+        for i in range(I):
+            k = pg(e, i)
+            w13c[e, i, k] = gcode
+            s13[e, i, :] = gscale + 3
+            s13[e, i, k // 32] = gscale + e  # expert e's gate weight is 0.75 * 2^e
+            k = pu(e, i)
+            w13c[e, I + i, k] = ucode
+            s13[e, I + i, :] = uscale + 2
+            s13[e, I + i, k // 32] = uscale
+        for h in range(H):
+            w2c[e, h, h % I] = dcode
+            s2[e, h, :] = dscale
+    cgv = lambda e: 0.75 * 2.0 ** e
+    wts = dict(w13=np.stack([_pack_rows(w13c[e]) for e in range(Ep)]), s13=s13,
+               w2=np.stack([_pack_rows(w2c[e]) for e in range(Ep)]), s2=s2)
+    return H, I, E, S, pg, pu, cgv, 1.0, 6.0, wts
+
+
+def _closed_form_out(x, ids, w, shared_w, E, offset, limit, H, I, pg, pu, cgv, cu, c2):
+    silu = lambda v: v / (1.0 + math.exp(-v))
+    T = x.shape[0]
+    out = np.zeros((T, H))
+    for t in range(T):
+        cols = [(int(g) - offset, float(wt)) for g, wt in zip(ids[t], w[t])
+                if g >= 0 and 0 <= int(g) - offset < E]
+        cols += [(E + s, float(shared_w[t, s])) for s in range(shared_w.shape[1])]
+        for e, wt in cols:
+            for h in range(H):
+                i = h % I
+                g = cgv(e) * x[t, pg(e, i)]
+                u = cu * x[t, pu(e, i)]
+                if limit > 0:
+                    g = min(g, limit)
+                    u = max(-limit, min(u, limit))
+                out[t, h] += wt * c2 * silu(g) * u
+    return out
+
+
+@pytest.mark.parametrize("limit", [0.0, 1.25])
+def test_whole_layer_closed_form(limit):
+    H, I, E, S, pg, pu, cgv, cu, c2, wts = _onehot_layer()
+    offset, E_g, topk, T = 2, 8, 3, 5
+    rng = np.random.default_rng(31)
+    x = (rng.integers(-16, 17, size=(T, H)) / 4.0).astype(np.float32)  # exact in bf16
+    ids = np.array([[2, 3, 4], [0, 3, -1], [5, 7, 1], [4, 2, 6], [-1, -1, -1]], np.int32)
+    w = np.array([[.5, .25, .25], [.3, .7, 0], [.6, .3, .1], [.125, .5, .375], [1, 0, 0]], np.float32)
+    sh = f32_to_bf16_bits(np.array([[0.0], [2.0], [-2.0], [1.0], [0.5]], np.float32))
+    shape = LayerShape("cf", T=T, E=E, E_g=E_g, topk=topk, H=H, I=I, B=2, S=S,
+                       expert_offset=offset, swiglu_limit=limit, shared_scale=0.5, mode="ids")
+    inp = dict(x=f32_to_bf16_bits(x), logits=np.zeros((T, E_g), np.float32), shared=sh,
+               topk_ids=ids, topk_w=w, **wts)
+    got = oracle.reference_forward(shape, inp)["out"]
+    shared_w = scipy.special.expit(oracle.bf16_bits_to_f64(sh)) * 0.5
+    want = _closed_form_out(x.astype(np.float64), ids, w.astype(np.float64), shared_w, E, offset,
+                            limit, H, I, pg, pu, cgv, cu, c2)
+    assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
+    if limit > 0:  # the clamp must actually bite in this example
+        g_all = [cgv(e) * abs(x[t, pg(e, i)]) for t in range(T) for e in range(E + S) for i in range(I)]
+        assert max(g_all) > limit
+
+
+def test_dense_glu_reduction_matches_torch():
+    # E = 1, top-1, weight 1: the layer is a plain gated MLP,
+    # y = W2 (silu(Wg x) * (Wu x)), evaluated with torch in float64.
+    s = LayerShape("glu", T=6, E=1, E_g=1, topk=1, H=64, I=32, B=16, exp_lo=120, exp_hi=127)
+    inp = make_inputs(s, 17)
+    got = oracle.reference_forward(s, inp)["out"]
+    table = torch.from_numpy(_e2m1_table())
+
+    def deq(packed, sc):
+        p = torch.from_numpy(packed.astype(np.int64))
+        codes = torch.stack([p & 15, p >> 4], dim=-1).reshape(p.shape[0], -1)
+        scale = torch.from_numpy(sc).view(torch.float8_e8m0fnu).double()
+        return table[codes] * scale.repeat_interleave(32, dim=1)
+
+    W13 = deq(inp["w13"][0], inp["s13"][0])
+    W2 = deq(inp["w2"][0], inp["s2"][0])
+    x = torch.from_numpy(inp["x"].astype(np.int32)).to(torch.int16).view(torch.bfloat16).double()
+    Wg, Wu = W13[:32], W13[32:]
+    y = torch.nn.functional.silu(x @ Wg.T) * (x @ Wu.T) @ W2.T
+    assert np.allclose(got, y.numpy(), rtol=1e-12, atol=1e-9)
+
+
+# ------------------------------------------------ grouped vs per-token loop
+
+SMALL = [
+    LayerShape("s1", T=9, E=8, E_g=8, topk=2, H=64, I=32, B=2),
+    LayerShape("s2", T=17, E=6, E_g=12, topk=4, H=64, I=64, B=3, expert_offset=6, routing="zipf"),
+    LayerShape("s3", T=11, E=5, E_g=5, topk=2, H=96, I=32, B=4, S=2, swiglu_limit=3.0,
+               shared_scale=0.5),
+    LayerShape("s4", T=13, E=7, E_g=20, topk=5, H=64, I=32, B=2, expert_offset=3, mode="ids"),
+    LayerShape("s5", T=7, E=4, E_g=4, topk=2, H=64, I=64, B=16, a_dtype="mxfp8", S=1,
+               swiglu_limit=2.0),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: s.name)
+def test_grouped_matches_per_token_loop(shape):
+    inp = make_inputs(shape, 100 + SMALL.index(shape))
+    if shape.mode == "ids":
+        inp["topk_ids"][0, 0] = -1
+        inp["topk_ids"][1, :] = -1
+    res = oracle.reference_forward(shape, inp)
+    loop = oracle.sampled_forward(shape, inp, np.arange(shape.T))
+    assert np.allclose(res["out"], loop, rtol=1e-12, atol=1e-9 * np.max(np.abs(loop)))
+    sub = np.array([shape.T - 1, 0, 2])
+    assert np.allclose(oracle.sampled_forward(shape, inp, sub), res["out"][sub],
+                       rtol=1e-12, atol=1e-9 * np.max(np.abs(loop)))
+
+
+def test_finalize_zero_and_single_slot():
+    s = LayerShape("z", T=4, E=4, E_g=8, topk=1, H=64, I=32, B=2, expert_offset=4, mode="ids")
+    inp = make_inputs(s, 41)
+    inp["topk_ids"][:] = np.array([[0], [3], [5], [-1]])
+    inp["topk_w"][:] = np.array([[1.0], [0.5], [0.25], [1.0]], np.float32)
+    res = oracle.reference_forward(s, inp)
+    out = res["out"]
+    assert np.all(out[0] == 0) and np.all(out[1] == 0) and np.all(out[3] == 0)
+    x = oracle.bf16_bits_to_f64(inp["x"][2:3])
+    W13 = oracle.dequant_mxfp4(inp["w13"][1], inp["s13"][1])
+    W2 = oracle.dequant_mxfp4(inp["w2"][1], inp["s2"][1])
+    assert np.allclose(out[2], 0.25 * oracle.expert_glu(x, W13, W2)[0], rtol=1e-14, atol=0)
+
+
+def test_mxfp8_activation_path_quantises_x_per_token():
+    s = SMALL[4]
+    inp = make_inputs(s, 104)
+    res = oracle.reference_forward(s, inp, compute_out=False)
+    q, sc = oracle.quant_mxfp8(oracle.bf16_bits_to_f64(inp["x"]))
+    assert np.array_equal(res["xq"], q) and np.array_equal(res["xs"], sc)
+    assert res["xq"].shape == (s.T, s.H) and res["xs"].shape == (s.T, s.H // 32)
+
+
+# ----------------------------------------------- planted mistakes are caught
+
+def _closed_form_error(limit=1.25):
+    try:
+        test_whole_layer_closed_form(limit)
+    except AssertionError:
+        return True
+    return False
+
+
+def test_planted_mistakes_are_caught(monkeypatch):
+    assert not _closed_form_error()
+    # 1. swapped nibble order
+    orig_unpack = omx._unpack_nibbles
+
+    def swapped(p):
+        c = orig_unpack(p)
+        return c.reshape(c.shape[:-1] + (-1, 2))[..., ::-1].reshape(c.shape)
+    monkeypatch.setattr(omx, "_unpack_nibbles", swapped)
+    assert _closed_form_error()
+    monkeypatch.setattr(omx, "_unpack_nibbles", orig_unpack)
+    # 2. gate and up halves swapped
+    orig_glu = omoe.expert_glu
+
+    def glu_swapped(xr, W13, W2, limit=0.0, act_mxfp8=False):
+        I = W13.shape[0] // 2
+        return orig_glu(xr, np.concatenate([W13[I:], W13[:I]]), W2, limit, act_mxfp8)
+    monkeypatch.setattr(omoe, "expert_glu", glu_swapped)
+    assert _closed_form_error()
+    monkeypatch.setattr(omoe, "expert_glu", orig_glu)
+    # 3. scale group index taken modulo instead of divided
+    orig_deq = omoe.dequant_mxfp4
+
+    def deq_bad(packed, scales):
+        codes = omx._unpack_nibbles(packed)
+        k = codes.shape[-1]
+        idx = np.arange(k) % scales.shape[-1]
+        return omx.e2m1_decode(codes) * omx.e8m0_decode(scales)[..., idx]
+    monkeypatch.setattr(omoe, "dequant_mxfp4", deq_bad)
+    assert _closed_form_error()
+    monkeypatch.setattr(omoe, "dequant_mxfp4", orig_deq)
+    # 4. gate clamped from below as well as above
+    def glu_clamp_both(xr, W13, W2, limit=0.0, act_mxfp8=False):
+        I = W13.shape[0] // 2
+        h = xr @ W13.T
+        g, u = h[:, :I], h[:, I:]
+        if limit > 0:
+            g, u = np.clip(g, -limit, limit), np.clip(u, -limit, limit)
+        return (g / (1 + np.exp(-g)) * u) @ W2.T
+    monkeypatch.setattr(omoe, "expert_glu", glu_clamp_both)
+    assert _closed_form_error()
+    monkeypatch.setattr(omoe, "expert_glu", orig_glu)
+    # 5. expert offset ignored
+    orig_lm = omoe.local_map
+    monkeypatch.setattr(omoe, "local_map", lambda ids, E, off: orig_lm(ids, E, 0))
+    assert _closed_form_error()
+    monkeypatch.setattr(omoe, "local_map", orig_lm)
+    # 6. shared weight without the sigmoid
+    orig_sig = omoe._sigmoid
+    monkeypatch.setattr(omoe, "shared_append",
+                        lambda b, E, S, sc: (np.broadcast_to(np.arange(E, E + S, dtype=np.int32),
+                                                             (b.shape[0], S)).copy(),
+                                             omoe.bf16_bits_to_f64(b).reshape(-1, S) * sc))
+    assert _closed_form_error()
+    assert orig_sig is omoe._sigmoid
