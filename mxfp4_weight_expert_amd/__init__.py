@@ -1,0 +1,197 @@
+"""Python binding of libmoe_mxfp4 (the fused MXFP4 MoE layer for MI355X).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. PyTorch supplies device memory and the current stream. The names
+mirror the C ABI in include/moe_mxfp4.h: query, workspace_layout, forward,
+strerror. There is no fallback: without the built library every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+__all__ = ["Shape", "query", "workspace_layout", "forward", "strerror", "lib_path",
+           "MoeError", "read_maps", "ADTYPE", "GEMM2_PATH", "load_library"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libmoe_mxfp4.so")
+
+MOE_OK = 0
+ADTYPE = {"bf16": 0, "mxfp8": 1}
+GEMM2_PATH = {"auto": -1, "split": 0, "dense": 1}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} (code {code})")
+        self.code = code
+
+
+class _Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "T", "E", "E_global", "topk", "S", "H", "I", "block_n", "expert_offset", "activation",
+        "a_dtype", "force_gemm2_path")] + [("swiglu_limit", ctypes.c_float),
+                                            ("shared_scale", ctypes.c_float)]
+
+
+_LAYOUT_U64 = ("total_bytes", "counters", "route_ids", "slot_expert", "slot_w", "range_counts",
+               "counts", "offsets", "sorted_slot", "expanded_idx", "vinfo", "dense_tiles", "act",
+               "act_scales", "y", "xq", "xs")
+_LAYOUT_I32 = ("kmax_v", "max_dense_tiles", "n_ranges", "rows_pad")
+
+
+class _Layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_uint64) for n in _LAYOUT_U64] + [(n, ctypes.c_int32) for n in _LAYOUT_I32]
+
+
+_lib = None
+
+
+def load_library():
+    """Load the built library (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(lib_path):
+        raise RuntimeError(f"{lib_path} is missing: build it with "
+                           "`python -m mxfp4_weight_expert_amd.build`")
+    lib = ctypes.CDLL(lib_path)
+    lib.moe_mxfp4_query.argtypes = [ctypes.POINTER(_Shape), ctypes.POINTER(ctypes.c_uint64)]
+    lib.moe_mxfp4_query.restype = ctypes.c_int
+    lib.moe_mxfp4_workspace_layout.argtypes = [ctypes.POINTER(_Shape), ctypes.POINTER(_Layout)]
+    lib.moe_mxfp4_workspace_layout.restype = ctypes.c_int
+    lib.moe_mxfp4_strerror.argtypes = [ctypes.c_int]
+    lib.moe_mxfp4_strerror.restype = ctypes.c_char_p
+    vp = ctypes.c_void_p
+    lib.moe_mxfp4_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Shape),
+                                      vp, vp, ctypes.c_uint64, vp]
+    lib.moe_mxfp4_forward.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+@dataclass(frozen=True)
+class Shape:
+    """Layer shape (fields as in moe_mxfp4_shape)."""
+
+    T: int
+    E: int
+    E_global: int
+    topk: int
+    H: int
+    I: int
+    block_n: int
+    S: int = 0
+    expert_offset: int = 0
+    swiglu_limit: float = 0.0
+    shared_scale: float = 1.0
+    a_dtype: str = "bf16"
+    force_gemm2_path: str = "auto"
+
+    def to_c(self) -> _Shape:
+        return _Shape(self.T, self.E, self.E_global, self.topk, self.S, self.H, self.I,
+                      self.block_n, self.expert_offset, 0, ADTYPE[self.a_dtype],
+                      GEMM2_PATH[self.force_gemm2_path], float(self.swiglu_limit),
+                      float(self.shared_scale))
+
+    @property
+    def Kp(self) -> int:
+        return self.topk + self.S
+
+    @property
+    def Ep(self) -> int:
+        return self.E + self.S
+
+
+def strerror(code: int) -> str:
+    return load_library().moe_mxfp4_strerror(code).decode()
+
+
+def query(shape: Shape) -> int:
+    """Workspace bytes for a shape (raises MoeError if unsupported)."""
+    n = ctypes.c_uint64()
+    rc = load_library().moe_mxfp4_query(ctypes.byref(shape.to_c()), ctypes.byref(n))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_mxfp4_query")
+    return int(n.value)
+
+
+def workspace_layout(shape: Shape) -> dict:
+    lay = _Layout()
+    rc = load_library().moe_mxfp4_workspace_layout(ctypes.byref(shape.to_c()), ctypes.byref(lay))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_mxfp4_workspace_layout")
+    return {n: int(getattr(lay, n)) for n in _LAYOUT_U64 + _LAYOUT_I32}
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def forward(x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=None, topk_w=None,
+            shared_logits=None, out=None, workspace=None, stream=None):
+    """Run the layer; returns out (bf16 [T, H]).
+
+    x bf16 [T, H]; w13/s13/w2/s2 uint8 as in the C header; router_logits
+    float32 [T, E_global] or (topk_ids int32 [T, topk], topk_w float32
+    [T, topk]); shared_logits bf16 [T, S]. workspace: a uint8 CUDA tensor of
+    at least query(shape) bytes (allocated here when None). All tensors must
+    be contiguous and on the current device.
+    """
+    import torch
+
+    lib = load_library()
+    tensors = [x, w13, s13, w2, s2, router_logits, topk_ids, topk_w, shared_logits, out, workspace]
+    for t in tensors:
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(query(shape), 256), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = lib.moe_mxfp4_forward(_ptr(x), _ptr(router_logits), _ptr(topk_ids), _ptr(topk_w),
+                               _ptr(shared_logits), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
+                               ctypes.byref(shape.to_c()), _ptr(out), _ptr(workspace),
+                               ctypes.c_uint64(workspace.numel()), ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_mxfp4_forward")
+    return out
+
+
+def read_maps(workspace, shape: Shape) -> dict:
+    """Views of the maps a forward call left in the workspace (device tensors)."""
+    import torch
+
+    L = workspace_layout(shape)
+    T, Kp, Ep = shape.T, shape.Kp, shape.Ep
+
+    def view(off, n, dtype):
+        nbytes = n * torch.tensor([], dtype=dtype).element_size()
+        return workspace[off: off + nbytes].view(dtype)
+
+    i32, f32 = torch.int32, torch.float32
+    ctr = view(L["counters"], 64, i32)
+    maps = {
+        "counters": ctr,
+        "route_ids": view(L["route_ids"], T * shape.topk, i32).view(T, shape.topk),
+        "slot_expert": view(L["slot_expert"], T * Kp, i32).view(T, Kp),
+        "slot_w": view(L["slot_w"], T * Kp, f32).view(T, Kp),
+        "counts": view(L["counts"], Ep, i32),
+        "offsets": view(L["offsets"], Ep + 1, i32),
+        "sorted_slot": view(L["sorted_slot"], T * Kp, i32),
+        "expanded_idx": view(L["expanded_idx"], T * Kp, i32),
+        "vinfo": view(L["vinfo"], L["kmax_v"] * 4, i32).view(-1, 4),
+        "dense_tiles": view(L["dense_tiles"], L["max_dense_tiles"] * 4, i32).view(-1, 4),
+        "act": view(L["act"], L["rows_pad"] * shape.I * (1 if shape.a_dtype == "mxfp8" else 2),
+                    torch.uint8),
+        "y": view(L["y"], L["rows_pad"] * shape.H, torch.bfloat16).view(L["rows_pad"], shape.H),
+        "layout": L,
+    }
+    if shape.a_dtype == "mxfp8":
+        maps["xq"] = view(L["xq"], T * shape.H, torch.uint8).view(T, shape.H)
+        maps["xs"] = view(L["xs"], T * shape.H // 32, torch.uint8).view(T, shape.H // 32)
+        maps["act_scales"] = view(L["act_scales"], L["rows_pad"] * shape.I // 32, torch.uint8)
+    return maps

@@ -1,0 +1,207 @@
+// C ABI of the MoE layer: shape checks, the workspace carve and the fixed
+// launch chain route -> sort (count, scan, scatter) -> GEMM2 gate -> GEMM1 ->
+// GEMM2 split -> GEMM2 dense -> finalize on one stream.
+//
+// The workspace carve follows the Shape-template page, section 3 (one byte
+// buffer, 256-byte aligned pieces, padding rows after the last chunk); the
+// shape limits are this library's own (the page's static_asserts fix
+// H % 512 and I % 128, which are kept).
+#include <cmath>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+constexpr int64_t kMaxSlots = int64_t(1) << 23;
+
+uint64_t align_up(uint64_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+int check_shape(const moe_mxfp4_shape* s) {
+  if (s == nullptr) return MOE_ERR_INVALID;
+  if (s->T < 0 || s->E < 1 || s->E_global < 1 || s->topk < 1 || s->S < 0 || s->H < 1 ||
+      s->I < 1 || s->expert_offset < 0)
+    return MOE_ERR_INVALID;
+  if (static_cast<int64_t>(s->expert_offset) + s->E > s->E_global) return MOE_ERR_INVALID;
+  if (!std::isfinite(s->swiglu_limit) || !std::isfinite(s->shared_scale)) return MOE_ERR_INVALID;
+  if (s->force_gemm2_path < -1 || s->force_gemm2_path > 1) return MOE_ERR_INVALID;
+  if (s->topk > kMaxTopK || s->topk > s->E_global || s->S > kMaxShared) return MOE_ERR_UNSUPPORTED;
+  if (s->E + s->S > kMaxExperts || s->E_global > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s->H % 512 != 0 || s->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if (s->block_n != 16 && s->block_n != 32 && s->block_n != 64 && s->block_n != 128 &&
+      s->block_n != 256)
+    return MOE_ERR_UNSUPPORTED;
+  if (s->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (s->a_dtype != MOE_ADTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(s->T) * (s->topk + s->S) > kMaxSlots) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+void carve(const moe_mxfp4_shape* s, moe_mxfp4_ws_layout* L) {
+  const uint64_t T = s->T, Kp = s->topk + s->S, Ep = s->E + s->S, H = s->H, I = s->I;
+  const uint64_t slots = T * Kp;
+  const bool a8 = s->a_dtype == MOE_ADTYPE_MXFP8;
+  L->kmax_v = static_cast<int32_t>(Ep + slots / s->block_n);
+  L->max_dense_tiles = static_cast<int32_t>(Ep + slots / kDenseMT);
+  L->n_ranges = static_cast<int32_t>(slots == 0 ? 1 : (slots + kRangeSlots - 1) / kRangeSlots);
+  const uint64_t pad = s->block_n > kDenseMT ? s->block_n : kDenseMT;
+  L->rows_pad = static_cast<int32_t>(slots + pad);
+  const uint64_t rp = static_cast<uint64_t>(L->rows_pad);
+  uint64_t o = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L->counters = take(kCounterWords * 4);
+  L->route_ids = take(T * s->topk * 4);
+  L->slot_expert = take(slots * 4);
+  L->slot_w = take(slots * 4);
+  L->range_counts = take(static_cast<uint64_t>(L->n_ranges) * Ep * 4);
+  L->counts = take(Ep * 4);
+  L->offsets = take((Ep + 1) * 4);
+  L->sorted_slot = take(slots * 4);
+  L->expanded_idx = take(slots * 4);
+  L->vinfo = take(static_cast<uint64_t>(L->kmax_v) * 16);
+  L->dense_tiles = take(static_cast<uint64_t>(L->max_dense_tiles) * 16);
+  L->act = take(rp * I * (a8 ? 1 : 2));
+  L->act_scales = take(a8 ? rp * I / 32 : 0);
+  L->y = take(rp * H * 2);
+  L->xq = take(a8 ? T * H : 0);
+  L->xs = take(a8 ? T * H / 32 : 0);
+  L->total_bytes = o;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_mxfp4_query(const moe_mxfp4_shape* shape, uint64_t* workspace_bytes) {
+  if (workspace_bytes == nullptr) return MOE_ERR_INVALID;
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  moe_mxfp4_ws_layout L;
+  carve(shape, &L);
+  *workspace_bytes = L.total_bytes;
+  return MOE_OK;
+}
+
+int moe_mxfp4_workspace_layout(const moe_mxfp4_shape* shape, moe_mxfp4_ws_layout* layout) {
+  if (layout == nullptr) return MOE_ERR_INVALID;
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  carve(shape, layout);
+  return MOE_OK;
+}
+
+const char* moe_mxfp4_strerror(int code) {
+  switch (code) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape";
+    case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown error";
+  }
+}
+
+int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
+                      const int32_t* topk_ids_dev, const float* topk_w_dev,
+                      const void* shared_logits_dev, const uint8_t* w13_dev,
+                      const uint8_t* s13_dev, const uint8_t* w2_dev, const uint8_t* s2_dev,
+                      const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
+                      uint64_t workspace_bytes, void* stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  const moe_mxfp4_shape& s = *shape;
+  const bool ids_mode = topk_ids_dev != nullptr || topk_w_dev != nullptr;
+  if (ids_mode == (router_logits_dev != nullptr)) return MOE_ERR_INVALID;
+  if (ids_mode && (topk_ids_dev == nullptr || topk_w_dev == nullptr)) return MOE_ERR_INVALID;
+  if (s.T == 0) return MOE_OK;
+  if (x_dev == nullptr || w13_dev == nullptr || s13_dev == nullptr || w2_dev == nullptr ||
+      s2_dev == nullptr || out_dev == nullptr || workspace_dev == nullptr)
+    return MOE_ERR_INVALID;
+  if (s.S > 0 && shared_logits_dev == nullptr) return MOE_ERR_INVALID;
+  moe_mxfp4_ws_layout L;
+  carve(&s, &L);
+  if (workspace_bytes < L.total_bytes || reinterpret_cast<uintptr_t>(workspace_dev) % kAlign != 0)
+    return MOE_ERR_WORKSPACE;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace_dev);
+  auto at = [&](uint64_t off) { return ws + off; };
+  const int Kp = s.topk + s.S, Ep = s.E + s.S;
+  const int nslots = s.T * Kp;
+
+  RouteArgs ra;
+  ra.logits = router_logits_dev;
+  ra.topk_ids = topk_ids_dev;
+  ra.topk_w = topk_w_dev;
+  ra.shared_logits = static_cast<const uint16_t*>(shared_logits_dev);
+  ra.T = s.T;
+  ra.Eg = s.E_global;
+  ra.topk = s.topk;
+  ra.S = s.S;
+  ra.E = s.E;
+  ra.expert_offset = s.expert_offset;
+  ra.shared_scale = s.shared_scale;
+  ra.route_ids = reinterpret_cast<int32_t*>(at(L.route_ids));
+  ra.slot_expert = reinterpret_cast<int32_t*>(at(L.slot_expert));
+  ra.slot_w = reinterpret_cast<float*>(at(L.slot_w));
+  if (launch_route(ra, st) != hipSuccess) return MOE_ERR_HIP;
+
+  SortArgs sa;
+  sa.slot_expert = ra.slot_expert;
+  sa.nslots = nslots;
+  sa.Ep = Ep;
+  sa.B = s.block_n;
+  sa.n_ranges = L.n_ranges;
+  sa.force_path = s.force_gemm2_path;
+  sa.range_counts = reinterpret_cast<int32_t*>(at(L.range_counts));
+  sa.counts = reinterpret_cast<int32_t*>(at(L.counts));
+  sa.offsets = reinterpret_cast<int32_t*>(at(L.offsets));
+  sa.sorted_slot = reinterpret_cast<int32_t*>(at(L.sorted_slot));
+  sa.expanded_idx = reinterpret_cast<int32_t*>(at(L.expanded_idx));
+  sa.vinfo = reinterpret_cast<int32_t*>(at(L.vinfo));
+  sa.dense_tiles = reinterpret_cast<int32_t*>(at(L.dense_tiles));
+  sa.counters = reinterpret_cast<int32_t*>(at(L.counters));
+  if (launch_sort_and_gate(sa, st) != hipSuccess) return MOE_ERR_HIP;
+
+  GemmArgs ga;
+  ga.x = static_cast<const uint16_t*>(x_dev);
+  ga.w13 = w13_dev;
+  ga.s13 = s13_dev;
+  ga.w2 = w2_dev;
+  ga.s2 = s2_dev;
+  ga.vinfo = sa.vinfo;
+  ga.dense_tiles = sa.dense_tiles;
+  ga.counters = sa.counters;
+  ga.sorted_slot = sa.sorted_slot;
+  ga.H = s.H;
+  ga.I = s.I;
+  ga.Kp = Kp;
+  ga.B = s.block_n;
+  ga.kmax_v = L.kmax_v;
+  ga.max_dense_tiles = L.max_dense_tiles;
+  ga.limit = s.swiglu_limit;
+  ga.act = reinterpret_cast<uint16_t*>(at(L.act));
+  ga.y = reinterpret_cast<uint16_t*>(at(L.y));
+  if (launch_gemm1(ga, st) != hipSuccess) return MOE_ERR_HIP;
+  if (launch_gemm2(ga, st) != hipSuccess) return MOE_ERR_HIP;
+
+  FinalizeArgs fa;
+  fa.y = ga.y;
+  fa.expanded_idx = sa.expanded_idx;
+  fa.slot_w = ra.slot_w;
+  fa.T = s.T;
+  fa.Kp = Kp;
+  fa.H = s.H;
+  fa.out = static_cast<uint16_t*>(out_dev);
+  if (launch_finalize(fa, st) != hipSuccess) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Internal device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_mxfp4.h"
+
+namespace moe {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxShared = 8;
+constexpr int kMaxExperts = 2048;  // E + S
+constexpr int kRangeSlots = 4096;  // slots per sort range (one wave each)
+constexpr int kGateTau = 64;       // dense GEMM2 when rows >= kGateTau * touched experts
+constexpr int kDenseMT = 128;      // dense-path row tile
+constexpr int kCounterWords = 64;
+constexpr int kCtrNumV = 0;
+constexpr int kCtrGate = 4;        // 4 words: path, U, R, dense tiles
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+// -------------------------------------------------------------- wave helpers
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// Lanes below this one set in mask.
+__device__ __forceinline__ int popc_below(uint64_t mask) {
+  uint32_t lo = static_cast<uint32_t>(mask), hi = static_cast<uint32_t>(mask >> 32);
+  return __builtin_amdgcn_mbcnt_hi(hi, __builtin_amdgcn_mbcnt_lo(lo, 0u));
+}
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_sum_f(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(v), o, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(v >> 32), o, kWave);
+    uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+    v = w > v ? w : v;
+  }
+  return v;
+}
+// Inclusive prefix sum across the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    int t = __shfl_up(v, o, kWave);
+    if (l >= o) v += t;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------- MX decoding
+// E8M0 byte as the float scale operand of the gfx950 scaled converts.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t e) {
+  return __uint_as_float(e << 23);
+}
+
+// Eight E2M1 codes (one dword, low nibble first) times 2^(e-127) -> 8 bf16.
+// The products are bf16 numbers for e in [0, 252], so the conversion is exact;
+// the convert takes the scale from the exponent field of its float operand.
+// The packed pairs are moved as whole dwords: extracting single bf16 lanes of
+// the convert's result has been seen to duplicate the low half.
+template <int SEL>
+__device__ __forceinline__ uint32_t cvt_fp4x2_sel(uint32_t packed, float scale) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, SEL));
+}
+__device__ __forceinline__ bf16x8_t decode_fp4x8(uint32_t packed, float scale) {
+  uint4 r;
+  r.x = cvt_fp4x2_sel<0>(packed, scale);
+  r.y = cvt_fp4x2_sel<1>(packed, scale);
+  r.z = cvt_fp4x2_sel<2>(packed, scale);
+  r.w = cvt_fp4x2_sel<3>(packed, scale);
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- activation
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+__device__ __forceinline__ float swiglu(float g, float u, float limit) {
+  if (limit > 0.0f) {
+    g = fminf(g, limit);
+    u = fminf(fmaxf(u, -limit), limit);
+  }
+  return silu_f(g) * u;
+}
+
+// Plain 16-byte global load through the vector path.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+}  // namespace moe

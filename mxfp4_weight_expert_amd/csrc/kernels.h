@@ -1,0 +1,64 @@
+// Host-side launchers of the layer's kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct RouteArgs {
+  const float* logits;       // [T, Eg] or null (ids mode)
+  const int32_t* topk_ids;   // [T, topk] (ids mode)
+  const float* topk_w;       // [T, topk] (ids mode)
+  const uint16_t* shared_logits;  // [T, S] bf16
+  int T, Eg, topk, S, E, expert_offset;
+  float shared_scale;
+  int32_t* route_ids;    // [T, topk]
+  int32_t* slot_expert;  // [T, K']
+  float* slot_w;         // [T, K']
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t st);
+
+struct SortArgs {
+  const int32_t* slot_expert;
+  int nslots, Ep, B, n_ranges, force_path;
+  int32_t* range_counts;  // [n_ranges, Ep]
+  int32_t* counts;        // [Ep]
+  int32_t* offsets;       // [Ep + 1]
+  int32_t* sorted_slot;   // [nslots]
+  int32_t* expanded_idx;  // [nslots]
+  int32_t* vinfo;         // [kmax_v, 4]
+  int32_t* dense_tiles;   // [max_dense_tiles, 4]
+  int32_t* counters;      // [kCounterWords]
+};
+// Histogram -> scan (+ chunk table) -> scatter -> GEMM2 gate.
+hipError_t launch_sort_and_gate(const SortArgs& a, hipStream_t st);
+
+struct GemmArgs {
+  const uint16_t* x;         // [T, H] bf16
+  const uint8_t* w13;        // [Ep, 2I, H/2]
+  const uint8_t* s13;        // [Ep, 2I, H/32]
+  const uint8_t* w2;         // [Ep, H, I/2]
+  const uint8_t* s2;         // [Ep, H, I/32]
+  const int32_t* vinfo;
+  const int32_t* dense_tiles;
+  const int32_t* counters;
+  const int32_t* sorted_slot;
+  int H, I, Kp, B, kmax_v, max_dense_tiles;
+  float limit;
+  uint16_t* act;  // [rows_pad, I] bf16
+  uint16_t* y;    // [rows_pad, H] bf16
+};
+hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st);  // split + dense, gated on device
+
+struct FinalizeArgs {
+  const uint16_t* y;
+  const int32_t* expanded_idx;
+  const float* slot_w;
+  int T, Kp, H;
+  uint16_t* out;
+};
+hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,137 @@
+// Routing: top-k with softmax weights (or given ids/weights), the local
+// expert map with expert offset, and the fused sigmoid shared-expert append.
+//
+// Sources: "Generalizing the Kimi-K3.1 MXFP4 decode MoE kernel with a Shape
+// template", section 5 (ids outside [expert_offset, expert_offset + E) and
+// the masked id -1 get no row); "SGLang MoE shared-expert optimisation",
+// the append kernel after the change (shared column s: expert N_BASE + s,
+// weight sigmoid(float(bf16 logit)) * scale, computed in registers).
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+// Total order on float logits, larger first: map the bits so that unsigned
+// comparison follows the float order. -0.0 is folded into +0.0 first so the
+// two compare equal (the tie then goes to the lower id).
+__device__ __forceinline__ uint32_t order_bits(float f) {
+  uint32_t u = __float_as_uint(f + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float unorder_bits(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7fffffffu) : ~o;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ void write_shared_columns(const uint16_t* shared_logits, int t, int topk,
+                                                     int S, int E, float shared_scale,
+                                                     int32_t* slot_expert, float* slot_w) {
+  const int lane = lane_id();
+  const int Kp = topk + S;
+  if (lane >= topk && lane < Kp) {
+    const int s = lane - topk;
+    const float lg = bf16_to_f32(shared_logits[static_cast<size_t>(t) * S + s]);
+    const float sig = 1.0f / (1.0f + expf(-lg));
+    slot_expert[static_cast<size_t>(t) * Kp + lane] = E + s;
+    slot_w[static_cast<size_t>(t) * Kp + lane] = sig * shared_scale;
+  }
+}
+
+// One wave per token. NPL = logits held per lane (E_global <= 64 * NPL).
+// Selection: topk rounds of a wave-wide max over 64-bit keys
+// (ordered logit << 32 | ~id), so equal logits go to the lower id.
+template <int NPL>
+__global__ __launch_bounds__(256) void route_logits_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ shared_logits, int T, int Eg,
+    int topk, int S, int E, int expert_offset, float shared_scale, int32_t* __restrict__ route_ids,
+    int32_t* __restrict__ slot_expert, float* __restrict__ slot_w) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + static_cast<size_t>(t) * Eg;
+  uint64_t key[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const int idx = lane + kWave * j;
+    key[j] = 0;
+    if (idx < Eg)
+      key[j] = (static_cast<uint64_t>(order_bits(row[idx])) << 32) | static_cast<uint32_t>(~idx);
+  }
+  uint64_t lmax = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) lmax = key[j] > lmax ? key[j] : lmax;
+
+  uint64_t mine = 0;  // lane r keeps the r-th selected key
+  for (int r = 0; r < topk; ++r) {
+    const uint64_t m = wave_max_u64(lmax);
+    if (lane == r) mine = m;
+    if (lmax == m) {  // exactly one lane holds the winner (ids are distinct)
+      lmax = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        if (key[j] == m) key[j] = 0;
+        lmax = key[j] > lmax ? key[j] : lmax;
+      }
+    }
+  }
+  const bool sel = lane < topk;
+  const float lg = unorder_bits(static_cast<uint32_t>(mine >> 32));
+  const int id = static_cast<int>(~static_cast<uint32_t>(mine));
+  const float lmax_f = __shfl(lg, 0, kWave);
+  const float ex = sel ? expf(lg - lmax_f) : 0.0f;
+  const float sum = wave_sum_f(ex);
+  const int Kp = topk + S;
+  if (sel) {
+    route_ids[static_cast<size_t>(t) * topk + lane] = id;
+    const int loc = id - expert_offset;
+    slot_expert[static_cast<size_t>(t) * Kp + lane] = (loc >= 0 && loc < E) ? loc : -1;
+    slot_w[static_cast<size_t>(t) * Kp + lane] = ex / sum;
+  }
+  write_shared_columns(shared_logits, t, topk, S, E, shared_scale, slot_expert, slot_w);
+}
+
+// Ids mode: one wave per token, lanes over the K' columns.
+__global__ __launch_bounds__(256) void route_ids_kernel(
+    const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
+    const uint16_t* __restrict__ shared_logits, int T, int topk, int S, int E, int expert_offset,
+    float shared_scale, int32_t* __restrict__ route_ids, int32_t* __restrict__ slot_expert,
+    float* __restrict__ slot_w) {
+  const int lane = lane_id();
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int Kp = topk + S;
+  if (lane < topk) {
+    const size_t i = static_cast<size_t>(t) * topk + lane;
+    const int id = topk_ids[i];
+    route_ids[i] = id;
+    const int loc = id - expert_offset;
+    slot_expert[static_cast<size_t>(t) * Kp + lane] = (id >= 0 && loc >= 0 && loc < E) ? loc : -1;
+    slot_w[static_cast<size_t>(t) * Kp + lane] = topk_w[i];
+  }
+  write_shared_columns(shared_logits, t, topk, S, E, shared_scale, slot_expert, slot_w);
+}
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
+  const dim3 grid((a.T + 3) / 4), block(256);
+  if (a.logits == nullptr) {
+    hipLaunchKernelGGL(route_ids_kernel, grid, block, 0, st, a.topk_ids, a.topk_w, a.shared_logits,
+                       a.T, a.topk, a.S, a.E, a.expert_offset, a.shared_scale, a.route_ids,
+                       a.slot_expert, a.slot_w);
+    return hipGetLastError();
+  }
+  const int npl = (a.Eg + kWave - 1) / kWave;
+#define MOE_ROUTE(N)                                                                             \
+  hipLaunchKernelGGL(route_logits_kernel<N>, grid, block, 0, st, a.logits, a.shared_logits, a.T, \
+                     a.Eg, a.topk, a.S, a.E, a.expert_offset, a.shared_scale, a.route_ids,       \
+                     a.slot_expert, a.slot_w)
+  if (npl <= 1) MOE_ROUTE(1);
+  else if (npl <= 2) MOE_ROUTE(2);
+  else if (npl <= 4) MOE_ROUTE(4);
+  else if (npl <= 8) MOE_ROUTE(8);
+  else if (npl <= 16) MOE_ROUTE(16);
+  else MOE_ROUTE(32);
+#undef MOE_ROUTE
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,239 @@
+// Deterministic device sort of token slots into per-expert rows, the B-row
+// chunk table, and the device-side GEMM2 path gate.
+//
+// Sources: "SGLang CUTLASS MoE", section 1 (prepare_moe_input: per-expert
+// offsets, the row permutation and its inverse); "Generalizing the Kimi-K3.1
+// MXFP4 decode MoE kernel with a Shape template", sections 1 and 5 (chunks
+// of at most BlockN rows -- "virtual experts" -- bounded by
+// E + T*top-k/BlockN; rows of an expert ranked in token order so the result
+// does not depend on atomic order); "Device-side gating of the MoE GEMM2
+// path", sections 1-2 (one wave reads the sorted table and picks Dense or
+// Split; the other path's kernels launch and find zero items).
+//
+// The slots t*K' + k are cut into ranges of kRangeSlots, one wave each.
+//   count:   per-range expert histograms (LDS atomics: order-free counts);
+//   scan:    per-expert exclusive scan over ranges, expert offsets, chunks;
+//   scatter: each wave walks its range in slot order, 64 slots at a time,
+//            ranking equal experts inside the wave by ballot/popcount
+//            (a wave multisplit), so rows follow slot order exactly.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ slot_expert,
+                                                         int nslots, int Ep, int n_ranges,
+                                                         int32_t* __restrict__ range_counts) {
+  extern __shared__ int32_t lds[];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int r = blockIdx.x * 4 + w;
+  int32_t* h = lds + w * Ep;
+  for (int i = lane; i < Ep; i += kWave) h[i] = 0;
+  __syncthreads();
+  if (r < n_ranges) {
+    const int s0 = r * kRangeSlots;
+    const int s1 = min(nslots, s0 + kRangeSlots);
+    for (int s = s0 + lane; s < s1; s += kWave) {
+      const int e = slot_expert[s];
+      if (e >= 0) atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  if (r < n_ranges)
+    for (int i = lane; i < Ep; i += kWave) range_counts[static_cast<size_t>(r) * Ep + i] = h[i];
+}
+
+// One block of 1024 threads. Turns range_counts into per-range bases, writes
+// counts, offsets, the chunk table and the chunk count.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ range_counts,
+                                                         int n_ranges, int Ep, int B,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ vinfo,
+                                                         int32_t* __restrict__ counters) {
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_wrows[16], s_wchunks[16];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  // 1) per expert: exclusive scan over ranges, in place.
+  for (int e = tid; e < Ep; e += 1024) {
+    int run = 0;
+    int r = 0;
+    for (; r + 8 <= n_ranges; r += 8) {
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = range_counts[static_cast<size_t>(r + j) * Ep + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        range_counts[static_cast<size_t>(r + j) * Ep + e] = run;
+        run += c[j];
+      }
+    }
+    for (; r < n_ranges; ++r) {
+      const int c = range_counts[static_cast<size_t>(r) * Ep + e];
+      range_counts[static_cast<size_t>(r) * Ep + e] = run;
+      run += c;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  // 2) each thread owns experts [e0, e0 + per) ; block scan of rows and chunks.
+  const int per = (Ep + 1023) / 1024;
+  const int e0 = tid * per;
+  int rows = 0, chunks = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e < Ep) {
+      rows += s_cnt[e];
+      chunks += (s_cnt[e] + B - 1) / B;
+    }
+  }
+  const int rin = wave_incl_scan(rows), cin = wave_incl_scan(chunks);
+  if (lane == kWave - 1) {
+    s_wrows[w] = rin;
+    s_wchunks[w] = cin;
+  }
+  __syncthreads();
+  int rbase = 0, cbase = 0;
+  for (int j = 0; j < w; ++j) {
+    rbase += s_wrows[j];
+    cbase += s_wchunks[j];
+  }
+  int row = rbase + rin - rows, chunk = cbase + cin - chunks;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    if (e >= Ep) break;
+    const int n = s_cnt[e];
+    counts[e] = n;
+    offsets[e] = row;
+    for (int c = 0; c * B < n; ++c) {
+      int4 v;
+      v.x = e;
+      v.y = row + c * B;
+      v.z = min(B, n - c * B);
+      v.w = c;
+      reinterpret_cast<int4*>(vinfo)[chunk + c] = v;
+    }
+    row += n;
+    chunk += (n + B - 1) / B;
+  }
+  if (tid == 1023) {
+    offsets[Ep] = row;  // thread 1023 owns the last experts (or none): row = R
+    counters[kCtrNumV] = chunk;
+  }
+}
+
+__global__ __launch_bounds__(256) void sort_scatter_kernel(
+    const int32_t* __restrict__ slot_expert, int nslots, int Ep, int n_ranges, int key_bits,
+    const int32_t* __restrict__ range_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ expanded_idx) {
+  extern __shared__ int32_t lds[];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int r = blockIdx.x * 4 + w;
+  if (r >= n_ranges) return;  // wave-uniform; no block barrier below
+  int32_t* next = lds + w * Ep;  // next free row per expert for this range
+  for (int i = lane; i < Ep; i += kWave)
+    next[i] = offsets[i] + range_base[static_cast<size_t>(r) * Ep + i];
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int s0 = r * kRangeSlots;
+  const int s1 = min(nslots, s0 + kRangeSlots);
+  for (int c = s0; c < s1; c += kWave) {
+    const int s = c + lane;
+    const bool in = s < s1;
+    const int e = in ? slot_expert[s] : -1;
+    const bool valid = e >= 0;
+    const int key = valid ? e : Ep;  // Ep marks empty lanes
+    uint64_t match = ~0ull;
+    for (int b = 0; b < key_bits; ++b) {
+      const bool bit = (key >> b) & 1;
+      const uint64_t bal = ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    const int rank = __popcll(match & lt);
+    int base = 0;
+    if (valid) base = next[e];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      const int row = base + rank;
+      sorted_slot[row] = s;
+      expanded_idx[s] = row;
+      if (rank == 0) next[e] = base + __popcll(match);
+    } else if (in) {
+      expanded_idx[s] = -1;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// One wave: rows R and touched experts U from the counts; Dense iff
+// R >= kGateTau * U (or forced). On Dense it writes the per-expert 128-row
+// tile list. Gate word: {path, U, R, dense tiles (0 on Split)}.
+__global__ __launch_bounds__(64) void gemm2_gate_kernel(const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int Ep, int force_path,
+                                                        int32_t* __restrict__ counters,
+                                                        int32_t* __restrict__ dense_tiles) {
+  const int lane = lane_id();
+  int U = 0, R = 0;
+  for (int e = lane; e < Ep; e += kWave) {
+    const int n = counts[e];
+    U += n > 0;
+    R += n;
+  }
+  U = wave_sum(U);
+  R = wave_sum(R);
+  int path = (U > 0 && R >= kGateTau * U) ? 1 : 0;
+  if (force_path == 0 || force_path == 1) path = force_path;
+  int ntiles = 0;
+  if (path == 1) {
+    for (int c = 0; c < Ep; c += kWave) {
+      const int e = c + lane;
+      const int n = e < Ep ? counts[e] : 0;
+      const int nt = (n + kDenseMT - 1) / kDenseMT;
+      const int incl = wave_incl_scan(nt);
+      const int first = ntiles + incl - nt;
+      const int off = e < Ep ? offsets[e] : 0;
+      for (int m = 0; m < nt; ++m) {
+        int4 v;
+        v.x = e;
+        v.y = off + m * kDenseMT;
+        v.z = min(kDenseMT, n - m * kDenseMT);
+        v.w = m;
+        reinterpret_cast<int4*>(dense_tiles)[first + m] = v;
+      }
+      ntiles += __shfl(incl, kWave - 1, kWave);
+    }
+  }
+  if (lane == 0) {
+    int4 g;
+    g.x = path;
+    g.y = U;
+    g.z = R;
+    g.w = ntiles;
+    *reinterpret_cast<int4*>(counters + kCtrGate) = g;
+  }
+}
+
+hipError_t launch_sort_and_gate(const SortArgs& a, hipStream_t st) {
+  const int blocks = (a.n_ranges + 3) / 4;
+  const size_t lds = static_cast<size_t>(4) * a.Ep * sizeof(int32_t);
+  hipLaunchKernelGGL(sort_count_kernel, dim3(blocks), dim3(256), lds, st, a.slot_expert, a.nslots,
+                     a.Ep, a.n_ranges, a.range_counts);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, st, a.range_counts, a.n_ranges,
+                     a.Ep, a.B, a.counts, a.offsets, a.vinfo, a.counters);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  int key_bits = 1;
+  while ((1 << key_bits) <= a.Ep) ++key_bits;  // keys 0..Ep inclusive
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(256), lds, st, a.slot_expert,
+                     a.nslots, a.Ep, a.n_ranges, key_bits, a.range_counts, a.offsets,
+                     a.sorted_slot, a.expanded_idx);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(gemm2_gate_kernel, dim3(1), dim3(64), 0, st, a.counts, a.offsets, a.Ep,
+                     a.force_path, a.counters, a.dense_tiles);
+  return hipGetLastError();
+}
+
+}  // namespace moe

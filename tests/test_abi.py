@@ -1,0 +1,122 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function the header declares, agrees with the header on struct layout,
+and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import mxfp4_weight_expert_amd as moe
+import oracle
+from workloads import CONFIGS, CONFIG_ORDER
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mxfp4.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_mxfp4_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = moe.load_library()
+    names = _declared_functions()
+    assert names == ["moe_mxfp4_forward", "moe_mxfp4_query", "moe_mxfp4_strerror",
+                     "moe_mxfp4_workspace_layout"]
+    for n in names:
+        assert hasattr(lib, n), n
+    nm = subprocess.run(["nm", "-D", "--defined-only", moe.lib_path], capture_output=True, text=True)
+    exported = set(re.findall(r"\bT (moe_mxfp4_\w+)", nm.stdout))
+    assert exported == set(names)
+
+
+def test_struct_layout_matches_header(tmp_path):
+    src = tmp_path / "probe.c"
+    fields_s = [f[0] for f in moe._Shape._fields_]
+    fields_l = [f[0] for f in moe._Layout._fields_]
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe_mxfp4.h"', "int main(void){",
+             'printf("%zu %zu\\n", sizeof(moe_mxfp4_shape), sizeof(moe_mxfp4_ws_layout));']
+    lines += [f'printf("%zu\\n", offsetof(moe_mxfp4_shape, {f}));' for f in fields_s]
+    lines += [f'printf("%zu\\n", offsetof(moe_mxfp4_ws_layout, {f}));' for f in fields_l]
+    lines += ["return 0;}"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "probe"
+    subprocess.run(["gcc", "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    vals = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                           check=True).stdout.split()]
+    assert vals[0] == ctypes.sizeof(moe._Shape) and vals[1] == ctypes.sizeof(moe._Layout)
+    offs = [getattr(moe._Shape, f).offset for f in fields_s] + \
+           [getattr(moe._Layout, f).offset for f in fields_l]
+    assert vals[2:] == offs
+
+
+def _shape(**kw):
+    base = dict(T=64, E=896, E_global=896, topk=16, H=3584, I=384, block_n=32)
+    base.update(kw)
+    return moe.Shape(**base)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=3584 + 256), 2), (dict(I=384 + 64), 2), (dict(block_n=48), 2), (dict(topk=33), 2),
+    (dict(S=9), 2), (dict(E=2040, E_global=2040, S=9), 2), (dict(E_global=3000, E=2000), 2),
+    (dict(expert_offset=1), 1), (dict(T=-1), 1), (dict(E=0), 1), (dict(topk=0), 1),
+    (dict(force_gemm2_path="dense", T=1 << 20), 2),
+])
+def test_query_rejects_bad_shapes(kw, code):
+    with pytest.raises(moe.MoeError) as ei:
+        moe.query(_shape(**kw))
+    assert ei.value.code == code
+
+
+@pytest.mark.parametrize("name", CONFIG_ORDER)
+def test_layout_bounds_match_oracle(name):
+    s = CONFIGS[name]
+    L = moe.workspace_layout(moe.Shape(T=s.T, E=s.E, E_global=s.E_g, topk=s.topk, H=s.H, I=s.I,
+                                       block_n=s.B, S=s.S, expert_offset=s.expert_offset))
+    assert L["kmax_v"] == oracle.kmax_v(s.Ep, s.T, s.Kp, s.B)
+    offs = [L[k] for k in ("counters", "route_ids", "slot_expert", "slot_w", "range_counts",
+                           "counts", "offsets", "sorted_slot", "expanded_idx", "vinfo",
+                           "dense_tiles", "act", "act_scales", "y", "xq", "xs")]
+    assert all(o % 256 == 0 for o in offs)
+    assert offs == sorted(offs) and offs[-1] <= L["total_bytes"]
+    assert L["y"] - L["act"] >= L["rows_pad"] * s.I * 2
+    assert L["total_bytes"] - L["y"] >= L["rows_pad"] * s.H * 2
+    assert L["rows_pad"] >= s.T * s.Kp
+
+
+def test_kimi_k31_virtual_expert_bound_from_layout():
+    L = moe.workspace_layout(_shape(T=256, block_n=32))
+    assert L["kmax_v"] == 1024
+
+
+def _fwd(shape, logits=1, ids=None, w=None, ws=256, wsb=1 << 40, shared=None):
+    lib = moe.load_library()
+    P = ctypes.c_void_p
+    return lib.moe_mxfp4_forward(P(256), P(logits) if logits else None, P(ids) if ids else None,
+                                 P(w) if w else None, P(shared) if shared else None, P(256), P(256),
+                                 P(256), P(256), ctypes.byref(shape.to_c()), P(256),
+                                 P(ws) if ws else None, ctypes.c_uint64(wsb), None)
+
+
+def test_forward_rejects_before_launch():
+    s = _shape()
+    assert _fwd(s, logits=1, ids=512, w=512) == 1       # both routing inputs
+    assert _fwd(s, logits=None) == 1                     # neither
+    assert _fwd(s, logits=None, ids=512) == 1            # ids without weights
+    assert _fwd(s, wsb=1024) == 3                        # workspace too small
+    assert _fwd(s, ws=256 + 64) == 3                     # misaligned workspace
+    assert _fwd(s, ws=None) == 1
+    assert _fwd(_shape(S=1), shared=None) == 1           # shared experts need logits
+    assert _fwd(_shape(H=100)) == 2
+    assert _fwd(_shape(T=0), ws=None) == 0               # empty call: nothing to do
+
+
+def test_strerror():
+    assert moe.strerror(0) == "ok"
+    assert "workspace" in moe.strerror(3)
+    assert moe.strerror(99) == "unknown error"
