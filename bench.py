@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the fused MXFP4 MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode]
+
+A step is one whole layer call (routing, shared append, sort, gate, GEMM1 +
+SwiGLU, GEMM2, finalize) on one batch of seeded synthetic inputs that are
+resident in HBM before timing starts. Steps are replayed from a captured
+graph and alternate between two copies of the weights, so no step finds the
+previous step's weights in L2 or the Infinity Cache. Prints one JSON line.
+
+The dominant kernel (GEMM1) is also timed live with HIP events recorded by
+the library between the stages of the chain; its algorithmic bytes (decode
+workloads) or FLOPs (prefill) per launch over that time give the roofline
+fraction. The CPU baseline is the fp64 oracle on a bounded token sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+METRIC = "MoE layer tokens/s and µs/layer; achieved HBM GB/s (decode), MFMA % (prefill)"
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--config", default="decode",
+                   help="tiny | decode | decode_ep | shared_clamp | prefill")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=15.0,
+                   help="target CPU time of one oracle sample run")
+    p.add_argument("--calib-copy-mib", type=int, default=0,
+                   help="first run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+def workload_name(s) -> str:
+    parts = [f"T={s.T}", f"E={s.E}" + (f"/{s.E_g}@{s.expert_offset}" if s.E != s.E_g else ""),
+             f"topk={s.topk}"]
+    if s.S:
+        parts.append(f"shared={s.S}")
+    parts += [f"H={s.H}", f"I={s.I}", f"BlockN={s.B}"]
+    if s.swiglu_limit > 0:
+        parts.append(f"clamp={s.swiglu_limit:g}")
+    if s.routing == "zipf":
+        parts.append(f"zipf={s.zipf_s:g}")
+    return f"MXFP4 MoE layer ({s.name}): " + " ".join(parts) + f", W4A16 {s.a_dtype} activations"
+
+
+def cpu_baseline(s, inp, target_s: float) -> dict:
+    """The oracle (as it stands) on a prefix of the tokens, doubling the prefix
+    until one run takes at least half the target time."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: report what numpy could use
+        cores = os.cpu_count() or 1
+    n, best = 1, None
+    while True:
+        n = min(n, s.T)
+        sub = s.replace(T=n)
+        sl = {k: (v[:n] if k in ("x", "logits", "shared", "topk_ids", "topk_w") else v)
+              for k, v in inp.items()}
+        t0 = time.perf_counter()
+        oracle.reference_forward(sub, sl)
+        dt = time.perf_counter() - t0
+        best = (n, dt)
+        if dt >= target_s / 2 or n >= s.T:
+            break
+        n *= 2
+    n, dt = best
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {n} of {s.T} tokens of the {s.name} workload, whole layer in fp64 "
+                      f"NumPy, one run of {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer has no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import mxfp4_weight_expert_amd as moe
+    from workloads import CONFIGS, config_seed, make_inputs
+
+    moe.load_library()  # fails loudly if the HIP library is not built
+    s = CONFIGS[args.config]
+    dev_id = 0
+    torch.cuda.set_device(dev_id)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+    log(f"[bench] generating {args.config} inputs")
+    inp = make_inputs(s, config_seed(args.config))
+    shp = moe.Shape(T=s.T, E=s.E, E_global=s.E_g, topk=s.topk, H=s.H, I=s.I, block_n=s.B, S=s.S,
+                    expert_offset=s.expert_offset, swiglu_limit=s.swiglu_limit,
+                    shared_scale=s.shared_scale, a_dtype=s.a_dtype)
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+
+    x = bf16(inp["x"])
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    shared = bf16(inp["shared"]) if s.S else None
+    wbytes = sum(inp[k].nbytes for k in ("w13", "s13", "w2", "s2"))
+    nsets = 2 if wbytes >= (1 << 30) else max(2, int((1 << 30) // max(wbytes, 1)) + 1)
+    nsets = min(nsets, 64)
+    sets = []
+    for _ in range(nsets):
+        sets.append({k: torch.from_numpy(inp[k]).cuda() for k in ("w13", "s13", "w2", "s2")})
+    ws = torch.empty(moe.query(shp), dtype=torch.uint8, device="cuda")
+    out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
+    del inp["w13"], inp["w2"]
+
+    def step(i, stream=None):
+        w = sets[i % nsets]
+        moe.forward(x, w["w13"], w["s13"], w["w2"], w["s2"], shp, router_logits=logits,
+                    shared_logits=shared, out=out, workspace=ws, stream=stream)
+
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    # eager warm-up, then one graph per weight set
+    for i in range(nsets):
+        step(i)
+    torch.cuda.synchronize()
+    graphs = []
+    cap = torch.cuda.Stream()
+    for i in range(nsets):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % nsets].replay()
+    torch.cuda.synchronize()
+
+    log(f"[bench] timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        graphs[i % nsets].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    log(f"[bench] {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+
+    # Per-stage timing of the chain (eager, same kernels), HIP events on the
+    # library's stream.
+    nst = moe.NUM_STAGES
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    for i in range(min(args.warmup, 3)):
+        step(i)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        w = sets[i % nsets]
+        moe.forward_timed(evs[i], x, w["w13"], w["s13"], w["w2"], w["s2"], shp,
+                          router_logits=logits, shared_logits=shared, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    stage_ms = [sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
+                for k in range(nst)]
+    stages = {n: round(v * 1e3, 2) for n, v in zip(moe.STAGE_NAMES, stage_ms)}
+    log(f"[bench] stage us: {stages}")
+
+    maps = moe.read_maps(ws, shp)
+    gate = maps["counters"][4:8].cpu().tolist()
+    counts = maps["counts"].cpu().numpy()
+    U_routed = int(np.count_nonzero(counts[: s.E]))
+    U = int(gate[1])
+    R = int(gate[2])
+    gemm1_ms = stage_ms[2]
+    tok_per_s = s.T / (ms_per_step / 1e3)
+    # GEMM1 algorithmic work per launch: W13 + its scales of every touched
+    # expert, x once, act written once (and the row -> slot map).
+    w13_expert_bytes = 2 * s.I * (s.H // 2 + s.H // 32)
+    gemm1_bytes = U * w13_expert_bytes + s.T * s.H * 2 + R * s.I * 2 + R * 4
+    gemm1_flops = 2.0 * R * s.H * 2 * s.I
+    layer_bytes = U * (w13_expert_bytes + s.H * (s.I // 2 + s.I // 32)) + s.T * s.H * 4 \
+        + s.T * s.E_g * 4
+    if R >= 64 * max(U, 1):  # prefill-like: the contraction dominates
+        roof = {"bound": "mfma", "achieved": round(gemm1_flops / (gemm1_ms / 1e3) / 1e12, 2),
+                "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gemm1_bytes / (gemm1_ms / 1e3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["kernel"] = "gemm1_tn_kernel"
+    roof["kernel_us"] = round(gemm1_ms * 1e3, 2)
+    roof["algorithmic_bytes" if roof["bound"] == "hbm" else "algorithmic_flops"] = \
+        gemm1_bytes if roof["bound"] == "hbm" else gemm1_flops
+
+    res = {
+        "metric": METRIC,
+        "value": round(tok_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded PCG64: N(0,1) bf16 x, N(0,1) router logits, uniform E2M1 "
+                "nibbles, E8M0 scales uniform in [118,127])",
+        "config": {"workload": workload_name(s), "T": s.T, "E": s.E, "E_global": s.E_g,
+                   "topk": s.topk, "S": s.S, "H": s.H, "I": s.I, "block_n": s.B,
+                   "touched_experts": U_routed, "rows": R, "gemm2_path": "dense" if gate[0] else "split",
+                   "layer_us": round(ms_per_step * 1e3, 2),
+                   "layer_hbm_GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
+                   "stage_us": stages, "weight_sets": nsets},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU baseline (oracle)")
+        inp2 = make_inputs(s, config_seed(args.config))
+        res["cpu_baseline"] = cpu_baseline(s, inp2, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -197,6 +197,28 @@ int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
                       const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
                       uint64_t workspace_bytes, void* stream);
 
+/*
+ * Stages of the launch chain, in order: routing (+ shared append), sort
+ * (count, scan, scatter) + GEMM2 gate, GEMM1 (+ SwiGLU), GEMM2 (split and
+ * dense kernels), finalize.
+ */
+#define MOE_NUM_STAGES 5
+
+/*
+ * moe_mxfp4_forward, with per-stage timing for measurement tools: before
+ * each of the MOE_NUM_STAGES stages and after the last one it records
+ * stage_events[i] (MOE_NUM_STAGES + 1 hipEvent_t created by the caller) on
+ * `stream`; elapsed time between events i and i+1 is stage i. Same work,
+ * kernels and results as moe_mxfp4_forward; not meant for graph capture.
+ * MOE_ERR_INVALID if stage_events or any of its entries is NULL.
+ */
+int moe_mxfp4_forward_timed(const void* x_dev, const float* router_logits_dev,
+                            const int32_t* topk_ids_dev, const float* topk_w_dev,
+                            const void* shared_logits_dev, const uint8_t* w13_dev,
+                            const uint8_t* s13_dev, const uint8_t* w2_dev, const uint8_t* s2_dev,
+                            const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
+                            uint64_t workspace_bytes, void* stream, void* const* stage_events);
+
 /* Static text for a return code. */
 const char* moe_mxfp4_strerror(int code);
 

@@ -11,13 +11,15 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-__all__ = ["Shape", "query", "workspace_layout", "forward", "strerror", "lib_path",
+__all__ = ["Shape", "query", "workspace_layout", "forward", "forward_timed", "strerror", "lib_path",
            "MoeError", "read_maps", "ADTYPE", "GEMM2_PATH", "load_library"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoe_mxfp4.so")
 
 MOE_OK = 0
+NUM_STAGES = 5  # route, sort + gate, GEMM1, GEMM2, finalize
+STAGE_NAMES = ("route", "sort_gate", "gemm1", "gemm2", "finalize")
 ADTYPE = {"bf16": 0, "mxfp8": 1}
 GEMM2_PATH = {"auto": -1, "split": 0, "dense": 1}
 
@@ -67,6 +69,8 @@ def load_library():
     lib.moe_mxfp4_forward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(_Shape),
                                       vp, vp, ctypes.c_uint64, vp]
     lib.moe_mxfp4_forward.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_timed.argtypes = lib.moe_mxfp4_forward.argtypes + [ctypes.c_void_p]
+    lib.moe_mxfp4_forward_timed.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -129,6 +133,27 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _call(fn, x, w13, s13, w2, s2, shape, router_logits, topk_ids, topk_w, shared_logits, out,
+          workspace, stream, extra):
+    import torch
+
+    for t in (x, w13, s13, w2, s2, router_logits, topk_ids, topk_w, shared_logits, out, workspace):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(query(shape), 256), dtype=torch.uint8, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    rc = fn(_ptr(x), _ptr(router_logits), _ptr(topk_ids), _ptr(topk_w), _ptr(shared_logits),
+            _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), ctypes.byref(shape.to_c()), _ptr(out),
+            _ptr(workspace), ctypes.c_uint64(workspace.numel()), ctypes.c_void_p(stream), *extra)
+    if rc != MOE_OK:
+        raise MoeError(rc, fn.__name__)
+    return out
+
+
 def forward(x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=None, topk_w=None,
             shared_logits=None, out=None, workspace=None, stream=None):
     """Run the layer; returns out (bf16 [T, H]).
@@ -139,26 +164,22 @@ def forward(x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=N
     at least query(shape) bytes (allocated here when None). All tensors must
     be contiguous and on the current device.
     """
-    import torch
+    return _call(load_library().moe_mxfp4_forward, x, w13, s13, w2, s2, shape, router_logits,
+                 topk_ids, topk_w, shared_logits, out, workspace, stream, ())
 
-    lib = load_library()
-    tensors = [x, w13, s13, w2, s2, router_logits, topk_ids, topk_w, shared_logits, out, workspace]
-    for t in tensors:
-        if t is not None and not t.is_contiguous():
-            raise ValueError("all tensors must be contiguous")
-    if out is None:
-        out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=x.device)
-    if workspace is None:
-        workspace = torch.empty(max(query(shape), 256), dtype=torch.uint8, device=x.device)
-    if stream is None:
-        stream = torch.cuda.current_stream(x.device).cuda_stream
-    rc = lib.moe_mxfp4_forward(_ptr(x), _ptr(router_logits), _ptr(topk_ids), _ptr(topk_w),
-                               _ptr(shared_logits), _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2),
-                               ctypes.byref(shape.to_c()), _ptr(out), _ptr(workspace),
-                               ctypes.c_uint64(workspace.numel()), ctypes.c_void_p(stream))
-    if rc != MOE_OK:
-        raise MoeError(rc, "moe_mxfp4_forward")
-    return out
+
+def forward_timed(events, x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=None,
+                  topk_w=None, shared_logits=None, out=None, workspace=None, stream=None):
+    """forward, recording NUM_STAGES + 1 torch.cuda.Event objects (enable_timing=True)
+    between the stages of the launch chain on the library's stream."""
+    if len(events) != NUM_STAGES + 1:
+        raise ValueError(f"need {NUM_STAGES + 1} events")
+    for e in events:
+        if not e.cuda_event:  # torch creates the HIP event on its first record
+            e.record()
+    arr = (ctypes.c_void_p * len(events))(*[ctypes.c_void_p(e.cuda_event) for e in events])
+    return _call(load_library().moe_mxfp4_forward_timed, x, w13, s13, w2, s2, shape,
+                 router_logits, topk_ids, topk_w, shared_logits, out, workspace, stream, (arr,))
 
 
 def read_maps(workspace, shape: Shape) -> dict:

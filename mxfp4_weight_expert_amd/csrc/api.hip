@@ -108,12 +108,15 @@ const char* moe_mxfp4_strerror(int code) {
   }
 }
 
-int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
-                      const int32_t* topk_ids_dev, const float* topk_w_dev,
-                      const void* shared_logits_dev, const uint8_t* w13_dev,
-                      const uint8_t* s13_dev, const uint8_t* w2_dev, const uint8_t* s2_dev,
-                      const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
-                      uint64_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_t* topk_ids_dev,
+                 const float* topk_w_dev, const void* shared_logits_dev, const uint8_t* w13_dev,
+                 const uint8_t* s13_dev, const uint8_t* w2_dev, const uint8_t* s2_dev,
+                 const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
+                 uint64_t workspace_bytes, void* stream, void* const* stage_events) {
   const int rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
   const moe_mxfp4_shape& s = *shape;
@@ -131,6 +134,11 @@ int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
     return MOE_ERR_WORKSPACE;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
+  int stage = 0;
+  auto mark = [&]() {
+    if (stage_events == nullptr) return hipSuccess;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[stage++]), st);
+  };
   uint8_t* ws = static_cast<uint8_t*>(workspace_dev);
   auto at = [&](uint64_t off) { return ws + off; };
   const int Kp = s.topk + s.S, Ep = s.E + s.S;
@@ -151,7 +159,7 @@ int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
   ra.route_ids = reinterpret_cast<int32_t*>(at(L.route_ids));
   ra.slot_expert = reinterpret_cast<int32_t*>(at(L.slot_expert));
   ra.slot_w = reinterpret_cast<float*>(at(L.slot_w));
-  if (launch_route(ra, st) != hipSuccess) return MOE_ERR_HIP;
+  if (mark() != hipSuccess || launch_route(ra, st) != hipSuccess) return MOE_ERR_HIP;
 
   SortArgs sa;
   sa.slot_expert = ra.slot_expert;
@@ -168,7 +176,7 @@ int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
   sa.vinfo = reinterpret_cast<int32_t*>(at(L.vinfo));
   sa.dense_tiles = reinterpret_cast<int32_t*>(at(L.dense_tiles));
   sa.counters = reinterpret_cast<int32_t*>(at(L.counters));
-  if (launch_sort_and_gate(sa, st) != hipSuccess) return MOE_ERR_HIP;
+  if (mark() != hipSuccess || launch_sort_and_gate(sa, st) != hipSuccess) return MOE_ERR_HIP;
 
   GemmArgs ga;
   ga.x = static_cast<const uint16_t*>(x_dev);
@@ -189,8 +197,8 @@ int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
   ga.limit = s.swiglu_limit;
   ga.act = reinterpret_cast<uint16_t*>(at(L.act));
   ga.y = reinterpret_cast<uint16_t*>(at(L.y));
-  if (launch_gemm1(ga, st) != hipSuccess) return MOE_ERR_HIP;
-  if (launch_gemm2(ga, st) != hipSuccess) return MOE_ERR_HIP;
+  if (mark() != hipSuccess || launch_gemm1(ga, st) != hipSuccess) return MOE_ERR_HIP;
+  if (mark() != hipSuccess || launch_gemm2(ga, st) != hipSuccess) return MOE_ERR_HIP;
 
   FinalizeArgs fa;
   fa.y = ga.y;
@@ -200,8 +208,38 @@ int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
   fa.Kp = Kp;
   fa.H = s.H;
   fa.out = static_cast<uint16_t*>(out_dev);
-  if (launch_finalize(fa, st) != hipSuccess) return MOE_ERR_HIP;
+  if (mark() != hipSuccess || launch_finalize(fa, st) != hipSuccess) return MOE_ERR_HIP;
+  if (mark() != hipSuccess) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_mxfp4_forward(const void* x_dev, const float* router_logits_dev,
+                      const int32_t* topk_ids_dev, const float* topk_w_dev,
+                      const void* shared_logits_dev, const uint8_t* w13_dev,
+                      const uint8_t* s13_dev, const uint8_t* w2_dev, const uint8_t* s2_dev,
+                      const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
+                      uint64_t workspace_bytes, void* stream) {
+  return forward_impl(x_dev, router_logits_dev, topk_ids_dev, topk_w_dev, shared_logits_dev,
+                      w13_dev, s13_dev, w2_dev, s2_dev, shape, out_dev, workspace_dev,
+                      workspace_bytes, stream, nullptr);
+}
+
+int moe_mxfp4_forward_timed(const void* x_dev, const float* router_logits_dev,
+                            const int32_t* topk_ids_dev, const float* topk_w_dev,
+                            const void* shared_logits_dev, const uint8_t* w13_dev,
+                            const uint8_t* s13_dev, const uint8_t* w2_dev, const uint8_t* s2_dev,
+                            const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
+                            uint64_t workspace_bytes, void* stream, void* const* stage_events) {
+  if (stage_events == nullptr) return MOE_ERR_INVALID;
+  for (int i = 0; i <= MOE_NUM_STAGES; ++i)
+    if (stage_events[i] == nullptr) return MOE_ERR_INVALID;
+  return forward_impl(x_dev, router_logits_dev, topk_ids_dev, topk_w_dev, shared_logits_dev,
+                      w13_dev, s13_dev, w2_dev, s2_dev, shape, out_dev, workspace_dev,
+                      workspace_bytes, stream, stage_events);
 }
 
 }  // extern "C"
