@@ -111,7 +111,8 @@ typedef struct moe_mxfp4_shape {
  * section 3: one byte tensor holds counters, chunk table, activations).
  * With K' = topk + S, E' = E + S and R_max = T * K':
  *
- *   counters      int32[64]       [0] number of chunks num_v, [4..7] gate word
+ *   counters      int32[64]       [0] number of chunks num_v, [1] number of
+ *                                 16-row units, [4..7] gate word
  *                                 {path (0 split, 1 dense), touched experts U,
  *                                 rows R, dense tiles}
  *   route_ids     int32[T*topk]   selected global ids (logits mode)
@@ -124,6 +125,9 @@ typedef struct moe_mxfp4_shape {
  *   expanded_idx  int32[T*K']     slot -> row, or -1
  *   vinfo         int32[kmax_v*4] chunk table (expert, first_row, rows, chunk)
  *   dense_tiles   int32[max_dense_tiles*4] dense-path tiles (same fields)
+ *   units16       int32[max_units16*4] the rows again in units of at most 16
+ *                 (same fields; counters[1] holds their number): the work list
+ *                 of the decode GEMMs
  *   act           [rows_pad, I]   bf16 (W4A16) or E4M3 bytes (W4A8)
  *   act_scales    uint8[rows_pad, I/32] E8M0 (W4A8 only)
  *   y             bf16[rows_pad, H] GEMM2 output in row order
@@ -142,6 +146,7 @@ typedef struct moe_mxfp4_ws_layout {
   uint64_t expanded_idx;
   uint64_t vinfo;
   uint64_t dense_tiles;
+  uint64_t units16;
   uint64_t act;
   uint64_t act_scales;
   uint64_t y;
@@ -149,6 +154,7 @@ typedef struct moe_mxfp4_ws_layout {
   uint64_t xs;
   int32_t kmax_v;          /* E' + (T*K') / B: bound on chunks */
   int32_t max_dense_tiles; /* E' + (T*K') / 128 */
+  int32_t max_units16;     /* E' + (T*K') / 16 */
   int32_t n_ranges;        /* slot ranges of the sort */
   int32_t rows_pad;        /* R_max plus padding rows */
 } moe_mxfp4_ws_layout;

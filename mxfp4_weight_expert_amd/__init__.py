@@ -38,9 +38,9 @@ class _Shape(ctypes.Structure):
 
 
 _LAYOUT_U64 = ("total_bytes", "counters", "route_ids", "slot_expert", "slot_w", "range_counts",
-               "counts", "offsets", "sorted_slot", "expanded_idx", "vinfo", "dense_tiles", "act",
+               "counts", "offsets", "sorted_slot", "expanded_idx", "vinfo", "dense_tiles", "units16", "act",
                "act_scales", "y", "xq", "xs")
-_LAYOUT_I32 = ("kmax_v", "max_dense_tiles", "n_ranges", "rows_pad")
+_LAYOUT_I32 = ("kmax_v", "max_dense_tiles", "max_units16", "n_ranges", "rows_pad")
 
 
 class _Layout(ctypes.Structure):
@@ -206,6 +206,7 @@ def read_maps(workspace, shape: Shape) -> dict:
         "expanded_idx": view(L["expanded_idx"], T * Kp, i32),
         "vinfo": view(L["vinfo"], L["kmax_v"] * 4, i32).view(-1, 4),
         "dense_tiles": view(L["dense_tiles"], L["max_dense_tiles"] * 4, i32).view(-1, 4),
+        "units16": view(L["units16"], L["max_units16"] * 4, i32).view(-1, 4),
         "act": view(L["act"], L["rows_pad"] * shape.I * (1 if shape.a_dtype == "mxfp8" else 2),
                     torch.uint8),
         "y": view(L["y"], L["rows_pad"] * shape.H, torch.bfloat16).view(L["rows_pad"], shape.H),

@@ -37,6 +37,11 @@ int check_shape(const moe_mxfp4_shape* s) {
   if (s->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (s->a_dtype != MOE_ADTYPE_BF16) return MOE_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(s->T) * (s->topk + s->S) > kMaxSlots) return MOE_ERR_UNSUPPORTED;
+  // the kernels address x and act with 32-bit buffer offsets
+  const int64_t rows = static_cast<int64_t>(s->T) * (s->topk + s->S) + 256;
+  if (static_cast<int64_t>(s->T) * s->H * 2 >= (int64_t(1) << 31) ||
+      rows * s->I * 2 >= (int64_t(1) << 31))
+    return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -46,6 +51,7 @@ void carve(const moe_mxfp4_shape* s, moe_mxfp4_ws_layout* L) {
   const bool a8 = s->a_dtype == MOE_ADTYPE_MXFP8;
   L->kmax_v = static_cast<int32_t>(Ep + slots / s->block_n);
   L->max_dense_tiles = static_cast<int32_t>(Ep + slots / kDenseMT);
+  L->max_units16 = static_cast<int32_t>(Ep + slots / 16);
   L->n_ranges = static_cast<int32_t>(slots == 0 ? 1 : (slots + kRangeSlots - 1) / kRangeSlots);
   const uint64_t pad = s->block_n > kDenseMT ? s->block_n : kDenseMT;
   L->rows_pad = static_cast<int32_t>(slots + pad);
@@ -67,6 +73,7 @@ void carve(const moe_mxfp4_shape* s, moe_mxfp4_ws_layout* L) {
   L->expanded_idx = take(slots * 4);
   L->vinfo = take(static_cast<uint64_t>(L->kmax_v) * 16);
   L->dense_tiles = take(static_cast<uint64_t>(L->max_dense_tiles) * 16);
+  L->units16 = take(static_cast<uint64_t>(L->max_units16) * 16);
   L->act = take(rp * I * (a8 ? 1 : 2));
   L->act_scales = take(a8 ? rp * I / 32 : 0);
   L->y = take(rp * H * 2);
@@ -174,6 +181,7 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   sa.sorted_slot = reinterpret_cast<int32_t*>(at(L.sorted_slot));
   sa.expanded_idx = reinterpret_cast<int32_t*>(at(L.expanded_idx));
   sa.vinfo = reinterpret_cast<int32_t*>(at(L.vinfo));
+  sa.units16 = reinterpret_cast<int32_t*>(at(L.units16));
   sa.dense_tiles = reinterpret_cast<int32_t*>(at(L.dense_tiles));
   sa.counters = reinterpret_cast<int32_t*>(at(L.counters));
   if (mark() != hipSuccess || launch_sort_and_gate(sa, st) != hipSuccess) return MOE_ERR_HIP;
@@ -185,15 +193,19 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   ga.w2 = w2_dev;
   ga.s2 = s2_dev;
   ga.vinfo = sa.vinfo;
+  ga.units16 = sa.units16;
   ga.dense_tiles = sa.dense_tiles;
   ga.counters = sa.counters;
   ga.sorted_slot = sa.sorted_slot;
+  ga.T = s.T;
+  ga.rows_pad = L.rows_pad;
   ga.H = s.H;
   ga.I = s.I;
   ga.Kp = Kp;
   ga.B = s.block_n;
   ga.kmax_v = L.kmax_v;
   ga.max_dense_tiles = L.max_dense_tiles;
+  ga.max_units16 = L.max_units16;
   ga.limit = s.swiglu_limit;
   ga.act = reinterpret_cast<uint16_t*>(at(L.act));
   ga.y = reinterpret_cast<uint16_t*>(at(L.y));

@@ -19,10 +19,12 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
 constexpr int kMaxExperts = 2048;  // E + S
 constexpr int kRangeSlots = 4096;  // slots per sort range (one wave each)
+constexpr int kSmallSlots = 8192;  // up to this many slots the sort runs in one block
 constexpr int kGateTau = 64;       // dense GEMM2 when rows >= kGateTau * touched experts
 constexpr int kDenseMT = 128;      // dense-path row tile
 constexpr int kCounterWords = 64;
 constexpr int kCtrNumV = 0;
+constexpr int kCtrNumU = 1;        // 16-row units (decode GEMM work list)
 constexpr int kCtrGate = 4;        // 4 words: path, U, R, dense tiles
 
 // ---------------------------------------------------------------- bf16 bits
@@ -36,12 +38,20 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return static_cast<uint16_t>(u >> 16);
 }
+// Two floats -> packed bf16 (lo in bits 0..15), round to nearest even, with
+// the gfx950 packed convert (one instruction, no branches).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // -------------------------------------------------------------- wave helpers
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+// Wave index in the block, as a value the compiler knows is wave-uniform
+// (kept in scalar registers; buffer descriptors built from it stay scalar).
+__device__ __forceinline__ int wave_index() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+}
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
@@ -71,6 +81,29 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   }
   return v;
 }
+// Wave-wide max of 64-bit values by DPP row shifts and row broadcasts (no
+// LDS traffic); every lane receives the result.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_max_step(uint64_t v) {
+  const int lo = static_cast<int>(static_cast<uint32_t>(v));
+  const int hi = static_cast<int>(static_cast<uint32_t>(v >> 32));
+  const uint32_t nlo = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xf, false));
+  const uint32_t nhi = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xf, false));
+  const uint64_t n = (static_cast<uint64_t>(nhi) << 32) | nlo;
+  return n > v ? n : v;
+}
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  v = dpp_max_step<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_max_step<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_max_step<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_max_step<0x118, 0xf>(v);  // row_shr:8  -> lane 15 of each row: row max
+  v = dpp_max_step<0x142, 0xa>(v);  // row_bcast:15 -> rows 1, 3
+  v = dpp_max_step<0x143, 0xc>(v);  // row_bcast:31 -> rows 2, 3: lane 63 = wave max
+  const uint32_t lo = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(static_cast<int>(static_cast<uint32_t>(v >> 32)), 63);
+  return (static_cast<uint64_t>(hi) << 32) | lo;
+}
+
 // Inclusive prefix sum across the wave.
 __device__ __forceinline__ int wave_incl_scan(int v) {
   const int l = lane_id();

@@ -11,45 +11,66 @@
 
 namespace moe {
 
+// Grid: T x nblk blocks; block (t, b) covers 16-byte vectors [b*256, b*256 + 256)
+// of token t's output row. Wave 0 first compacts the token's valid columns
+// (row >= 0) into LDS, keeping their order, so the accumulation loop has no
+// branches and issues its row loads back to back.
 __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restrict__ y,
                                                        const int32_t* __restrict__ expanded_idx,
                                                        const float* __restrict__ slot_w, int Kp,
-                                                       int H, uint16_t* __restrict__ out) {
+                                                       int H, int nblk, uint16_t* __restrict__ out) {
   __shared__ int32_t s_row[kMaxTopK + kMaxShared];
   __shared__ float s_w[kMaxTopK + kMaxShared];
-  const int t = blockIdx.x;
-  if (threadIdx.x < Kp) {
-    s_row[threadIdx.x] = expanded_idx[static_cast<size_t>(t) * Kp + threadIdx.x];
-    s_w[threadIdx.x] = slot_w[static_cast<size_t>(t) * Kp + threadIdx.x];
+  __shared__ int s_n;
+  const int t = blockIdx.x / nblk;
+  const int b = blockIdx.x - t * nblk;
+  if (threadIdx.x < kWave) {
+    const int k = threadIdx.x;
+    const int row = k < Kp ? expanded_idx[static_cast<size_t>(t) * Kp + k] : -1;
+    const bool valid = row >= 0;
+    const uint64_t m = ballot(valid);
+    if (valid) {
+      const int pos = popc_below(m);
+      s_row[pos] = row;
+      s_w[pos] = slot_w[static_cast<size_t>(t) * Kp + k];
+    }
+    if (k == 0) s_n = __popcll(m);
   }
   __syncthreads();
-  const int nvec = H >> 3;  // 8 bf16 per 16-byte vector
-  for (int c = threadIdx.x; c < nvec; c += blockDim.x) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < Kp; ++k) {
-      const int row = s_row[k];
-      if (row < 0) continue;
-      const float w = s_w[k];
-      const uint4 v = ld16(y + static_cast<size_t>(row) * H + c * 8);
-      const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+  const int c = b * 256 + threadIdx.x;  // 16-byte vector index in the row
+  if (c >= (H >> 3)) return;
+  const int n = s_n;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  auto add = [&](const uint4& v, float w) {
+    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += w * __uint_as_float(d[q] << 16);
-        acc[2 * q + 1] += w * __uint_as_float(d[q] & 0xffff0000u);
-      }
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += w * __uint_as_float(d[q] << 16);
+      acc[2 * q + 1] += w * __uint_as_float(d[q] & 0xffff0000u);
     }
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    *reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * H + c * 8) = o;
+  };
+  const uint16_t* yc = y + static_cast<size_t>(c) * 8;
+  int k = 0;
+  for (; k + 8 <= n; k += 8) {
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = ld16(yc + static_cast<size_t>(s_row[k + u]) * H);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) add(v[u], s_w[k + u]);
   }
+  for (; k < n; ++k) add(ld16(yc + static_cast<size_t>(s_row[k]) * H), s_w[k]);
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(out + static_cast<size_t>(t) * H + c * 8) = o;
 }
 
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(finalize_kernel, dim3(a.T), dim3(256), 0, st, a.y, a.expanded_idx, a.slot_w,
-                     a.Kp, a.H, a.out);
+  const int nblk = ((a.H >> 3) + 255) / 256;
+  hipLaunchKernelGGL(finalize_kernel, dim3(a.T * nblk), dim3(256), 0, st, a.y, a.expanded_idx,
+                     a.slot_w, a.Kp, a.H, nblk, a.out);
   return hipGetLastError();
 }
 

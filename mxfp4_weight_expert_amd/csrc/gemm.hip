@@ -39,7 +39,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_tn_kernel(
   const int nitems = counters[kCtrNumV] * ftiles;
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
   const int nkb = H >> 7;
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nitems; item += gridDim.x * 4) {
+  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
     const int v = item / ftiles;
     const int ft = item - v * ftiles;
     const int4 vi = reinterpret_cast<const int4*>(vinfo)[v];
@@ -126,7 +126,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_tn_kernel(
   const int nitems = (DENSE ? counters[kCtrGate + 3] : counters[kCtrNumV]) * htiles;
   const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
   const int nkb = I >> 7;
-  for (int item = blockIdx.x * 4 + (threadIdx.x >> 6); item < nitems; item += gridDim.x * 4) {
+  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
     const int v = item / htiles;
     const int ht = item - v * htiles;
     const int4 vi = reinterpret_cast<const int4*>(items)[v];
@@ -178,6 +178,314 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_tn_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Decode GEMMs: a wave streams a 64-row weight block (four 16-row MFMA tiles)
+// against one 16-row sub-tile of a chunk. K advances in 128-element steps; a
+// ring of D steps of weight and activation loads stays in flight ahead of the
+// MFMAs. The chunk's token rows are the N side; each 8-bf16 activation
+// fragment feeds the four weight tiles.
+//
+// Load mix, as measured on MI355X: per-step byte loads of scales and
+// activation loads from up to 16 distinct rows each touch 16 cache lines per
+// instruction and cut the weight stream's bandwidth nearly in half. So the
+// block's 64 scale rows are copied once per item into a per-wave LDS block
+// with coalesced 16-byte loads and read from LDS each step, and activations
+// use buffer loads whose out-of-range offset (lanes past the chunk's last
+// row) returns zero without touching memory.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kNoRow = 0x80000000u;  // buffer offset beyond any operand
+// s_waitcnt immediate (gfx9 encoding): vmcnt = 0, expcnt and lgkmcnt not waited.
+constexpr int kWaitVmcnt0 = 0x0f70;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), bytes,
+                                           0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, v), r,
+                                        off, 0, 0);
+}
+
+// Copy `bytes` (a multiple of 16) from global to this wave's LDS block.
+__device__ __forceinline__ void wave_copy_to_lds(uint8_t* lds, const uint8_t* src, int bytes) {
+  for (int off = lane_id() * 16; off < bytes; off += kWave * 16)
+    *reinterpret_cast<uint4*>(lds + off) = ld16(src + off);
+}
+
+// acc[t] += W_tile_t (16 x K) * B^T for one sub-tile of token rows.
+// wp: lane's weight-row pointer of tile 0, offset by g*16 bytes; tile t is
+// wofs[t] bytes further (wave-uniform). ls: lane's scale row in LDS, offset by
+// g; tile t is lofs[t] bytes further. brs/boff: buffer and byte offset of the
+// lane's B row plus g*64 bytes (kNoRow for lanes past the chunk's end).
+// D divides nkb, so the unrolled body has no tail branches: the
+// vector-memory counter retires loads in issue order, and straight-line code
+// lets every wait cover only the step it needs.
+template <int D>
+__device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (&wofs)[4],
+                                             const uint8_t* ls, const uint32_t (&lofs)[4], int nkb,
+                                             __amdgpu_buffer_rsrc_t brs, uint32_t boff,
+                                             f32x4_t (&acc)[4]) {
+  uint4 w[D][4], xb[D][4];
+  // Prologue in slot order (pinned), matching the steady-state issue order.
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xb[d][j] = bld16(brs, boff + d * 256 + j * 16);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + d * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int last = nkb - 1;
+  // One ring step: multiply slot d (step kb), then refill it with step
+  // kb + D (near the end the last step again; those loads are never used).
+  auto step = [&](int kb, int d) {
+    float sc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sc[t] = e8m0_scale_operand(ls[lofs[t] + kb * 4]);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint32_t ww[4] = {w[d][t].x, w[d][t].y, w[d][t].z, w[d][t].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[t] = mfma16x16x32(decode_fp4x8(ww[j], sc[t]), as_bf16x8(xb[d][j]), acc[t]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    const int nk = min(kb + D, last);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xb[d][j] = bld16(brs, boff + nk * 256 + j * 16);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + nk * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The first ring cycle is peeled: the loop is then entered with loads
+  // pending in the same order as on every later iteration, so its waits
+  // cover only the slot being consumed.
+#pragma unroll
+  for (int d = 0; d < D; ++d) step(d, d);
+  for (int kb0 = D; kb0 < nkb; kb0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(kb0 + d, d);
+  }
+}
+
+#ifndef MOE_MAX_RING_DEPTH
+#define MOE_MAX_RING_DEPTH 2
+#endif
+// Largest ring depth <= MOE_MAX_RING_DEPTH that divides the step count.
+inline int ring_depth(int nkb) {
+  for (int d = MOE_MAX_RING_DEPTH; d > 1; --d)
+    if (nkb % d == 0) return d;
+  return 1;
+}
+
+// GEMM1 + SwiGLU, decode shape. Item = (16-row unit, 32-feature group):
+// tiles are gate rows f0+[0,16), up rows I+f0+[0,16), gate f0+16+[0,16),
+// up I+f0+16+[0,16). Dynamic LDS: 4 waves x 2H bytes (the group's 32 gate
+// and 32 up scale rows).
+template <int D>
+__global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
+    const uint8_t* __restrict__ s13, const int32_t* __restrict__ units,
+    const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int T, int H,
+    int I, int Kp, float limit, uint16_t* __restrict__ act) {
+  extern __shared__ uint8_t lds_scales[];
+  const int lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  const int groups = I >> 5;
+  const int nitems = counters[kCtrNumU] * groups;
+  const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
+  const int nkb = H >> 7;
+  const int blk = 32 * static_cast<int>(srow);  // 32 scale rows = H bytes
+  uint8_t* my = lds_scales + wave_index() * 2 * blk;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(T) * H * 2));
+  const uint32_t wofs[4] = {0u, static_cast<uint32_t>(I * wrow), static_cast<uint32_t>(16 * wrow),
+                            static_cast<uint32_t>((I + 16) * wrow)};
+  const uint32_t lofs[4] = {0u, static_cast<uint32_t>(blk), static_cast<uint32_t>(16 * srow),
+                            static_cast<uint32_t>(blk + 16 * srow)};
+  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
+    const int u = item / groups;
+    const int f0 = (item - u * groups) * 32;
+    const int4 ui = reinterpret_cast<const int4*>(units)[u];
+    const int e = ui.x, r0 = ui.y, nrows = ui.z;
+    const size_t row0 = static_cast<size_t>(e) * 2 * I + f0;
+    const uint8_t* sg = s13 + row0 * srow;
+    wave_copy_to_lds(my, sg, blk);
+    wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
+    const uint8_t* wp = w13 + (row0 + r) * wrow + g * 16;
+    const bool valid = r < nrows;
+    const int tok = sorted_slot[r0 + min(r, nrows - 1)] / Kp;
+    const uint32_t boff = valid ? static_cast<uint32_t>(tok) * H * 2 + g * 64 : kNoRow;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    stream_block<D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, boff, acc);
+    // rows past the unit's end fall outside the buffer: stores dropped
+    const __amdgpu_buffer_rsrc_t ars =
+        make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
+    const uint32_t aoff = static_cast<uint32_t>(r) * I * 2 + (f0 + g * 4) * 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const f32x4_t& ag = acc[2 * h];
+      const f32x4_t& au = acc[2 * h + 1];
+      uint2 pk;
+      pk.x = pack_bf16x2(swiglu(ag[0], au[0], limit), swiglu(ag[1], au[1], limit));
+      pk.y = pack_bf16x2(swiglu(ag[2], au[2], limit), swiglu(ag[3], au[3], limit));
+      bst8(ars, aoff + h * 32, pk);
+    }
+  }
+}
+
+// GEMM2 split path, decode shape, long K. Item = (16-row unit, 64 output
+// rows of H). Dynamic LDS: 4 waves x 2I bytes (the 64 rows' scales).
+template <int D>
+__global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
+    const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2,
+    const uint8_t* __restrict__ s2, const int32_t* __restrict__ units,
+    const int32_t* __restrict__ counters, int H, int I, uint16_t* __restrict__ y) {
+  if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
+  extern __shared__ uint8_t lds_scales[];
+  const int lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  const int quads = H >> 6;
+  const int nitems = counters[kCtrNumU] * quads;
+  const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
+  const int nkb = I >> 7;
+  const int blk = 64 * static_cast<int>(srow);  // = 2I bytes
+  uint8_t* my = lds_scales + wave_index() * blk;
+  const uint32_t wofs[4] = {0u, static_cast<uint32_t>(16 * wrow), static_cast<uint32_t>(32 * wrow),
+                            static_cast<uint32_t>(48 * wrow)};
+  const uint32_t lofs[4] = {0u, static_cast<uint32_t>(16 * srow), static_cast<uint32_t>(32 * srow),
+                            static_cast<uint32_t>(48 * srow)};
+  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
+    const int u = item / quads;
+    const int h0 = (item - u * quads) * 64;
+    const int4 ui = reinterpret_cast<const int4*>(units)[u];
+    const int e = ui.x, r0 = ui.y, nrows = ui.z;
+    const size_t row0 = static_cast<size_t>(e) * H + h0;
+    wave_copy_to_lds(my, s2 + row0 * srow, blk);
+    const uint8_t* wp = w2 + (row0 + r) * wrow + g * 16;
+    // unit-relative buffers: rows past the unit's end read 0 / drop stores
+    const __amdgpu_buffer_rsrc_t ars =
+        make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
+    const __amdgpu_buffer_rsrc_t yrs =
+        make_rsrc(y + static_cast<size_t>(r0) * H, static_cast<uint32_t>(nrows) * H * 2);
+    const uint32_t boff = static_cast<uint32_t>(r) * I * 2 + g * 64;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    stream_block<D>(wp, wofs, my + r * srow + g, lofs, nkb, ars, boff, acc);
+    const uint32_t yoff = static_cast<uint32_t>(r) * H * 2 + (h0 + g * 4) * 2;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      uint2 pk;
+      pk.x = pack_bf16x2(acc[t][0], acc[t][1]);
+      pk.y = pack_bf16x2(acc[t][2], acc[t][3]);
+      bst8(yrs, yoff + t * 32, pk);
+    }
+  }
+}
+
+// GEMM2 split path for short K (NKB = I/128 <= 4 steps), balanced stream.
+// The work unit is a 16-row tile of one 16-row unit's output over the full
+// K. Waves own equal contiguous ranges of the unit-major tile list, so the
+// last wave ends at most one tile after the first. Within the part of its
+// range that falls in one unit, a wave keeps the unit's activation fragments
+// in registers and streams tiles through a ring kStreamAhead tiles deep;
+// each tile's scales come in with one 16-byte load per lane (the row's I/32
+// bytes). The ring is unrolled by kStreamAhead; iterations past the range
+// recompute the last tile and their stores fall outside the unit's output
+// buffer, so the hardware drops them (no branches in the stream).
+#ifndef MOE_STREAM_AHEAD
+#define MOE_STREAM_AHEAD 4
+#endif
+constexpr int kStreamAhead = MOE_STREAM_AHEAD;
+
+template <int NKB>
+__global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
+    const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2,
+    const uint8_t* __restrict__ s2, const int32_t* __restrict__ units,
+    const int32_t* __restrict__ counters, int H, int I, uint16_t* __restrict__ y) {
+  if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
+  const int lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  const int tpu = H >> 4;  // tiles per unit
+  const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave_index();
+  int64_t t = total * wid / nwaves;
+  const int64_t t_end = total * (wid + 1) / nwaves;
+  const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
+  const uint32_t tstride = static_cast<uint32_t>(16 * wrow);
+  const uint32_t sstride = static_cast<uint32_t>(16 * srow);
+  while (t < t_end) {
+    const int u = static_cast<int>(t / tpu);
+    const int h0 = static_cast<int>(t - static_cast<int64_t>(u) * tpu);  // first tile
+    const int nt = static_cast<int>(min(t_end, static_cast<int64_t>(u + 1) * tpu) - t);
+    const int4 ui = reinterpret_cast<const int4*>(units)[u];
+    const int e = ui.x, r0 = ui.y, nrows = ui.z;
+    const size_t row0 = static_cast<size_t>(e) * H + h0 * 16 + r;
+    const uint8_t* wp = w2 + row0 * wrow + g * 16;
+    const uint8_t* sp = s2 + row0 * srow;
+    const __amdgpu_buffer_rsrc_t ars =
+        make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
+    const __amdgpu_buffer_rsrc_t yrs =
+        make_rsrc(y + static_cast<size_t>(r0) * H, static_cast<uint32_t>(nrows) * H * 2);
+    const uint32_t boff = static_cast<uint32_t>(r) * I * 2 + g * 64;
+    const uint32_t yrow = static_cast<uint32_t>(r) * H * 2 + (h0 * 16 + g * 4) * 2;
+    uint4 xa[NKB][4];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xa[kb][j] = bld16(ars, boff + kb * 256 + j * 16);
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 w[kStreamAhead][NKB];
+    uint4 sc[kStreamAhead];  // the lane row's scale bytes (I/32 <= 16)
+    // prologue in slot order (pinned): the loop head then sees the same
+    // pending-load order on entry as on every later iteration
+#pragma unroll
+    for (int a = 0; a < kStreamAhead; ++a) {
+      const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+      sc[a] = ld16(sp + ti * sstride);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
+      uint2 res[kStreamAhead];
+#pragma unroll
+      for (int a = 0; a < kStreamAhead; ++a) {
+        const int i = i0 + a;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const float s = e8m0_scale_operand((sw[kb] >> (8 * g)) & 0xffu);
+          const uint32_t ww[4] = {w[a][kb].x, w[a][kb].y, w[a][kb].z, w[a][kb].w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc = mfma16x16x32(decode_fp4x8(ww[j], s), as_bf16x8(xa[kb][j]), acc);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+        sc[a] = ld16(sp + ti * sstride);
+        res[a].x = pack_bf16x2(acc[0], acc[1]);
+        res[a].y = pack_bf16x2(acc[2], acc[3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int a = 0; a < kStreamAhead; ++a)
+        bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
+    }
+    t += nt;
+  }
+}
+
 static int grid_for(long items) {
   long blocks = (items + 3) / 4;
   if (blocks < 1) blocks = 1;
@@ -185,13 +493,27 @@ static int grid_for(long items) {
 }
 
 hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
+  if (a.B <= 32) {
+    const int grid = grid_for(static_cast<long>(a.max_units16) * (a.I / 32));
+    const size_t lds = static_cast<size_t>(4) * 2 * a.H;
+#define MOE_G1D(DD)                                                                               \
+  hipLaunchKernelGGL(gemm1_decode_kernel<DD>, dim3(grid), dim3(kGemmBlock), lds, st, a.x, a.w13,   \
+                     a.s13, a.units16, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp, a.limit,     \
+                     a.act)
+    switch (ring_depth(a.H / 128)) {
+      case 4: MOE_G1D(4); break;
+      case 3: MOE_G1D(3); break;
+      case 2: MOE_G1D(2); break;
+      default: MOE_G1D(1); break;
+    }
+#undef MOE_G1D
+    return hipGetLastError();
+  }
   const int grid = grid_for(static_cast<long>(a.kmax_v) * (a.I / 16));
 #define MOE_G1(N)                                                                              \
   hipLaunchKernelGGL(gemm1_tn_kernel<N>, dim3(grid), dim3(kGemmBlock), 0, st, a.x, a.w13, a.s13, \
                      a.vinfo, a.counters, a.sorted_slot, a.H, a.I, a.Kp, a.limit, a.act)
   switch (a.B) {
-    case 16: MOE_G1(1); break;
-    case 32: MOE_G1(2); break;
     case 64: MOE_G1(4); break;
     case 128: MOE_G1(8); break;
     default: MOE_G1(16); break;
@@ -201,32 +523,39 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
-  const int gsplit = grid_for(static_cast<long>(a.kmax_v) * (a.H / 16));
-  const int gdense = grid_for(static_cast<long>(a.max_dense_tiles) * (a.H / 16));
-  switch (a.B) {
-    case 16:
-      hipLaunchKernelGGL((gemm2_tn_kernel<1, false>), dim3(gsplit), dim3(kGemmBlock), 0, st, a.act,
-                         a.w2, a.s2, a.vinfo, a.counters, a.H, a.I, a.y);
-      break;
-    case 32:
-      hipLaunchKernelGGL((gemm2_tn_kernel<2, false>), dim3(gsplit), dim3(kGemmBlock), 0, st, a.act,
-                         a.w2, a.s2, a.vinfo, a.counters, a.H, a.I, a.y);
-      break;
-    case 64:
-      hipLaunchKernelGGL((gemm2_tn_kernel<4, false>), dim3(gsplit), dim3(kGemmBlock), 0, st, a.act,
-                         a.w2, a.s2, a.vinfo, a.counters, a.H, a.I, a.y);
-      break;
-    case 128:
-      hipLaunchKernelGGL((gemm2_tn_kernel<8, false>), dim3(gsplit), dim3(kGemmBlock), 0, st, a.act,
-                         a.w2, a.s2, a.vinfo, a.counters, a.H, a.I, a.y);
-      break;
-    default:
-      hipLaunchKernelGGL((gemm2_tn_kernel<16, false>), dim3(gsplit), dim3(kGemmBlock), 0, st,
-                         a.act, a.w2, a.s2, a.vinfo, a.counters, a.H, a.I, a.y);
-      break;
+  const int nkb2 = a.I / 128;
+  if (nkb2 <= 4) {
+#ifndef MOE_STREAM_GRID
+#define MOE_STREAM_GRID (256 * 3)
+#endif
+    const int gstream = MOE_STREAM_GRID;  // persistent: waves split the tile list evenly
+#define MOE_G2S(NK)                                                                      \
+  hipLaunchKernelGGL(gemm2_stream_kernel<NK>, dim3(gstream), dim3(kGemmBlock), 0, st,   \
+                     a.act, a.w2, a.s2, a.units16, a.counters, a.H, a.I, a.y)
+    switch (nkb2) {
+      case 1: MOE_G2S(1); break;
+      case 2: MOE_G2S(2); break;
+      case 3: MOE_G2S(3); break;
+      default: MOE_G2S(4); break;
+    }
+#undef MOE_G2S
+  } else {
+    const int gsplit = grid_for(static_cast<long>(a.max_units16) * (a.H / 64));
+    const size_t lds2 = static_cast<size_t>(4) * 2 * a.I;
+#define MOE_G2D(DD)                                                                           \
+  hipLaunchKernelGGL(gemm2_split_kernel<DD>, dim3(gsplit), dim3(kGemmBlock), lds2, st, a.act, \
+                     a.w2, a.s2, a.units16, a.counters, a.H, a.I, a.y)
+    switch (ring_depth(a.I / 128)) {
+      case 4: MOE_G2D(4); break;
+      case 3: MOE_G2D(3); break;
+      case 2: MOE_G2D(2); break;
+      default: MOE_G2D(1); break;
+    }
+#undef MOE_G2D
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  const int gdense = grid_for(static_cast<long>(a.max_dense_tiles) * (a.H / 16));
   hipLaunchKernelGGL((gemm2_tn_kernel<kDenseMT / 16, true>), dim3(gdense), dim3(kGemmBlock), 0, st,
                      a.act, a.w2, a.s2, a.dense_tiles, a.counters, a.H, a.I, a.y);
   return hipGetLastError();

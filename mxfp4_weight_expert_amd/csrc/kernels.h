@@ -28,6 +28,7 @@ struct SortArgs {
   int32_t* sorted_slot;   // [nslots]
   int32_t* expanded_idx;  // [nslots]
   int32_t* vinfo;         // [kmax_v, 4]
+  int32_t* units16;       // [max_units16, 4]: 16-row units
   int32_t* dense_tiles;   // [max_dense_tiles, 4]
   int32_t* counters;      // [kCounterWords]
 };
@@ -41,10 +42,11 @@ struct GemmArgs {
   const uint8_t* w2;         // [Ep, H, I/2]
   const uint8_t* s2;         // [Ep, H, I/32]
   const int32_t* vinfo;
+  const int32_t* units16;
   const int32_t* dense_tiles;
   const int32_t* counters;
   const int32_t* sorted_slot;
-  int H, I, Kp, B, kmax_v, max_dense_tiles;
+  int T, H, I, Kp, B, kmax_v, max_dense_tiles, max_units16, rows_pad;
   float limit;
   uint16_t* act;  // [rows_pad, I] bf16
   uint16_t* y;    // [rows_pad, H] bf16

@@ -37,9 +37,11 @@ __device__ __forceinline__ void write_shared_columns(const uint16_t* shared_logi
   }
 }
 
-// One wave per token. NPL = logits held per lane (E_global <= 64 * NPL).
-// Selection: topk rounds of a wave-wide max over 64-bit keys
-// (ordered logit << 32 | ~id), so equal logits go to the lower id.
+// One wave per token. The token's logits become 64-bit keys (ordered logit
+// << 32 | ~id), NPL per lane (E_global <= 64 * NPL). Each of topk rounds takes
+// the wave-wide maximum key (DPP reduction) and removes it from its lane, so
+// keys come out in descending order: larger logit first, equal logits lower
+// id first.
 template <int NPL>
 __global__ __launch_bounds__(256) void route_logits_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ shared_logits, int T, int Eg,
@@ -49,27 +51,30 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const float* row = logits + static_cast<size_t>(t) * Eg;
+  // Unconditional loads (clamped index) so all of them are in flight at once.
+  float lv[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) lv[j] = row[min(lane + kWave * j, Eg - 1)];
   uint64_t key[NPL];
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int idx = lane + kWave * j;
-    key[j] = 0;
-    if (idx < Eg)
-      key[j] = (static_cast<uint64_t>(order_bits(row[idx])) << 32) | static_cast<uint32_t>(~idx);
+    key[j] = idx < Eg ? ((static_cast<uint64_t>(order_bits(lv[j])) << 32) |
+                         static_cast<uint32_t>(~idx))
+                      : 0ull;
   }
   uint64_t lmax = 0;
 #pragma unroll
   for (int j = 0; j < NPL; ++j) lmax = key[j] > lmax ? key[j] : lmax;
-
   uint64_t mine = 0;  // lane r keeps the r-th selected key
   for (int r = 0; r < topk; ++r) {
-    const uint64_t m = wave_max_u64(lmax);
+    const uint64_t m = wave_max_u64_dpp(lmax);
     if (lane == r) mine = m;
-    if (lmax == m) {  // exactly one lane holds the winner (ids are distinct)
+    if (lmax == m) {  // the one lane holding the winner (keys are distinct)
       lmax = 0;
 #pragma unroll
       for (int j = 0; j < NPL; ++j) {
-        if (key[j] == m) key[j] = 0;
+        key[j] = key[j] == m ? 0ull : key[j];
         lmax = key[j] > lmax ? key[j] : lmax;
       }
     }
@@ -119,15 +124,16 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t st) {
                        a.slot_expert, a.slot_w);
     return hipGetLastError();
   }
-  const int npl = (a.Eg + kWave - 1) / kWave;
-#define MOE_ROUTE(N)                                                                             \
+#define MOE_ROUTE(N)                                                                        \
   hipLaunchKernelGGL(route_logits_kernel<N>, grid, block, 0, st, a.logits, a.shared_logits, a.T, \
                      a.Eg, a.topk, a.S, a.E, a.expert_offset, a.shared_scale, a.route_ids,       \
                      a.slot_expert, a.slot_w)
+  const int npl = (a.Eg + kWave - 1) / kWave;
   if (npl <= 1) MOE_ROUTE(1);
   else if (npl <= 2) MOE_ROUTE(2);
   else if (npl <= 4) MOE_ROUTE(4);
   else if (npl <= 8) MOE_ROUTE(8);
+  else if (npl <= 14) MOE_ROUTE(14);
   else if (npl <= 16) MOE_ROUTE(16);
   else MOE_ROUTE(32);
 #undef MOE_ROUTE

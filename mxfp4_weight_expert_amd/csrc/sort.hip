@@ -10,101 +10,61 @@
 // path", sections 1-2 (one wave reads the sorted table and picks Dense or
 // Split; the other path's kernels launch and find zero items).
 //
-// The slots t*K' + k are cut into ranges of kRangeSlots, one wave each.
+// Up to kSmallSlots slots: one block does everything (histogram, scan,
+// chunk table, placement, gate). Beyond that the slots t*K' + k are cut into
+// ranges of kRangeSlots, one wave each:
 //   count:   per-range expert histograms (LDS atomics: order-free counts);
 //   scan:    per-expert exclusive scan over ranges, expert offsets, chunks;
-//   scatter: each wave walks its range in slot order, 64 slots at a time,
-//            ranking equal experts inside the wave by ballot/popcount
-//            (a wave multisplit), so rows follow slot order exactly.
+//   scatter: each wave walks its range in slot order, 64 slots at a time;
+//   gate:    one wave.
+// Placement ranks equal experts inside a wave by ballot/popcount (a wave
+// multisplit), so rows follow slot order exactly.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
-__global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ slot_expert,
-                                                         int nslots, int Ep, int n_ranges,
-                                                         int32_t* __restrict__ range_counts) {
-  extern __shared__ int32_t lds[];
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  const int r = blockIdx.x * 4 + w;
-  int32_t* h = lds + w * Ep;
-  for (int i = lane; i < Ep; i += kWave) h[i] = 0;
-  __syncthreads();
-  if (r < n_ranges) {
-    const int s0 = r * kRangeSlots;
-    const int s1 = min(nslots, s0 + kRangeSlots);
-    for (int s = s0 + lane; s < s1; s += kWave) {
-      const int e = slot_expert[s];
-      if (e >= 0) atomicAdd(&h[e], 1);
-    }
-  }
-  __syncthreads();
-  if (r < n_ranges)
-    for (int i = lane; i < Ep; i += kWave) range_counts[static_cast<size_t>(r) * Ep + i] = h[i];
-}
-
-// One block of 1024 threads. Turns range_counts into per-range bases, writes
-// counts, offsets, the chunk table and the chunk count.
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ range_counts,
-                                                         int n_ranges, int Ep, int B,
-                                                         int32_t* __restrict__ counts,
-                                                         int32_t* __restrict__ offsets,
-                                                         int32_t* __restrict__ vinfo,
-                                                         int32_t* __restrict__ counters) {
-  __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_wrows[16], s_wchunks[16];
+// Block of 1024 threads: from per-expert row counts (LDS), write counts,
+// offsets (exclusive scan, offsets[Ep] = R), the chunk table in expert-major
+// order and the chunk count, and the same table for 16-row units (the decode
+// GEMMs' work list). If next_row is given, it receives offsets[e].
+__device__ void block_scan_experts(const int32_t* s_cnt, int Ep, int B, int32_t* counts,
+                                   int32_t* offsets, int32_t* vinfo, int32_t* units16,
+                                   int32_t* counters, int32_t* next_row) {
+  __shared__ int32_t s_wrows[16], s_wchunks[16], s_wunits[16];
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  // 1) per expert: exclusive scan over ranges, in place.
-  for (int e = tid; e < Ep; e += 1024) {
-    int run = 0;
-    int r = 0;
-    for (; r + 8 <= n_ranges; r += 8) {
-      int c[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = range_counts[static_cast<size_t>(r + j) * Ep + e];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        range_counts[static_cast<size_t>(r + j) * Ep + e] = run;
-        run += c[j];
-      }
-    }
-    for (; r < n_ranges; ++r) {
-      const int c = range_counts[static_cast<size_t>(r) * Ep + e];
-      range_counts[static_cast<size_t>(r) * Ep + e] = run;
-      run += c;
-    }
-    s_cnt[e] = run;
-  }
-  __syncthreads();
-  // 2) each thread owns experts [e0, e0 + per) ; block scan of rows and chunks.
   const int per = (Ep + 1023) / 1024;
   const int e0 = tid * per;
-  int rows = 0, chunks = 0;
+  int rows = 0, chunks = 0, units = 0;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e < Ep) {
       rows += s_cnt[e];
       chunks += (s_cnt[e] + B - 1) / B;
+      units += (s_cnt[e] + 15) / 16;
     }
   }
-  const int rin = wave_incl_scan(rows), cin = wave_incl_scan(chunks);
+  const int rin = wave_incl_scan(rows), cin = wave_incl_scan(chunks), uin = wave_incl_scan(units);
   if (lane == kWave - 1) {
     s_wrows[w] = rin;
     s_wchunks[w] = cin;
+    s_wunits[w] = uin;
   }
   __syncthreads();
-  int rbase = 0, cbase = 0;
+  int rbase = 0, cbase = 0, ubase = 0;
   for (int j = 0; j < w; ++j) {
     rbase += s_wrows[j];
     cbase += s_wchunks[j];
+    ubase += s_wunits[j];
   }
-  int row = rbase + rin - rows, chunk = cbase + cin - chunks;
+  int row = rbase + rin - rows, chunk = cbase + cin - chunks, unit = ubase + uin - units;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= Ep) break;
     const int n = s_cnt[e];
     counts[e] = n;
     offsets[e] = row;
+    if (next_row != nullptr) next_row[e] = row;
     for (int c = 0; c * B < n; ++c) {
       int4 v;
       v.x = e;
@@ -113,65 +73,30 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ r
       v.w = c;
       reinterpret_cast<int4*>(vinfo)[chunk + c] = v;
     }
+    for (int c = 0; c * 16 < n; ++c) {
+      int4 v;
+      v.x = e;
+      v.y = row + c * 16;
+      v.z = min(16, n - c * 16);
+      v.w = c;
+      reinterpret_cast<int4*>(units16)[unit + c] = v;
+    }
     row += n;
     chunk += (n + B - 1) / B;
+    unit += (n + 15) / 16;
   }
   if (tid == 1023) {
     offsets[Ep] = row;  // thread 1023 owns the last experts (or none): row = R
     counters[kCtrNumV] = chunk;
-  }
-}
-
-__global__ __launch_bounds__(256) void sort_scatter_kernel(
-    const int32_t* __restrict__ slot_expert, int nslots, int Ep, int n_ranges, int key_bits,
-    const int32_t* __restrict__ range_base, const int32_t* __restrict__ offsets,
-    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ expanded_idx) {
-  extern __shared__ int32_t lds[];
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  const int r = blockIdx.x * 4 + w;
-  if (r >= n_ranges) return;  // wave-uniform; no block barrier below
-  int32_t* next = lds + w * Ep;  // next free row per expert for this range
-  for (int i = lane; i < Ep; i += kWave)
-    next[i] = offsets[i] + range_base[static_cast<size_t>(r) * Ep + i];
-  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int s0 = r * kRangeSlots;
-  const int s1 = min(nslots, s0 + kRangeSlots);
-  for (int c = s0; c < s1; c += kWave) {
-    const int s = c + lane;
-    const bool in = s < s1;
-    const int e = in ? slot_expert[s] : -1;
-    const bool valid = e >= 0;
-    const int key = valid ? e : Ep;  // Ep marks empty lanes
-    uint64_t match = ~0ull;
-    for (int b = 0; b < key_bits; ++b) {
-      const bool bit = (key >> b) & 1;
-      const uint64_t bal = ballot(bit);
-      match &= bit ? bal : ~bal;
-    }
-    const int rank = __popcll(match & lt);
-    int base = 0;
-    if (valid) base = next[e];
-    __builtin_amdgcn_wave_barrier();
-    if (valid) {
-      const int row = base + rank;
-      sorted_slot[row] = s;
-      expanded_idx[s] = row;
-      if (rank == 0) next[e] = base + __popcll(match);
-    } else if (in) {
-      expanded_idx[s] = -1;
-    }
-    __builtin_amdgcn_wave_barrier();
+    counters[kCtrNumU] = unit;
   }
 }
 
 // One wave: rows R and touched experts U from the counts; Dense iff
 // R >= kGateTau * U (or forced). On Dense it writes the per-expert 128-row
 // tile list. Gate word: {path, U, R, dense tiles (0 on Split)}.
-__global__ __launch_bounds__(64) void gemm2_gate_kernel(const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ offsets,
-                                                        int Ep, int force_path,
-                                                        int32_t* __restrict__ counters,
-                                                        int32_t* __restrict__ dense_tiles) {
+__device__ void gate_wave(const int32_t* counts, const int32_t* offsets, int Ep, int force_path,
+                          int32_t* counters, int32_t* dense_tiles) {
   const int lane = lane_id();
   int U = 0, R = 0;
   for (int e = lane; e < Ep; e += kWave) {
@@ -213,7 +138,232 @@ __global__ __launch_bounds__(64) void gemm2_gate_kernel(const int32_t* __restric
   }
 }
 
+// Rank 64 slots (one per lane, in slot order) among equal experts and place
+// them, so rows follow slot order within each expert. next[e] (LDS) is the
+// expert's next free row; the group's first lane advances it by the group
+// size after every lane of the group has read it.
+__device__ __forceinline__ void place_slots(int s, bool in, int e, int key_bits, int Ep,
+                                            int32_t* next, int32_t* sorted_slot,
+                                            int32_t* expanded_idx) {
+  const int lane = lane_id();
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const bool valid = e >= 0;
+  const int key = valid ? e : Ep;  // Ep marks empty lanes
+  uint64_t match = ~0ull;
+  for (int b = 0; b < key_bits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = ballot(bit);
+    match &= bit ? bal : ~bal;
+  }
+  const int rank = __popcll(match & lt);
+  int base = 0;
+  if (valid) base = next[e];
+  __builtin_amdgcn_wave_barrier();
+  if (valid) {
+    const int row = base + rank;
+    sorted_slot[row] = s;
+    expanded_idx[s] = row;
+    if (rank == 0) next[e] = base + __popcll(match);
+  } else if (in) {
+    expanded_idx[s] = -1;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// ------------------------------------------------------------- small shapes
+// Equal-expert groups among 64 slots (one per lane): each lane's match mask.
+__device__ __forceinline__ uint64_t match_mask(int key, int key_bits) {
+  uint64_t match = ~0ull;
+  for (int b = 0; b < key_bits; ++b) {
+    const bool bit = (key >> b) & 1;
+    const uint64_t bal = ballot(bit);
+    match &= bit ? bal : ~bal;
+  }
+  return match;
+}
+
+constexpr int kSmallWaves = 16;
+constexpr int kSmallGroups = kSmallSlots / (kSmallWaves * kWave);  // 64-slot groups per wave
+
+// One block of 16 waves. Wave w owns slots [w*rw, (w+1)*rw) (rw a multiple of
+// 64): it counts its experts into its own 16-bit histogram (the first lane of
+// each equal-expert group adds the group size: no atomics), the block scans
+// the histograms per expert (wave bases) and over experts (offsets, chunk
+// table), then each wave places its own slots in slot order. Wave 0 then runs
+// the GEMM2 gate. Dynamic LDS: kSmallWaves * Ep 16-bit counters.
+__global__ __launch_bounds__(1024) void sort_small_kernel(
+    const int32_t* __restrict__ slot_expert, int nslots, int Ep, int B, int key_bits,
+    int force_path, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ expanded_idx,
+    int32_t* __restrict__ vinfo, int32_t* __restrict__ units16, int32_t* __restrict__ counters,
+    int32_t* __restrict__ dense_tiles) {
+  extern __shared__ uint16_t s_wcnt[];  // [kSmallWaves][Ep]
+  __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_off[kMaxExperts];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i = tid; i < kSmallWaves * Ep; i += 1024) s_wcnt[i] = 0;
+  const int rw = ((nslots + kSmallWaves * kWave - 1) / (kSmallWaves * kWave)) * kWave;
+  const int s0 = w * rw;
+  int ex[kSmallGroups];
+#pragma unroll
+  for (int gi = 0; gi < kSmallGroups; ++gi)  // clamped, unconditional loads
+    ex[gi] = slot_expert[min(s0 + gi * kWave + lane, nslots - 1)];
+#pragma unroll
+  for (int gi = 0; gi < kSmallGroups; ++gi) {
+    const int s = s0 + gi * kWave + lane;
+    if (!(gi * kWave < rw && s < nslots)) ex[gi] = -1;
+  }
+  __syncthreads();
+  uint16_t* h = s_wcnt + w * Ep;
+#pragma unroll
+  for (int gi = 0; gi < kSmallGroups; ++gi) {
+    if (gi * kWave < rw) {
+      const uint64_t match = match_mask(ex[gi] >= 0 ? ex[gi] : Ep, key_bits);
+      if (ex[gi] >= 0 && __popcll(match & lt) == 0)
+        h[ex[gi]] = static_cast<uint16_t>(h[ex[gi]] + __popcll(match));
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  __syncthreads();
+  // per expert: exclusive scan over the waves (in place) and the total
+  for (int e = tid; e < Ep; e += 1024) {
+    int run = 0;
+#pragma unroll
+    for (int v = 0; v < kSmallWaves; ++v) {
+      const int c = s_wcnt[v * Ep + e];
+      s_wcnt[v * Ep + e] = static_cast<uint16_t>(run);
+      run += c;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  block_scan_experts(s_cnt, Ep, B, counts, offsets, vinfo, units16, counters, s_off);
+  __syncthreads();
+  // placement of this wave's slots
+#pragma unroll
+  for (int gi = 0; gi < kSmallGroups; ++gi) {
+    if (gi * kWave < rw) {
+      const int s = s0 + gi * kWave + lane;
+      const int e = ex[gi];
+      const bool valid = e >= 0;
+      const uint64_t match = match_mask(valid ? e : Ep, key_bits);
+      const int rank = __popcll(match & lt);
+      int base = 0;
+      if (valid) base = h[e];
+      __builtin_amdgcn_wave_barrier();
+      if (valid) {
+        const int row = s_off[e] + base + rank;
+        sorted_slot[row] = s;
+        expanded_idx[s] = row;
+        if (rank == 0) h[e] = static_cast<uint16_t>(base + __popcll(match));
+      } else if (s < nslots) {
+        expanded_idx[s] = -1;
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  if (w == 0) gate_wave(s_cnt, s_off, Ep, force_path, counters, dense_tiles);
+}
+
+// ------------------------------------------------------------ large shapes
+__global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ slot_expert,
+                                                         int nslots, int Ep, int n_ranges,
+                                                         int32_t* __restrict__ range_counts) {
+  extern __shared__ int32_t lds[];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int r = blockIdx.x * 4 + w;
+  int32_t* h = lds + w * Ep;
+  for (int i = lane; i < Ep; i += kWave) h[i] = 0;
+  __syncthreads();
+  if (r < n_ranges) {
+    const int s0 = r * kRangeSlots;
+    const int s1 = min(nslots, s0 + kRangeSlots);
+    for (int s = s0 + lane; s < s1; s += kWave) {
+      const int e = slot_expert[s];
+      if (e >= 0) atomicAdd(&h[e], 1);
+    }
+  }
+  __syncthreads();
+  if (r < n_ranges)
+    for (int i = lane; i < Ep; i += kWave) range_counts[static_cast<size_t>(r) * Ep + i] = h[i];
+}
+
+// One block of 1024 threads. Turns range_counts into per-range bases, writes
+// counts, offsets, the chunk table and the chunk count.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ range_counts,
+                                                         int n_ranges, int Ep, int B,
+                                                         int32_t* __restrict__ counts,
+                                                         int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ vinfo,
+                                                         int32_t* __restrict__ units16,
+                                                         int32_t* __restrict__ counters) {
+  __shared__ int32_t s_cnt[kMaxExperts];
+  const int tid = threadIdx.x;
+  // 1) per expert: exclusive scan over ranges, in place.
+  for (int e = tid; e < Ep; e += 1024) {
+    int run = 0;
+    int r = 0;
+    for (; r + 8 <= n_ranges; r += 8) {
+      int c[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = range_counts[static_cast<size_t>(r + j) * Ep + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        range_counts[static_cast<size_t>(r + j) * Ep + e] = run;
+        run += c[j];
+      }
+    }
+    for (; r < n_ranges; ++r) {
+      const int c = range_counts[static_cast<size_t>(r) * Ep + e];
+      range_counts[static_cast<size_t>(r) * Ep + e] = run;
+      run += c;
+    }
+    s_cnt[e] = run;
+  }
+  __syncthreads();
+  // 2) expert offsets and the chunk table
+  block_scan_experts(s_cnt, Ep, B, counts, offsets, vinfo, units16, counters, nullptr);
+}
+
+__global__ __launch_bounds__(256) void sort_scatter_kernel(
+    const int32_t* __restrict__ slot_expert, int nslots, int Ep, int n_ranges, int key_bits,
+    const int32_t* __restrict__ range_base, const int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_slot, int32_t* __restrict__ expanded_idx) {
+  extern __shared__ int32_t lds[];
+  const int w = threadIdx.x >> 6, lane = lane_id();
+  const int r = blockIdx.x * 4 + w;
+  if (r >= n_ranges) return;  // wave-uniform; no block barrier below
+  int32_t* next = lds + w * Ep;  // next free row per expert for this range
+  for (int i = lane; i < Ep; i += kWave)
+    next[i] = offsets[i] + range_base[static_cast<size_t>(r) * Ep + i];
+  const int s0 = r * kRangeSlots;
+  const int s1 = min(nslots, s0 + kRangeSlots);
+  for (int c = s0; c < s1; c += kWave) {
+    const int s = c + lane;
+    const bool in = s < s1;
+    place_slots(s, in, in ? slot_expert[s] : -1, key_bits, Ep, next, sorted_slot, expanded_idx);
+  }
+}
+
+__global__ __launch_bounds__(64) void gemm2_gate_kernel(const int32_t* __restrict__ counts,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int Ep, int force_path,
+                                                        int32_t* __restrict__ counters,
+                                                        int32_t* __restrict__ dense_tiles) {
+  gate_wave(counts, offsets, Ep, force_path, counters, dense_tiles);
+}
+
 hipError_t launch_sort_and_gate(const SortArgs& a, hipStream_t st) {
+  int key_bits = 1;
+  while ((1 << key_bits) <= a.Ep) ++key_bits;  // keys 0..Ep inclusive
+  if (a.nslots <= kSmallSlots) {
+    const size_t lds = static_cast<size_t>(kSmallWaves) * a.Ep * sizeof(uint16_t);
+    hipLaunchKernelGGL(sort_small_kernel, dim3(1), dim3(1024), lds, st, a.slot_expert, a.nslots,
+                       a.Ep, a.B, key_bits, a.force_path, a.counts, a.offsets, a.sorted_slot,
+                       a.expanded_idx, a.vinfo, a.units16, a.counters, a.dense_tiles);
+    return hipGetLastError();
+  }
   const int blocks = (a.n_ranges + 3) / 4;
   const size_t lds = static_cast<size_t>(4) * a.Ep * sizeof(int32_t);
   hipLaunchKernelGGL(sort_count_kernel, dim3(blocks), dim3(256), lds, st, a.slot_expert, a.nslots,
@@ -221,11 +371,9 @@ hipError_t launch_sort_and_gate(const SortArgs& a, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, st, a.range_counts, a.n_ranges,
-                     a.Ep, a.B, a.counts, a.offsets, a.vinfo, a.counters);
+                     a.Ep, a.B, a.counts, a.offsets, a.vinfo, a.units16, a.counters);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  int key_bits = 1;
-  while ((1 << key_bits) <= a.Ep) ++key_bits;  // keys 0..Ep inclusive
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(256), lds, st, a.slot_expert,
                      a.nslots, a.Ep, a.n_ranges, key_bits, a.range_counts, a.offsets,
                      a.sorted_slot, a.expanded_idx);

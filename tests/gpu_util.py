@@ -8,6 +8,7 @@ import numpy as np
 import torch
 
 import mxfp4_weight_expert_amd as moe
+import oracle
 from workloads import LayerShape
 
 # Output tolerances: max |got - want| / max |want| and ||got - want|| / ||want||.
@@ -111,3 +112,6 @@ def check_maps(s: LayerShape, got: dict, ref: dict, force_path: int = -1):
     assert gate == tuple(ref["gate"]), f"gate word {gate} != {ref['gate']}"
     nt = gate[3]
     assert np.array_equal(got["dense_tiles"][:nt], ref["dense_tiles"]), "dense tiles differ"
+    nu = int(got["counters"][1])
+    u16 = oracle.sort_align(ref["slot_expert"], s.Ep, 16)["vinfo"]
+    assert nu == u16.shape[0] and np.array_equal(got["units16"][:nu], u16), "16-row units differ"

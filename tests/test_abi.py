@@ -81,7 +81,7 @@ def test_layout_bounds_match_oracle(name):
     assert L["kmax_v"] == oracle.kmax_v(s.Ep, s.T, s.Kp, s.B)
     offs = [L[k] for k in ("counters", "route_ids", "slot_expert", "slot_w", "range_counts",
                            "counts", "offsets", "sorted_slot", "expanded_idx", "vinfo",
-                           "dense_tiles", "act", "act_scales", "y", "xq", "xs")]
+                           "dense_tiles", "units16", "act", "act_scales", "y", "xq", "xs")]
     assert all(o % 256 == 0 for o in offs)
     assert offs == sorted(offs) and offs[-1] <= L["total_bytes"]
     assert L["y"] - L["act"] >= L["rows_pad"] * s.I * 2
