@@ -53,6 +53,10 @@ struct GemmArgs {
 };
 hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st);  // split + dense, gated on device
+// LDS-tiled kernels for many rows per expert (gemm_tiled.hip): GEMM1 over the
+// chunk table (B >= 64), and the dense GEMM2 path over the dense tiles.
+hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st);
 
 struct FinalizeArgs {
   const uint16_t* y;
