@@ -75,7 +75,8 @@ extern "C" {
  *   topk            routed experts per token, 1..32
  *   S               shared experts appended per token, 0..8; their weights
  *                   sit after the E routed experts in w13/s13/w2/s2
- *   H, I            hidden and intermediate sizes; H % 512 == 0, I % 128 == 0
+ *   H, I            hidden and intermediate sizes; H % 512 == 0, I % 128 == 0,
+ *                   both at most 8192
  *   block_n         B: rows per chunk ("virtual expert"). 16 or 32 select the
  *                   decode GEMM1 (tokens on the MFMA N side); 64, 128 or 256
  *                   the prefill GEMM1 (tokens on the M side)
@@ -163,7 +164,7 @@ typedef struct moe_mxfp4_ws_layout {
  * Check a shape and return the workspace size it needs.
  * Host only; touches no device. Returns MOE_OK, MOE_ERR_INVALID (null
  * pointer, negative sizes, offset range outside E_global) or
- * MOE_ERR_UNSUPPORTED (H % 512, I % 128, block_n, topk, S, E + S > 2048,
+ * MOE_ERR_UNSUPPORTED (H % 512, I % 128, H or I > 8192, block_n, topk, S, E + S > 2048,
  * T * K' > 2^23, unknown activation or a_dtype).
  */
 int moe_mxfp4_query(const moe_mxfp4_shape* shape, uint64_t* workspace_bytes);

@@ -31,6 +31,8 @@ int check_shape(const moe_mxfp4_shape* s) {
   if (s->topk > kMaxTopK || s->topk > s->E_global || s->S > kMaxShared) return MOE_ERR_UNSUPPORTED;
   if (s->E + s->S > kMaxExperts || s->E_global > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->H % 512 != 0 || s->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  // the tiled GEMMs keep a tile's scale rows (8 bytes per K element) in LDS
+  if (s->H > kMaxTiledK || s->I > kMaxTiledK) return MOE_ERR_UNSUPPORTED;
   if (s->block_n != 16 && s->block_n != 32 && s->block_n != 64 && s->block_n != 128 &&
       s->block_n != 256)
     return MOE_ERR_UNSUPPORTED;

@@ -22,6 +22,7 @@ constexpr int kRangeSlots = 4096;  // slots per sort range (one wave each)
 constexpr int kSmallSlots = 8192;  // up to this many slots the sort runs in one block
 constexpr int kGateTau = 64;       // dense GEMM2 when rows >= kGateTau * touched experts
 constexpr int kDenseMT = 128;      // dense-path row tile
+constexpr int kMaxTiledK = 8192;   // largest H and I (LDS budget of the tiled GEMMs)
 constexpr int kCounterWords = 64;
 constexpr int kCtrNumV = 0;
 constexpr int kCtrNumU = 1;        // 16-row units (decode GEMM work list)

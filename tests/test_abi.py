@@ -65,7 +65,7 @@ def _shape(**kw):
     (dict(H=3584 + 256), 2), (dict(I=384 + 64), 2), (dict(block_n=48), 2), (dict(topk=33), 2),
     (dict(S=9), 2), (dict(E=2040, E_global=2040, S=9), 2), (dict(E_global=3000, E=2000), 2),
     (dict(expert_offset=1), 1), (dict(T=-1), 1), (dict(E=0), 1), (dict(topk=0), 1),
-    (dict(force_gemm2_path="dense", T=1 << 20), 2),
+    (dict(force_gemm2_path="dense", T=1 << 20), 2), (dict(H=8192 + 512), 2), (dict(I=8192 + 128), 2),
 ])
 def test_query_rejects_bad_shapes(kw, code):
     with pytest.raises(moe.MoeError) as ei:
