@@ -45,6 +45,37 @@ def parse():
     return p.parse_args()
 
 
+KERNEL_SOURCES = {"gemm1_decode_kernel": ["gemm.hip", "common.h"],
+                  "gemm_tiled_kernel<true>": ["gemm_tiled.hip", "common.h"]}
+
+
+def measured_traffic(config: str, kernel: str):
+    """HBM bytes per launch of `kernel` on this workload, from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary under profiles/, scaled by the
+    counters' reading for a 1 GiB copy; None when no summary matches or the
+    kernel's sources changed since the counters were taken."""
+    import glob
+    import hashlib
+    csrc = os.path.join(ROOT, "mxfp4_weight_expert_amd", "csrc")
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        with open(path) as f:
+            for line in f:
+                if not line.startswith("traffic-json: "):
+                    continue
+                rec = json.loads(line[len("traffic-json: "):])
+                if rec.get("workload") != config or not rec.get("kernel", "").startswith("moe::" + kernel.split("<")[0]):
+                    continue
+                if ("<true>" in kernel) != ("<true>" in rec["kernel"]):
+                    continue
+                h = hashlib.sha256()
+                for src in rec["src"]:
+                    with open(os.path.join(csrc, src), "rb") as g:
+                        h.update(g.read())
+                if h.hexdigest()[:16] == rec["src_sha256_16"]:
+                    return rec["traffic_bytes"]
+    return None
+
+
 def workload_name(s) -> str:
     parts = [f"T={s.T}", f"E={s.E}" + (f"/{s.E_g}@{s.expert_offset}" if s.E != s.E_g else ""),
              f"topk={s.topk}"]
@@ -90,8 +121,9 @@ def cpu_baseline(s, inp, target_s: float) -> dict:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the layer has no multi-GPU path in this build)", file=sys.stderr)
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported: the layer "
+              "runs on one GPU, and splitting experts over GPUs (expert_offset) is the "
+              "caller's part", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -209,8 +241,9 @@ def main():
         roof = {"bound": "hbm", "achieved": round(gemm1_bytes / (gemm1_ms / 1e3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = None
-    roof["kernel"] = "gemm1_tn_kernel"
+    kernel = "gemm1_decode_kernel" if s.B <= 32 else "gemm_tiled_kernel<true>"
+    roof["traffic"] = measured_traffic(args.config, kernel)
+    roof["kernel"] = kernel
     roof["kernel_us"] = round(gemm1_ms * 1e3, 2)
     roof["algorithmic_bytes" if roof["bound"] == "hbm" else "algorithmic_flops"] = \
         gemm1_bytes if roof["bound"] == "hbm" else gemm1_flops

@@ -23,11 +23,11 @@
 // + 8j + [0, 8) on both operands, which keeps each weight fragment a
 // contiguous 16 bytes and leaves the dot products unchanged.
 //
-// Blocks are mapped XCD-aware: the hardware deals consecutive block ids
-// round-robin over the 8 XCDs, so block b works on item
-// (b mod 8) * ceil(items / 8) + b / 8, and the blocks that share a token tile
-// (consecutive items) and an expert's weights run together on one XCD and
-// meet in its L2.
+// Blocks are persistent and mapped XCD-aware: the hardware deals
+// consecutive block ids round-robin over the 8 XCDs, so the items are cut
+// into 8 contiguous ranges, one per XCD, and the blocks of an XCD walk its
+// range in order: blocks that share a token tile (consecutive items) and an
+// expert's weights run together on one XCD and meet in its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -84,215 +84,222 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(
   const int nitems = ntiles * sub * nspan;
   const int xcd = blockIdx.x & 7;
   const int per = (nitems + 7) >> 3;
-  const int slot = blockIdx.x >> 3;
-  const int item = xcd * per + slot;
-  if (slot >= per || item >= nitems) return;
-  const int span = item % nspan;
-  const int ts = item / nspan;
-  const int tile = ts / sub;
-  const int st = ts - tile * sub;
-  const int4 ti = reinterpret_cast<const int4*>(tiles)[tile];
-  const int e = ti.x;
-  const int row0 = ti.y + st * kTileRows;
-  const int nrows = min(kTileRows, ti.z - st * kTileRows);
-  if (nrows <= 0) return;
-  const int t = threadIdx.x;
-  const size_t wrow = static_cast<size_t>(K) >> 1, srow = static_cast<size_t>(K) >> 5;
-  // Global weight row of tile row rho: GEMM1 rows [0, 128) are the gate rows
-  // of features f0 + rho, rows [128, 256) the up rows of the same features.
-  const int f0 = G1 ? span * 128 : span * 256;
-  auto grow_of = [&](int rho) -> size_t {
-    if (G1) return static_cast<size_t>(e) * 2 * I + (rho < 128 ? f0 + rho : I + f0 + rho - 128);
-    return static_cast<size_t>(e) * H + f0 + rho;
-  };
+  const int nblk_x = static_cast<int>(gridDim.x) >> 3;  // blocks per XCD
+  for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
+    const int item = xcd * per + slot;
+    if (item >= nitems) break;
+    const int span = item % nspan;
+    const int ts = item / nspan;
+    const int tile = ts / sub;
+    const int st = ts - tile * sub;
+    const int4 ti = reinterpret_cast<const int4*>(tiles)[tile];
+    const int e = ti.x;
+    const int row0 = ti.y + st * kTileRows;
+    const int nrows = min(kTileRows, ti.z - st * kTileRows);
+    if (nrows <= 0) continue;
+    const int t = threadIdx.x;
+    const size_t wrow = static_cast<size_t>(K) >> 1, srow = static_cast<size_t>(K) >> 5;
+    // Global weight row of tile row rho: GEMM1 rows [0, 128) are the gate rows
+    // of features f0 + rho, rows [128, 256) the up rows of the same features.
+    const int f0 = G1 ? span * 128 : span * 256;
+    auto grow_of = [&](int rho) -> size_t {
+      if (G1) return static_cast<size_t>(e) * 2 * I + (rho < 128 ? f0 + rho : I + f0 + rho - 128);
+      return static_cast<size_t>(e) * H + f0 + rho;
+    };
 
-  // ---- scale rows of the tile -> LDS (256 rows x K/32 bytes, row-major)
-  {
-    const int seg = G1 ? 128 * static_cast<int>(srow) : 256 * static_cast<int>(srow);
-    const uint8_t* s0 = s + grow_of(0) * srow;
-    for (int o = t * 16; o < seg; o += kTiledThreads * 16)
-      *reinterpret_cast<uint4*>(s_lds + o) = ld16(s0 + o);
-    if (G1) {
-      const uint8_t* s1 = s + grow_of(128) * srow;
+    // ---- scale rows of the tile -> LDS (256 rows x K/32 bytes, row-major)
+    {
+      const int seg = G1 ? 128 * static_cast<int>(srow) : 256 * static_cast<int>(srow);
+      const uint8_t* s0 = s + grow_of(0) * srow;
       for (int o = t * 16; o < seg; o += kTiledThreads * 16)
-        *reinterpret_cast<uint4*>(s_lds + seg + o) = ld16(s1 + o);
-    }
-  }
-
-  // ---- token tile loads: thread t moves chunk t%16 of rows 32i + t/16.
-  // Rows past the tile's end get an out-of-range offset (their loads return
-  // zero). The row -> slot reads are buffer loads too, so that none of them
-  // sits behind a branch.
-  const int lc = t & 15, lr = t >> 4;
-  uint32_t toff[4];
-  if (G1) {
-    const __amdgpu_buffer_rsrc_t ssr =
-        make_rsrc(sorted_slot + row0, static_cast<uint32_t>(nrows) * 4u);
-    uint32_t slotv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      slotv[i] = __builtin_amdgcn_raw_buffer_load_b32(ssr, (i * 32 + lr) * 4, 0, 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = i * 32 + lr;
-      const uint32_t tok = slotv[i] / static_cast<uint32_t>(Kp);
-      toff[i] = tok * static_cast<uint32_t>(K) * 2u + lc * 16 + (r < nrows ? 0u : kNoRow);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = i * 32 + lr;
-      toff[i] = static_cast<uint32_t>(row0 + r) * static_cast<uint32_t>(K) * 2u + lc * 16 +
-                (r < nrows ? 0u : kNoRow);
-    }
-  }
-  const __amdgpu_buffer_rsrc_t srs = make_rsrc(src, src_bytes);
-  // ---- weight tile loads: thread t moves chunk t%4 of tile rows 128i + t/4
-  const int wc = t & 3, wr = t >> 2;
-  const uint8_t* wsrc[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) wsrc[i] = w + grow_of(i * 128 + wr) * wrow + wc * 16;
-
-  const int nkb = K >> 7;
-  const int last = nkb - 1;
-  uint4 tv[4], wv[2];
-  auto load_stage = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) tv[i] = bld16(srs, toff[i] + kb * 256);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * 64);
-  };
-  auto store_stage = [&](int b) {
-    uint8_t* tb = tok_lds + b * kTokStage;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tb + tok_off(i * 32 + lr, lc)) = tv[i];
-    uint8_t* wb = w_lds + b * kWStage;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(wb + w_off(i * 128 + wr, wc)) = wv[i];
-  };
-
-  // ---- this wave's share
-  const int wave = wave_index();
-  const int wm = wave & 1, wn = wave >> 1;
-  const int lane = lane_id();
-  const int r = lane & 31, h = lane >> 5;
-  int rho[2];  // tile weight rows of the wave's two 32-row MFMA tiles (lane r)
-  if (G1) {
-    rho[0] = wn * 32 + r;         // gate
-    rho[1] = 128 + wn * 32 + r;   // up, same features
-  } else {
-    rho[0] = wn * 64 + r;
-    rho[1] = wn * 64 + 32 + r;
-  }
-  const uint8_t* srow_lds[2] = {s_lds + rho[0] * srow, s_lds + rho[1] * srow};
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int m = 0; m < 2; ++m)
-#pragma unroll
-    for (int n = 0; n < 2; ++n)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
-
-  // Prologue: stage 0 in LDS, stage 1 in flight.
-  load_stage(0);
-  __builtin_amdgcn_sched_barrier(0);
-  store_stage(0);
-  __builtin_amdgcn_sched_barrier(0);
-  load_stage(min(1, last));
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int b = kb & 1;
-    const uint8_t* tb = tok_lds + b * kTokStage;
-    const uint8_t* wb = w_lds + b * kWStage;
-    uint32_t sdw[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(srow_lds[m] + kb * 4);
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      bf16x8_t a[2][4];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        const uint4 wf = *reinterpret_cast<const uint4*>(wb + w_off(rho[m], 2 * q + h));
-        const float scale = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
-        const uint32_t dw[4] = {wf.x, wf.y, wf.z, wf.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) a[m][j] = decode_fp4x8(dw[j], scale);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8_t bf[2];
-#pragma unroll
-        for (int n = 0; n < 2; ++n)
-          bf[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
-              tb + tok_off(wm * 64 + n * 32 + r, 8 * q + 4 * h + j)));
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m][j], bf[n], acc[m][n]);
+        *reinterpret_cast<uint4*>(s_lds + o) = ld16(s0 + o);
+      if (G1) {
+        const uint8_t* s1 = s + grow_of(128) * srow;
+        for (int o = t * 16; o < seg; o += kTiledThreads * 16)
+          *reinterpret_cast<uint4*>(s_lds + seg + o) = ld16(s1 + o);
       }
     }
-    // Stage kb+1 into the other buffers (read last in stage kb-1, finished
-    // by every wave before the previous barrier), then start the loads of
-    // stage kb+2 (near the end the last stage again: loaded, never used).
-    // Loads retire in issue order; the pinned order keeps each wait to what
-    // it needs.
-    __builtin_amdgcn_sched_barrier(0);
-    store_stage(b ^ 1);
-    __builtin_amdgcn_sched_barrier(0);
-    load_stage(min(kb + 2, last));
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-  }
 
-  // ---- epilogue. Lane (r, h), accumulator register 4*b4 + i holds weight
-  // row 8*b4 + 4*h + i of the 32-row tile against token row 32*n + r of the
-  // wave's 64 tokens.
-  if (G1) {
-    const int fbase = f0 + wn * 32;
-    const __amdgpu_buffer_rsrc_t ors =
-        make_rsrc(dst + static_cast<size_t>(row0) * I, static_cast<uint32_t>(nrows) * I * 2);
+    // ---- token tile loads: thread t moves chunk t%16 of rows 32i + t/16.
+    // Rows past the tile's end get an out-of-range offset (their loads return
+    // zero). The row -> slot reads are buffer loads too, so that none of them
+    // sits behind a branch.
+    const int lc = t & 15, lr = t >> 4;
+    uint32_t toff[4];
+    if (G1) {
+      const __amdgpu_buffer_rsrc_t ssr =
+          make_rsrc(sorted_slot + row0, static_cast<uint32_t>(nrows) * 4u);
+      uint32_t slotv[4];
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
+      for (int i = 0; i < 4; ++i)
+        slotv[i] = __builtin_amdgcn_raw_buffer_load_b32(ssr, (i * 32 + lr) * 4, 0, 0);
 #pragma unroll
-      for (int b4 = 0; b4 < 4; ++b4) {
-        const f32x16_t& g = acc[0][n];
-        const f32x16_t& u = acc[1][n];
-        uint2 pk;
-        pk.x = pack_bf16x2(swiglu(g[4 * b4 + 0], u[4 * b4 + 0], limit),
-                           swiglu(g[4 * b4 + 1], u[4 * b4 + 1], limit));
-        pk.y = pack_bf16x2(swiglu(g[4 * b4 + 2], u[4 * b4 + 2], limit),
-                           swiglu(g[4 * b4 + 3], u[4 * b4 + 3], limit));
-        const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * I * 2 +
-                             (fbase + 8 * b4 + 4 * h) * 2;
-        bst8(ors, off, pk);
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + lr;
+        const uint32_t tok = slotv[i] / static_cast<uint32_t>(Kp);
+        toff[i] = tok * static_cast<uint32_t>(K) * 2u + lc * 16 + (r < nrows ? 0u : kNoRow);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + lr;
+        toff[i] = static_cast<uint32_t>(row0 + r) * static_cast<uint32_t>(K) * 2u + lc * 16 +
+                  (r < nrows ? 0u : kNoRow);
       }
     }
-  } else {
-    const int fbase = f0 + wn * 64;
-    const __amdgpu_buffer_rsrc_t ors =
-        make_rsrc(dst + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(src, src_bytes);
+    // ---- weight tile loads: thread t moves chunk t%4 of tile rows 128i + t/4
+    const int wc = t & 3, wr = t >> 2;
+    const uint8_t* wsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wsrc[i] = w + grow_of(i * 128 + wr) * wrow + wc * 16;
+
+    const int nkb = K >> 7;
+    const int last = nkb - 1;
+    uint4 tv[4], wv[2];
+    auto load_stage = [&](int kb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tv[i] = bld16(srs, toff[i] + kb * 256);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * 64);
+    };
+    auto store_stage = [&](int b) {
+      uint8_t* tb = tok_lds + b * kTokStage;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tb + tok_off(i * 32 + lr, lc)) = tv[i];
+      uint8_t* wb = w_lds + b * kWStage;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(wb + w_off(i * 128 + wr, wc)) = wv[i];
+    };
+
+    // ---- this wave's share
+    const int wave = wave_index();
+    const int wm = wave & 1, wn = wave >> 1;
+    const int lane = lane_id();
+    const int r = lane & 31, h = lane >> 5;
+    int rho[2];  // tile weight rows of the wave's two 32-row MFMA tiles (lane r)
+    if (G1) {
+      rho[0] = wn * 32 + r;         // gate
+      rho[1] = 128 + wn * 32 + r;   // up, same features
+    } else {
+      rho[0] = wn * 64 + r;
+      rho[1] = wn * 64 + 32 + r;
+    }
+    const uint8_t* srow_lds[2] = {s_lds + rho[0] * srow, s_lds + rho[1] * srow};
+
+    f32x16_t acc[2][2];
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
+        for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
+
+    // Prologue: stage 0 in LDS, stage 1 in flight.
+    load_stage(0);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(min(1, last));
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int b = kb & 1;
+      const uint8_t* tb = tok_lds + b * kTokStage;
+      const uint8_t* wb = w_lds + b * kWStage;
+      uint32_t sdw[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(srow_lds[m] + kb * 4);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        bf16x8_t a[2][4];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const uint4 wf = *reinterpret_cast<const uint4*>(wb + w_off(rho[m], 2 * q + h));
+          const float scale = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
+          const uint32_t dw[4] = {wf.x, wf.y, wf.z, wf.w};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) a[m][j] = decode_fp4x8(dw[j], scale);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          bf16x8_t bf[2];
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            bf[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                tb + tok_off(wm * 64 + n * 32 + r, 8 * q + 4 * h + j)));
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m][j], bf[n], acc[m][n]);
+        }
+      }
+      // Stage kb+1 into the other buffers (read last in stage kb-1, finished
+      // by every wave before the previous barrier), then start the loads of
+      // stage kb+2 (near the end the last stage again: loaded, never used).
+      // Loads retire in issue order; the pinned order keeps each wait to what
+      // it needs.
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage(b ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(min(kb + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    }
+
+    // ---- epilogue. Lane (r, h), accumulator register 4*b4 + i holds weight
+    // row 8*b4 + 4*h + i of the 32-row tile against token row 32*n + r of the
+    // wave's 64 tokens.
+    if (G1) {
+      const int fbase = f0 + wn * 32;
+      const __amdgpu_buffer_rsrc_t ors =
+          make_rsrc(dst + static_cast<size_t>(row0) * I, static_cast<uint32_t>(nrows) * I * 2);
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+#pragma unroll
         for (int b4 = 0; b4 < 4; ++b4) {
+          const f32x16_t& g = acc[0][n];
+          const f32x16_t& u = acc[1][n];
           uint2 pk;
-          pk.x = pack_bf16x2(acc[m][n][4 * b4 + 0], acc[m][n][4 * b4 + 1]);
-          pk.y = pack_bf16x2(acc[m][n][4 * b4 + 2], acc[m][n][4 * b4 + 3]);
-          const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * H * 2 +
-                               (fbase + 32 * m + 8 * b4 + 4 * h) * 2;
+          pk.x = pack_bf16x2(swiglu(g[4 * b4 + 0], u[4 * b4 + 0], limit),
+                             swiglu(g[4 * b4 + 1], u[4 * b4 + 1], limit));
+          pk.y = pack_bf16x2(swiglu(g[4 * b4 + 2], u[4 * b4 + 2], limit),
+                             swiglu(g[4 * b4 + 3], u[4 * b4 + 3], limit));
+          const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * I * 2 +
+                               (fbase + 8 * b4 + 4 * h) * 2;
           bst8(ors, off, pk);
         }
-  }
+      }
+    } else {
+      const int fbase = f0 + wn * 64;
+      const __amdgpu_buffer_rsrc_t ors =
+          make_rsrc(dst + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[m][n][4 * b4 + 0], acc[m][n][4 * b4 + 1]);
+            pk.y = pack_bf16x2(acc[m][n][4 * b4 + 2], acc[m][n][4 * b4 + 3]);
+            const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * H * 2 +
+                                 (fbase + 32 * m + 8 * b4 + 4 * h) * 2;
+            bst8(ors, off, pk);
+          }
+    }
+  }  // items
 }
 
+// Persistent grid: one block per CU (a block holds 96 KB of LDS and two
+// waves per SIMD), at most one block per item; a multiple of 8 so that every
+// XCD gets the same number of blocks.
 static int tiled_grid(long items) {
-  const long per = (items + 7) / 8;
-  return static_cast<int>(8 * (per < 1 ? 1 : per));
+  long per = (items + 7) / 8;
+  if (per < 1) per = 1;
+  if (per > 32) per = 32;
+  return static_cast<int>(8 * per);
 }
 
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st) {
