@@ -35,6 +35,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--a-dtype", default="bf16", choices=["bf16", "mxfp8"],
+                   help="activation format: bf16 (W4A16) or mxfp8 (W4A8)")
     p.add_argument("--config", default="decode",
                    help="tiny | decode | decode_ep | shared_clamp | prefill")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -43,10 +45,6 @@ def parse():
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
-
-
-KERNEL_SOURCES = {"gemm1_decode_kernel": ["gemm.hip", "common.h"],
-                  "gemm_tiled_kernel<true>": ["gemm_tiled.hip", "common.h"]}
 
 
 def measured_traffic(config: str, kernel: str):
@@ -86,7 +84,8 @@ def workload_name(s) -> str:
         parts.append(f"clamp={s.swiglu_limit:g}")
     if s.routing == "zipf":
         parts.append(f"zipf={s.zipf_s:g}")
-    return f"MXFP4 MoE layer ({s.name}): " + " ".join(parts) + f", W4A16 {s.a_dtype} activations"
+    act = "W4A8 MXFP8 (E4M3) activations" if s.a_dtype == "mxfp8" else "W4A16 bf16 activations"
+    return f"MXFP4 MoE layer ({s.name}): " + " ".join(parts) + f", {act}"
 
 
 def cpu_baseline(s, inp, target_s: float) -> dict:
@@ -132,7 +131,8 @@ def main():
     from workloads import CONFIGS, config_seed, make_inputs
 
     moe.load_library()  # fails loudly if the HIP library is not built
-    s = CONFIGS[args.config]
+    s = CONFIGS[args.config].replace(a_dtype=args.a_dtype)
+    a8 = s.a_dtype == "mxfp8"
     dev_id = 0
     torch.cuda.set_device(dev_id)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)
@@ -230,18 +230,22 @@ def main():
     # GEMM1 algorithmic work per launch: W13 + its scales of every touched
     # expert, x once, act written once (and the row -> slot map).
     w13_expert_bytes = 2 * s.I * (s.H // 2 + s.H // 32)
-    gemm1_bytes = U * w13_expert_bytes + s.T * s.H * 2 + R * s.I * 2 + R * 4
+    # activations: bf16, or E4M3 codes plus one scale byte per 32
+    x_bytes = s.T * (s.H + s.H // 32) if a8 else s.T * s.H * 2
+    act_bytes = R * (s.I + s.I // 32) if a8 else R * s.I * 2
+    gemm1_bytes = U * w13_expert_bytes + x_bytes + act_bytes + R * 4
     gemm1_flops = 2.0 * R * s.H * 2 * s.I
     layer_bytes = U * (w13_expert_bytes + s.H * (s.I // 2 + s.I // 32)) + s.T * s.H * 4 \
         + s.T * s.E_g * 4
     if R >= 64 * max(U, 1):  # prefill-like: the contraction dominates
         roof = {"bound": "mfma", "achieved": round(gemm1_flops / (gemm1_ms / 1e3) / 1e12, 2),
-                "peak": MFMA_PEAK_TFLOPS["bf16"], "unit": "TFLOP/s"}
+                "peak": MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"], "unit": "TFLOP/s"}
     else:
         roof = {"bound": "hbm", "achieved": round(gemm1_bytes / (gemm1_ms / 1e3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    kernel = "gemm1_decode_kernel" if s.B <= 32 else "gemm_tiled_kernel<true>"
+    kernel = ("gemm1_decode_a8_kernel" if a8 else "gemm1_decode_kernel") if s.B <= 32 else \
+        ("gemm_tiled_a8_kernel<true>" if a8 else "gemm_tiled_kernel<true>")
     roof["traffic"] = measured_traffic(args.config, kernel)
     roof["kernel"] = kernel
     roof["kernel_us"] = round(gemm1_ms * 1e3, 2)
@@ -259,11 +263,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3 x e2m1 (fp32 acc)" if a8 else "bf16",
         "data": "synthetic (seeded PCG64: N(0,1) bf16 x, N(0,1) router logits, uniform E2M1 "
                 "nibbles, E8M0 scales uniform in [118,127])",
         "config": {"workload": workload_name(s), "T": s.T, "E": s.E, "E_global": s.E_g,
                    "topk": s.topk, "S": s.S, "H": s.H, "I": s.I, "block_n": s.B,
+                   "a_dtype": s.a_dtype,
                    "touched_experts": U_routed, "rows": R, "gemm2_path": "dense" if gate[0] else "split",
                    "layer_us": round(ms_per_step * 1e3, 2),
                    "layer_hbm_GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),

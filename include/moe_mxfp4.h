@@ -82,7 +82,10 @@ extern "C" {
  *                   the prefill GEMM1 (tokens on the M side)
  *   expert_offset   global id of local expert 0
  *   activation      MOE_ACT_SWIGLU
- *   a_dtype         MOE_ADTYPE_BF16 or MOE_ADTYPE_MXFP8
+ *   a_dtype         MOE_ADTYPE_BF16 or MOE_ADTYPE_MXFP8 (W4A8; needs I <= 512).
+ *                   W4A8 quantises x to MXFP8 and the SwiGLU output act to
+ *                   MXFP8 (per 32 along I) before GEMM2; the GEMMs run on
+ *                   scaled f8f6f4 MFMA with the E2M1 weights fed as they are
  *   force_gemm2_path  MOE_GEMM2_AUTO, _SPLIT or _DENSE
  *   swiglu_limit    > 0: gate = min(gate, L), up = clamp(up, -L, L)
  *                   before silu(gate) * up; <= 0: no clamp
@@ -165,7 +168,7 @@ typedef struct moe_mxfp4_ws_layout {
  * Host only; touches no device. Returns MOE_OK, MOE_ERR_INVALID (null
  * pointer, negative sizes, offset range outside E_global) or
  * MOE_ERR_UNSUPPORTED (H % 512, I % 128, H or I > 8192, block_n, topk, S, E + S > 2048,
- * T * K' > 2^23, unknown activation or a_dtype).
+ * T * K' > 2^23, unknown activation or a_dtype, MXFP8 with I > 512).
  */
 int moe_mxfp4_query(const moe_mxfp4_shape* shape, uint64_t* workspace_bytes);
 

@@ -15,7 +15,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
-SOURCES = ["api.hip", "route.hip", "sort.hip", "gemm.hip", "gemm_tiled.hip", "finalize.hip"]
+SOURCES = ["api.hip", "route.hip", "sort.hip", "quant.hip", "gemm.hip", "gemm_tiled.hip",
+           "finalize.hip"]
 ARCH = "gfx950"
 
 

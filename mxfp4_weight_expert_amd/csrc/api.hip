@@ -37,7 +37,9 @@ int check_shape(const moe_mxfp4_shape* s) {
       s->block_n != 256)
     return MOE_ERR_UNSUPPORTED;
   if (s->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
-  if (s->a_dtype != MOE_ADTYPE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->a_dtype != MOE_ADTYPE_BF16 && s->a_dtype != MOE_ADTYPE_MXFP8) return MOE_ERR_UNSUPPORTED;
+  // the W4A8 split GEMM2 keeps a row's whole K in registers: I <= 512
+  if (s->a_dtype == MOE_ADTYPE_MXFP8 && s->I > 512) return MOE_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(s->T) * (s->topk + s->S) > kMaxSlots) return MOE_ERR_UNSUPPORTED;
   // the kernels address x and act with 32-bit buffer offsets
   const int64_t rows = static_cast<int64_t>(s->T) * (s->topk + s->S) + 256;
@@ -211,7 +213,14 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   ga.limit = s.swiglu_limit;
   ga.act = reinterpret_cast<uint16_t*>(at(L.act));
   ga.y = reinterpret_cast<uint16_t*>(at(L.y));
-  if (mark() != hipSuccess || launch_gemm1(ga, st) != hipSuccess) return MOE_ERR_HIP;
+  ga.a8 = s.a_dtype == MOE_ADTYPE_MXFP8;
+  ga.xq = at(L.xq);
+  ga.xs = at(L.xs);
+  ga.act_scales = at(L.act_scales);
+  if (mark() != hipSuccess) return MOE_ERR_HIP;
+  if (ga.a8 && launch_quant_x(ga.x, s.T, s.H, at(L.xq), at(L.xs), st) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (launch_gemm1(ga, st) != hipSuccess) return MOE_ERR_HIP;
   if (mark() != hipSuccess || launch_gemm2(ga, st) != hipSuccess) return MOE_ERR_HIP;
 
   FinalizeArgs fa;

@@ -148,6 +148,52 @@ __device__ __forceinline__ f32x4_t mfma16x16x32(bf16x8_t a, bf16x8_t b, f32x4_t 
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// ------------------------------------------------------------------ MXFP8
+// MXFP8 block scale of a 32-element block with maximum magnitude amax (a
+// finite float): the shared exponent floor(log2(amax)) - 8 (8 = the largest
+// E4M3 exponent), biased by 127 and clamped to [0, 254]; amax = 0 gives 0.
+// With the exponent field e of amax this is max(e - 8, 0): subnormal and
+// zero amax (e = 0) clamp to 0, and e <= 254 keeps the result <= 246.
+__device__ __forceinline__ uint32_t mxfp8_scale_byte(float amax) {
+  const uint32_t e = (__float_as_uint(amax) >> 23) & 0xffu;
+  return e >= 8u ? e - 8u : 0u;
+}
+// 2^(127 - b) for a scale byte b <= 246: a normal float, so v * factor is
+// exact for every element of the block (|v * factor| < 512).
+__device__ __forceinline__ float mxfp8_inv_scale(uint32_t b) {
+  return __uint_as_float((254u - b) << 23);
+}
+// Four scaled values -> four E4M3 codes (byte i = value i), round to nearest
+// even, saturating at +-448 (the hardware convert itself does not saturate).
+__device__ __forceinline__ uint32_t pack_e4m3x4(float a, float b, float c, float d) {
+  const float m = 448.0f;
+  a = fminf(fmaxf(a, -m), m);
+  b = fminf(fmaxf(b, -m), m);
+  c = fminf(fmaxf(c, -m), m);
+  d = fminf(fmaxf(d, -m), m);
+  int p = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  p = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, p, true);
+  return static_cast<uint32_t>(p);
+}
+
+// Scaled MFMA, 16x16 output, K = 128: A = 16 rows of E2M1 codes (lane group
+// g holds K [32g, 32g + 32) of its row, 16 bytes, low nibble first), B = 16
+// columns of E4M3 codes (lane group g holds K [16g, 16g + 16) in x0 and
+// K [64 + 16g, 64 + 16g + 16) in x1). Scales are E8M0 bytes in the low byte
+// of sa / sb: lane (i, g) gives the scale of row / column i for the K block
+// [32g, 32g + 32). D lane (i, g), register v = row 4g + v, column i.
+__device__ __forceinline__ f32x4_t mfma_f4xf8(const uint4& w, uint32_t sa, const uint4& x0,
+                                              const uint4& x1, uint32_t sb, f32x4_t c) {
+  const i32x8_t a = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                     static_cast<int>(w.w), 0, 0, 0, 0};
+  const i32x8_t b = {static_cast<int>(x0.x), static_cast<int>(x0.y), static_cast<int>(x0.z),
+                     static_cast<int>(x0.w), static_cast<int>(x1.x), static_cast<int>(x1.y),
+                     static_cast<int>(x1.z), static_cast<int>(x1.w)};
+  // format codes: 4 = E2M1 (A), 0 = E4M3 (B)
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 0, 0, static_cast<int>(sa), 0,
+                                                          static_cast<int>(sb));
+}
+
 // ---------------------------------------------------------------- activation
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -179,6 +225,18 @@ __device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, v), r,
                                         off, 0, 0);
+}
+__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bst1(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(v), r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
 
 }  // namespace moe

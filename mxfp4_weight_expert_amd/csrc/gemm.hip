@@ -318,6 +318,227 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// W4A8 decode GEMMs (MXFP8 activations). The E2M1 weights go into the
+// scaled MFMA as they are, with their E8M0 scales; no decode. One 16x16x128
+// MFMA per weight tile and K step: lane (r, g) supplies weight row r's codes
+// K [32g, 32g + 32) (the same 16-byte load as the bf16 path) and that
+// group's scale byte, and token r's E4M3 codes K [16g, 16g + 16) and
+// [64 + 16g, 64 + 16g + 16) with its scale byte for block g.
+// ---------------------------------------------------------------------------
+
+// acc[t] += W_tile_t * Xq^T over nkb steps. xrs/xoff: buffer and byte offset
+// of the lane's E4M3 row plus 16g (kNoRow past the unit's end); srs/soff:
+// the row's scale bytes plus g (kNoRow likewise).
+template <int D>
+__device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_t (&wofs)[4],
+                                                const uint8_t* ls, const uint32_t (&lofs)[4],
+                                                int nkb, __amdgpu_buffer_rsrc_t xrs, uint32_t xoff,
+                                                __amdgpu_buffer_rsrc_t srs, uint32_t soff,
+                                                f32x4_t (&acc)[4]) {
+  uint4 w[D][4], xb[D][2];
+  uint32_t xsb[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    xb[d][0] = bld16(xrs, xoff + d * 128);
+    xb[d][1] = bld16(xrs, xoff + d * 128 + 64);
+    xsb[d] = bld1(srs, soff + d * 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + d * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  const int last = nkb - 1;
+  auto step = [&](int kb, int d) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      acc[t] = mfma_f4xf8(w[d][t], ls[lofs[t] + kb * 4], xb[d][0], xb[d][1], xsb[d], acc[t]);
+    __builtin_amdgcn_sched_barrier(0);
+    const int nk = min(kb + D, last);
+    xb[d][0] = bld16(xrs, xoff + nk * 128);
+    xb[d][1] = bld16(xrs, xoff + nk * 128 + 64);
+    xsb[d] = bld1(srs, soff + nk * 4);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + nk * 64);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) step(d, d);
+  for (int kb0 = D; kb0 < nkb; kb0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(kb0 + d, d);
+  }
+}
+
+// The 32 act values of one token row and one 32-feature group, spread as 8
+// values over the four lanes r, r + 16, r + 32, r + 48: MXFP8-quantise them
+// (block amax over the four lanes) and store the lane's two 4-byte runs at
+// byte offsets o0 and o1 of `qrs`, and the block's scale byte at `soff` of
+// `srs` (lanes with g != 0 pass an out-of-range offset).
+__device__ __forceinline__ void quant_store_act(const float (&a)[8], __amdgpu_buffer_rsrc_t qrs,
+                                                uint32_t o0, uint32_t o1,
+                                                __amdgpu_buffer_rsrc_t srs, uint32_t soff) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
+  amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+  const uint32_t b = mxfp8_scale_byte(amax);
+  const float inv = mxfp8_inv_scale(b);
+  bst4(qrs, o0, pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
+  bst4(qrs, o1, pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
+  bst1(srs, soff, b);
+}
+
+// GEMM1 + SwiGLU + act quantisation, W4A8, decode shape. Items and LDS as
+// in gemm1_decode_kernel; the 32-feature group of an item is exactly one
+// MXFP8 block of act.
+template <int D>
+__global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
+    const int32_t* __restrict__ units, const int32_t* __restrict__ counters,
+    const int32_t* __restrict__ sorted_slot, int T, int H, int I, int Kp, float limit,
+    uint8_t* __restrict__ actq, uint8_t* __restrict__ acts) {
+  extern __shared__ uint8_t lds_scales[];
+  const int lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  const int groups = I >> 5;
+  const int nitems = counters[kCtrNumU] * groups;
+  const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
+  const int nkb = H >> 7;
+  const int blk = 32 * static_cast<int>(srow);
+  uint8_t* my = lds_scales + wave_index() * 2 * blk;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xq, static_cast<uint32_t>(static_cast<size_t>(T) * H));
+  const __amdgpu_buffer_rsrc_t srs = make_rsrc(xs, static_cast<uint32_t>(static_cast<size_t>(T) * srow));
+  const uint32_t wofs[4] = {0u, static_cast<uint32_t>(I * wrow), static_cast<uint32_t>(16 * wrow),
+                            static_cast<uint32_t>((I + 16) * wrow)};
+  const uint32_t lofs[4] = {0u, static_cast<uint32_t>(blk), static_cast<uint32_t>(16 * srow),
+                            static_cast<uint32_t>(blk + 16 * srow)};
+  const uint32_t srow_a = static_cast<uint32_t>(I) >> 5;
+  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
+    const int u = item / groups;
+    const int f0 = (item - u * groups) * 32;
+    const int4 ui = reinterpret_cast<const int4*>(units)[u];
+    const int e = ui.x, r0 = ui.y, nrows = ui.z;
+    const size_t row0 = static_cast<size_t>(e) * 2 * I + f0;
+    const uint8_t* sg = s13 + row0 * srow;
+    wave_copy_to_lds(my, sg, blk);
+    wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
+    const uint8_t* wp = w13 + (row0 + r) * wrow + g * 16;
+    const bool valid = r < nrows;
+    const uint32_t tok = static_cast<uint32_t>(sorted_slot[r0 + min(r, nrows - 1)] / Kp);
+    const uint32_t xoff = valid ? tok * static_cast<uint32_t>(H) + g * 16 : kNoRow;
+    const uint32_t soff = valid ? tok * static_cast<uint32_t>(srow) + g : kNoRow;
+    f32x4_t acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    stream_block_a8<D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff, srs, soff, acc);
+    // lane (r, g): features f0 + 16h + 4g + v of token row r0 + r
+    float a[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) a[4 * h + v] = swiglu(acc[2 * h][v], acc[2 * h + 1][v], limit);
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc(actq + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I);
+    const __amdgpu_buffer_rsrc_t ars =
+        make_rsrc(acts + static_cast<size_t>(r0) * srow_a, static_cast<uint32_t>(nrows) * srow_a);
+    const uint32_t o0 = static_cast<uint32_t>(r) * I + f0 + 4 * g;
+    quant_store_act(a, qrs, o0, o0 + 16, ars,
+                    g == 0 ? static_cast<uint32_t>(r) * srow_a + (f0 >> 5) : kNoRow);
+  }
+}
+
+// GEMM2 split path, W4A8, short K (NKB = I/128 <= 4): the balanced stream of
+// gemm2_stream_kernel with E4M3 act fragments (and their scale bytes) in
+// registers and one scaled MFMA per tile and K step.
+template <int NKB>
+__global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
+    const uint8_t* __restrict__ actq, const uint8_t* __restrict__ acts,
+    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
+    const int32_t* __restrict__ units, const int32_t* __restrict__ counters, int H, int I,
+    uint16_t* __restrict__ y) {
+  if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
+  const int lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  const int tpu = H >> 4;
+  const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
+  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave_index();
+  int64_t t = total * wid / nwaves;
+  const int64_t t_end = total * (wid + 1) / nwaves;
+  const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
+  const uint32_t tstride = static_cast<uint32_t>(16 * wrow);
+  const uint32_t sstride = static_cast<uint32_t>(16 * srow);
+  while (t < t_end) {
+    const int u = static_cast<int>(t / tpu);
+    const int h0 = static_cast<int>(t - static_cast<int64_t>(u) * tpu);
+    const int nt = static_cast<int>(min(t_end, static_cast<int64_t>(u + 1) * tpu) - t);
+    const int4 ui = reinterpret_cast<const int4*>(units)[u];
+    const int e = ui.x, r0 = ui.y, nrows = ui.z;
+    const size_t row0 = static_cast<size_t>(e) * H + h0 * 16 + r;
+    const uint8_t* wp = w2 + row0 * wrow + g * 16;
+    const uint8_t* sp = s2 + row0 * srow;
+    const __amdgpu_buffer_rsrc_t qrs =
+        make_rsrc(actq + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I);
+    const __amdgpu_buffer_rsrc_t ars =
+        make_rsrc(acts + static_cast<size_t>(r0) * srow, static_cast<uint32_t>(nrows * srow));
+    const __amdgpu_buffer_rsrc_t yrs =
+        make_rsrc(y + static_cast<size_t>(r0) * H, static_cast<uint32_t>(nrows) * H * 2);
+    const uint32_t qoff = static_cast<uint32_t>(r) * I + g * 16;
+    const uint32_t aoff = static_cast<uint32_t>(r * srow) + g;
+    const uint32_t yrow = static_cast<uint32_t>(r) * H * 2 + (h0 * 16 + g * 4) * 2;
+    uint4 xa[NKB][2];
+    uint32_t xsa[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      xa[kb][0] = bld16(qrs, qoff + kb * 128);
+      xa[kb][1] = bld16(qrs, qoff + kb * 128 + 64);
+      xsa[kb] = bld1(ars, aoff + kb * 4);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    uint4 w[kStreamAhead][NKB];
+    uint4 sc[kStreamAhead];
+#pragma unroll
+    for (int a = 0; a < kStreamAhead; ++a) {
+      const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+      sc[a] = ld16(sp + ti * sstride);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
+      uint2 res[kStreamAhead];
+#pragma unroll
+      for (int a = 0; a < kStreamAhead; ++a) {
+        const int i = i0 + a;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          acc = mfma_f4xf8(w[a][kb], (sw[kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+        sc[a] = ld16(sp + ti * sstride);
+        res[a].x = pack_bf16x2(acc[0], acc[1]);
+        res[a].y = pack_bf16x2(acc[2], acc[3]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int a = 0; a < kStreamAhead; ++a)
+        bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
+    }
+    t += nt;
+  }
+}
+
+// Persistent grid of the streaming GEMM2 kernels: waves split the tile list evenly.
+#ifndef MOE_STREAM_GRID
+#define MOE_STREAM_GRID (256 * 3)
+#endif
+
 static int grid_for(long items) {
   long blocks = (items + 3) / 4;
   if (blocks < 1) blocks = 1;
@@ -325,6 +546,7 @@ static int grid_for(long items) {
 }
 
 hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
+  if (a.a8) return a.B <= 32 ? launch_gemm1_a8(a, st) : launch_gemm1_tiled_a8(a, st);
   if (a.B <= 32) {
     const int grid = grid_for(static_cast<long>(a.max_units16) * (a.I / 32));
     const size_t lds = static_cast<size_t>(4) * 2 * a.H;
@@ -345,12 +567,10 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
+  if (a.a8) return launch_gemm2_a8(a, st);
   const int nkb2 = a.I / 128;
   if (nkb2 <= 4) {
-#ifndef MOE_STREAM_GRID
-#define MOE_STREAM_GRID (256 * 3)
-#endif
-    const int gstream = MOE_STREAM_GRID;  // persistent: waves split the tile list evenly
+    const int gstream = MOE_STREAM_GRID;
 #define MOE_G2S(NK)                                                                      \
   hipLaunchKernelGGL(gemm2_stream_kernel<NK>, dim3(gstream), dim3(kGemmBlock), 0, st,   \
                      a.act, a.w2, a.s2, a.units16, a.counters, a.H, a.I, a.y)
@@ -378,6 +598,42 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   return launch_gemm2_dense_tiled(a, st);
+}
+
+hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
+  const int grid = grid_for(static_cast<long>(a.max_units16) * (a.I / 32));
+  const size_t lds = static_cast<size_t>(4) * 2 * a.H;
+  uint8_t* actq = reinterpret_cast<uint8_t*>(a.act);
+#define MOE_G1A(DD)                                                                              \
+  hipLaunchKernelGGL(gemm1_decode_a8_kernel<DD>, dim3(grid), dim3(kGemmBlock), lds, st, a.xq,    \
+                     a.xs, a.w13, a.s13, a.units16, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp, \
+                     a.limit, actq, a.act_scales)
+  switch (ring_depth(a.H / 128)) {
+    case 4: MOE_G1A(4); break;
+    case 3: MOE_G1A(3); break;
+    case 2: MOE_G1A(2); break;
+    default: MOE_G1A(1); break;
+  }
+#undef MOE_G1A
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st) {
+  const uint8_t* actq = reinterpret_cast<const uint8_t*>(a.act);
+  const int gstream = MOE_STREAM_GRID;
+#define MOE_G2SA(NK)                                                                       \
+  hipLaunchKernelGGL(gemm2_stream_a8_kernel<NK>, dim3(gstream), dim3(kGemmBlock), 0, st,  \
+                     actq, a.act_scales, a.w2, a.s2, a.units16, a.counters, a.H, a.I, a.y)
+  switch (a.I / 128) {
+    case 1: MOE_G2SA(1); break;
+    case 2: MOE_G2SA(2); break;
+    case 3: MOE_G2SA(3); break;
+    default: MOE_G2SA(4); break;
+  }
+#undef MOE_G2SA
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  return launch_gemm2_dense_tiled_a8(a, st);
 }
 
 }  // namespace moe

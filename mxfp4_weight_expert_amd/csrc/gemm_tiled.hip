@@ -321,4 +321,258 @@ hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// W4A8 tiled GEMMs: MXFP8 tokens, E2M1 weights fed to the scaled 16x16x128
+// MFMA as they are (no decode). Same block tile, waves and pipeline as
+// above; a token stage is 128 rows x 128 E4M3 bytes (16 KB) plus the rows'
+// four scale bytes. Wave (wm, wn) computes four 16-row weight tiles (GEMM1:
+// gate features +0 / +16, then the up rows of the same features) x four
+// 16-token tiles: 16 MFMAs per K stage.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr int kTok8Stage = kTileRows * 128;   // E4M3 token bytes of one K stage
+constexpr int kTokScStage = kTileRows * 4;    // their scale bytes
+
+// Byte offset of 16-byte chunk c (0..7) of E4M3 token row r: 16 consecutive
+// rows read at one chunk hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t tok8_off(int r, int c) {
+  return static_cast<uint32_t>(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+}
+}  // namespace
+
+template <bool G1>
+__global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
+    const uint8_t* __restrict__ src, uint32_t src_bytes, const uint8_t* __restrict__ srcs,
+    uint32_t srcs_bytes, const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ counters,
+    const int32_t* __restrict__ sorted_slot, int I, int H, int Kp, int sub, float limit,
+    uint8_t* __restrict__ dstq, uint8_t* __restrict__ dsts, uint16_t* __restrict__ dsty) {
+  __shared__ __attribute__((aligned(16))) uint8_t tok_lds[2 * kTok8Stage];
+  __shared__ __attribute__((aligned(16))) uint8_t tsc_lds[2 * kTokScStage];
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kWStage];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
+  const int K = G1 ? H : I;
+  int ntiles;
+  if (G1) {
+    ntiles = counters[kCtrNumV];
+  } else {
+    ntiles = counters[kCtrGate] == 1 ? counters[kCtrGate + 3] : 0;
+  }
+  const int nspan = G1 ? (I >> 7) : (H >> 8);
+  const int nitems = ntiles * sub * nspan;
+  const int xcd = blockIdx.x & 7;
+  const int per = (nitems + 7) >> 3;
+  const int nblk_x = static_cast<int>(gridDim.x) >> 3;
+  const int t = threadIdx.x;
+  const size_t wrow = static_cast<size_t>(K) >> 1, srow = static_cast<size_t>(K) >> 5;
+  const int wave = wave_index();
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = lane_id();
+  const int c = lane & 15, g = lane >> 4;
+  for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
+    const int item = xcd * per + slot;
+    if (item >= nitems) break;
+    const int span = item % nspan;
+    const int ts = item / nspan;
+    const int tile = ts / sub;
+    const int st = ts - tile * sub;
+    const int4 ti = reinterpret_cast<const int4*>(tiles)[tile];
+    const int e = ti.x;
+    const int row0 = ti.y + st * kTileRows;
+    const int nrows = min(kTileRows, ti.z - st * kTileRows);
+    if (nrows <= 0) continue;
+    const int f0 = G1 ? span * 128 : span * 256;
+    auto grow_of = [&](int rho) -> size_t {
+      if (G1) return static_cast<size_t>(e) * 2 * I + (rho < 128 ? f0 + rho : I + f0 + rho - 128);
+      return static_cast<size_t>(e) * H + f0 + rho;
+    };
+
+    // ---- weight scale rows of the tile -> LDS
+    {
+      const int seg = G1 ? 128 * static_cast<int>(srow) : 256 * static_cast<int>(srow);
+      const uint8_t* s0 = s + grow_of(0) * srow;
+      for (int o = t * 16; o < seg; o += kTiledThreads * 16)
+        *reinterpret_cast<uint4*>(s_lds + o) = ld16(s0 + o);
+      if (G1) {
+        const uint8_t* s1 = s + grow_of(128) * srow;
+        for (int o = t * 16; o < seg; o += kTiledThreads * 16)
+          *reinterpret_cast<uint4*>(s_lds + seg + o) = ld16(s1 + o);
+      }
+    }
+
+    // ---- token rows: thread t moves chunk t%8 of rows 64i + t/8, and the
+    // 4 scale bytes of row t%128 (four threads per row store the same word).
+    const int lc = t & 7, lr = t >> 3, sr = t & 127;
+    uint32_t toff[2], soff;
+    {
+      uint32_t base[3];
+      const int rr[3] = {lr, 64 + lr, sr};
+      if (G1) {
+        const __amdgpu_buffer_rsrc_t ssr =
+            make_rsrc(sorted_slot + row0, static_cast<uint32_t>(nrows) * 4u);
+        uint32_t sv[3];
+#pragma unroll
+        for (int i = 0; i < 3; ++i) sv[i] = bld4(ssr, rr[i] * 4);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) base[i] = sv[i] / static_cast<uint32_t>(Kp);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) base[i] = static_cast<uint32_t>(row0 + rr[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        toff[i] = base[i] * static_cast<uint32_t>(K) + lc * 16 + (rr[i] < nrows ? 0u : kNoRow);
+      soff = base[2] * static_cast<uint32_t>(srow) + (sr < nrows ? 0u : kNoRow);
+    }
+    const __amdgpu_buffer_rsrc_t srs = make_rsrc(src, src_bytes);
+    const __amdgpu_buffer_rsrc_t ssc = make_rsrc(srcs, srcs_bytes);
+    const int wc = t & 3, wr = t >> 2;
+    const uint8_t* wsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) wsrc[i] = w + grow_of(i * 128 + wr) * wrow + wc * 16;
+
+    const int nkb = K >> 7;
+    const int last = nkb - 1;
+    uint4 tv[2], wv[2];
+    uint32_t sv;
+    auto load_stage = [&](int kb) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) tv[i] = bld16(srs, toff[i] + kb * 128);
+      sv = bld4(ssc, soff + kb * 4);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * 64);
+    };
+    auto store_stage = [&](int b) {
+      uint8_t* tb = tok_lds + b * kTok8Stage;
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<uint4*>(tb + tok8_off(i * 64 + lr, lc)) = tv[i];
+      *reinterpret_cast<uint32_t*>(tsc_lds + b * kTokScStage + sr * 4) = sv;
+      uint8_t* wb = w_lds + b * kWStage;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(wb + w_off(i * 128 + wr, wc)) = wv[i];
+    };
+
+    // weight tile rows of the wave's four 16-row MFMA tiles (lane c)
+    int rho[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      if (G1) rho[mt] = (mt >> 1) * 128 + wn * 32 + (mt & 1) * 16 + c;
+      else rho[mt] = wn * 64 + mt * 16 + c;
+    }
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    load_stage(0);
+    __builtin_amdgcn_sched_barrier(0);
+    store_stage(0);
+    __builtin_amdgcn_sched_barrier(0);
+    load_stage(min(1, last));
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int b = kb & 1;
+      const uint8_t* tb = tok_lds + b * kTok8Stage;
+      const uint8_t* tsb = tsc_lds + b * kTokScStage;
+      const uint8_t* wb = w_lds + b * kWStage;
+      uint4 af[4];
+      uint32_t as[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        af[mt] = *reinterpret_cast<const uint4*>(wb + w_off(rho[mt], g));
+        as[mt] = s_lds[rho[mt] * srow + kb * 4 + g];
+      }
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int tr = wm * 64 + nt * 16 + c;
+        const uint4 x0 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, g));
+        const uint4 x1 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, 4 + g));
+        const uint32_t bs = tsb[tr * 4 + g];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_f4xf8(af[mt], as[mt], x0, x1, bs, acc[mt][nt]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      store_stage(b ^ 1);
+      __builtin_amdgcn_sched_barrier(0);
+      load_stage(min(kb + 2, last));
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    }
+
+    // ---- epilogue. Lane (c, g), register v of tile (mt, nt): weight row
+    // 4g + v of the 16-row tile, token row wm*64 + nt*16 + c.
+    if (G1) {
+      const int fbase = f0 + wn * 32;
+      const uint32_t srow_a = static_cast<uint32_t>(I) >> 5;
+      const __amdgpu_buffer_rsrc_t qrs =
+          make_rsrc(dstq + static_cast<size_t>(row0) * I, static_cast<uint32_t>(nrows) * I);
+      const __amdgpu_buffer_rsrc_t ars =
+          make_rsrc(dsts + static_cast<size_t>(row0) * srow_a, static_cast<uint32_t>(nrows) * srow_a);
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const uint32_t tr = static_cast<uint32_t>(wm * 64 + nt * 16 + c);
+        float a[8];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) a[4 * h + v] = swiglu(acc[h][nt][v], acc[2 + h][nt][v], limit);
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
+        amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
+        const uint32_t sb = mxfp8_scale_byte(amax);
+        const float inv = mxfp8_inv_scale(sb);
+        const uint32_t o0 = tr * I + fbase + 4 * g;
+        bst4(qrs, o0, pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
+        bst4(qrs, o0 + 16, pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
+        bst1(ars, g == 0 ? tr * srow_a + (fbase >> 5) : kNoRow, sb);
+      }
+    } else {
+      const int fbase = f0 + wn * 64;
+      const __amdgpu_buffer_rsrc_t ors =
+          make_rsrc(dsty + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
+          pk.y = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
+          const uint32_t off = static_cast<uint32_t>(wm * 64 + nt * 16 + c) * H * 2 +
+                               (fbase + 16 * mt + 4 * g) * 2;
+          bst8(ors, off, pk);
+        }
+    }
+  }  // items
+}
+
+hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
+  const int sub = a.B > kTileRows ? a.B / kTileRows : 1;
+  const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128));
+  hipLaunchKernelGGL(gemm_tiled_a8_kernel<true>, dim3(grid), dim3(kTiledThreads),
+                     static_cast<size_t>(8) * a.H, st, a.xq,
+                     static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H), a.xs,
+                     static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H / 32), a.w13, a.s13,
+                     a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp, sub, a.limit,
+                     reinterpret_cast<uint8_t*>(a.act), a.act_scales, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
+  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256));
+  hipLaunchKernelGGL(gemm_tiled_a8_kernel<false>, dim3(grid), dim3(kTiledThreads),
+                     static_cast<size_t>(8) * a.I, st, reinterpret_cast<const uint8_t*>(a.act),
+                     static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I), a.act_scales,
+                     static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / 32), a.w2, a.s2,
+                     a.dense_tiles, a.counters, a.sorted_slot, a.I, a.H, a.Kp, 1, a.limit, nullptr,
+                     nullptr, a.y);
+  return hipGetLastError();
+}
+
 }  // namespace moe

@@ -48,8 +48,13 @@ struct GemmArgs {
   const int32_t* sorted_slot;
   int T, H, I, Kp, B, kmax_v, max_dense_tiles, max_units16, rows_pad;
   float limit;
-  uint16_t* act;  // [rows_pad, I] bf16
+  uint16_t* act;  // [rows_pad, I] bf16 (W4A16), or E4M3 codes (W4A8)
   uint16_t* y;    // [rows_pad, H] bf16
+  // W4A8 only (a8 != 0): MXFP8 x and act scales
+  int a8;
+  const uint8_t* xq;    // [T, H] E4M3
+  const uint8_t* xs;    // [T, H/32] E8M0
+  uint8_t* act_scales;  // [rows_pad, I/32] E8M0
 };
 hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st);  // split + dense, gated on device
@@ -57,6 +62,15 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st);  // split + dense, g
 // chunk table (B >= 64), and the dense GEMM2 path over the dense tiles.
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st);
+
+// x -> MXFP8 (W4A8 path): xq [T, H] E4M3 codes, xs [T, H/32] E8M0 scales.
+hipError_t launch_quant_x(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs,
+                          hipStream_t st);
+// W4A8 kernels (the launchers above dispatch to them when a8 is set).
+hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st);
 
 struct FinalizeArgs {
   const uint16_t* y;

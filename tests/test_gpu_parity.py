@@ -106,3 +106,76 @@ def test_kimi_shape_token_sweep(kimi_weights, T, B):
     check_maps(s, maps_np(s, ws), ref)
     toks = _sample_tokens(T, 3, T)
     check_out(out_np(out)[toks], oracle.sampled_forward(s, inp, toks), f"T{T}/B{B}")
+
+
+# ------------------------------------------------------------------ W4A8
+# MXFP8 activations: x's codes and scales bit-exact (the quantiser is exact in
+# fp32); the layer output to the same tolerances as W4A16 against the
+# quantisation-aware oracle (act is quantised from fp32 on the GPU and from
+# fp64 in the oracle, so an act code at a rounding boundary may differ by one).
+SMALL_A8 = [
+    LayerShape("a8_decode_small", T=64, E=64, E_g=64, topk=8, H=512, I=256, B=32, a_dtype="mxfp8"),
+    LayerShape("a8_ep_zipf", T=96, E=64, E_g=128, topk=8, H=1024, I=128, B=16, expert_offset=64,
+               routing="zipf", a_dtype="mxfp8"),
+    LayerShape("a8_shared_clamp", T=48, E=32, E_g=32, topk=4, H=512, I=384, B=32, S=1,
+               swiglu_limit=7.0, a_dtype="mxfp8"),
+    LayerShape("a8_prefill_small", T=1024, E=16, E_g=16, topk=4, H=512, I=128, B=128,
+               a_dtype="mxfp8"),
+    LayerShape("a8_prefill_b256", T=700, E=6, E_g=6, topk=2, H=1536, I=256, B=256, a_dtype="mxfp8"),
+    LayerShape("a8_one_token", T=1, E=32, E_g=32, topk=8, H=512, I=128, B=16, a_dtype="mxfp8"),
+]
+
+
+def _check_xq(got, ref):
+    assert np.array_equal(got["xq"], ref["xq"]), "MXFP8 x codes differ"
+    assert np.array_equal(got["xs"], ref["xs"]), "MXFP8 x scales differ"
+
+
+@pytest.mark.parametrize("force", list(FORCES))
+@pytest.mark.parametrize("s", SMALL_A8, ids=lambda s: s.name)
+def test_w4a8_small_full_parity(s, force):
+    say(f"[w4a8] {s.name} force={force}")
+    inp = make_inputs(s, 700 + SMALL_A8.index(s))
+    ref = oracle.reference_forward(s, inp, force_path=FORCES[force])
+    dev = to_device(s, inp)
+    out, ws = run(s, dev, force)
+    got = maps_np(s, ws, force)
+    check_maps(s, got, ref)
+    _check_xq(got, ref)
+    check_out(out_np(out), ref["out"], f"{s.name}/{force}")
+
+
+def test_w4a8_quant_special_values():
+    """Zeros, signed zeros, subnormal-range and saturating blocks of x."""
+    s = LayerShape("a8_special", T=4, E=4, E_g=4, topk=2, H=512, I=128, B=16, a_dtype="mxfp8")
+    inp = make_inputs(s, 77)
+    x = inp["x"].copy()
+    x[0, :32] = 0                      # all-zero block -> scale 0, codes 0
+    x[0, 32:64] = 0x8000               # negative zeros -> codes 0x80
+    x[1, :32] = 0x0001                 # bf16 subnormals: scale byte clamps to 0
+    x[1, 32:64] = 0x7F00               # huge values (2^127): scale byte 246
+    x[2, :32] = np.arange(32, dtype=np.uint16) + 0x3F80  # 1.0 .. just above, ties
+    x[3, :32] = 0xC3E0                 # -448 exactly
+    x[3, 32:64] = 0x43F8               # 496: saturates to 448 after scaling
+    inp["x"] = x
+    ref = oracle.reference_forward(s, inp)
+    out, ws = run(s, to_device(s, inp))
+    _check_xq(maps_np(s, ws), ref)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_w4a8_config_parity(name):
+    s = CONFIGS[name].replace(a_dtype="mxfp8", name=name + "_w4a8")
+    say(f"[w4a8 config] {s.name}")
+    inp = make_inputs(s, config_seed(name))
+    dev = to_device(s, inp)
+    ref = oracle.reference_forward(s, inp, compute_out=False)
+    toks = _sample_tokens(s.T, 6 if name == "prefill" else 8, 11)
+    want = oracle.sampled_forward(s, inp, toks)
+    out, ws = run(s, dev)
+    got = maps_np(s, ws)
+    check_maps(s, got, ref)
+    _check_xq(got, ref)
+    check_out(out_np(out)[toks], want, f"{s.name} sampled tokens {len(toks)}")
+    del out, ws
+    torch.cuda.empty_cache()
