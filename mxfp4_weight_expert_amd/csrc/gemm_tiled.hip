@@ -39,40 +39,51 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTileRows = 128;                     // token rows per tile
 constexpr int kTileWRows = 256;                    // weight rows per tile
-constexpr int kTokStage = kTileRows * 128 * 2;     // token bytes of one K stage
-constexpr int kWStage = kTileWRows * 64;           // packed weight bytes of one K stage
 constexpr int kTiledThreads = 512;
+constexpr int kTokStage = kTileRows * 128 * 2;     // bf16 token bytes of one K stage (32 KB)
+constexpr int kTok8Stage = kTileRows * 128;        // E4M3 token bytes of one K stage (16 KB)
+constexpr int kWStage = kTileWRows * 64;           // packed weight bytes of one K stage (16 KB)
+constexpr int kScStage = kTileWRows * 4;           // weight scale bytes of one K stage
+constexpr int kRing = 3;                           // stages of global loads in flight
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Byte offset of 16-byte chunk c (0..15) of token row r inside a stage. The
-// XOR swizzle puts 16 consecutive rows read at one chunk on 16 distinct
-// 16-byte bank groups, and 16 consecutive chunks of one row written by 16
-// lanes likewise.
+// Byte offset of 16-byte chunk c (0..15) of bf16 token row r (256-byte rows)
+// inside a stage. The XOR swizzle puts 16 consecutive rows read at one chunk
+// on 16 distinct 16-byte bank groups, and 16 consecutive chunks of one row
+// written by 16 lanes likewise.
 __device__ __forceinline__ uint32_t tok_off(int r, int c) {
   return static_cast<uint32_t>(r * 256 + ((c ^ (r & 15)) << 4));
 }
-// Byte offset of 16-byte chunk c (0..3) of weight row rho: chunk-major, so
-// the 32 rows of one MFMA fragment are 32 consecutive 16-byte slots.
+// Byte offset of 16-byte chunk c (0..7) of E4M3 token row r (128-byte rows):
+// 16 consecutive rows read at one chunk differ in row parity or in
+// (row >> 1) & 7, so they hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t tok8_off(int r, int c) {
+  return static_cast<uint32_t>(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
+}
+// Byte offset of 16-byte chunk c (0..3) of weight row rho in a stage:
+// chunk-major, so the rows of one MFMA fragment are consecutive 16-byte
+// slots.
 __device__ __forceinline__ uint32_t w_off(int rho, int c) {
   return static_cast<uint32_t>(c * (kTileWRows * 16) + rho * 16);
 }
 
 }  // namespace
 
-// LDS: two token stages and two weight stages (static, 96 KB) plus the
-// tile's scale rows (dynamic, 256 * K/32 bytes).
+// LDS: two stages of tokens, packed weights and weight scales (98 KB). The
+// stage copy goes global -> registers -> LDS with kRing stages of loads in
+// flight, so every load has two full stages of MFMA work to arrive.
 template <bool G1>
-__global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(
+__global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     const uint16_t* __restrict__ src, uint32_t src_bytes, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ s, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int I, int H,
     int Kp, int sub, float limit, uint16_t* __restrict__ dst) {
   __shared__ __attribute__((aligned(16))) uint8_t tok_lds[2 * kTokStage];
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kWStage];
-  extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2 * kScStage];
   const int K = G1 ? H : I;
   int ntiles;
   if (G1) {
@@ -85,6 +96,16 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(
   const int xcd = blockIdx.x & 7;
   const int per = (nitems + 7) >> 3;
   const int nblk_x = static_cast<int>(gridDim.x) >> 3;  // blocks per XCD
+  const int t = threadIdx.x;
+  const size_t wrow = static_cast<size_t>(K) >> 1, srow = static_cast<size_t>(K) >> 5;
+  const int wave = wave_index();
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = lane_id();
+  const int r = lane & 31, h = lane >> 5;
+  // thread roles in the stage copy: token chunk t%16 of rows 32i + t/16;
+  // weight chunk t%4 of tile rows 128i + t/4; the 4 scale bytes of tile row
+  // t%256 (threads t and t + 256 store the same word)
+  const int lc = t & 15, lr = t >> 4, wc = t & 3, wr = t >> 2, sr = t & 255;
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
     const int item = xcd * per + slot;
     if (item >= nitems) break;
@@ -97,95 +118,81 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(
     const int row0 = ti.y + st * kTileRows;
     const int nrows = min(kTileRows, ti.z - st * kTileRows);
     if (nrows <= 0) continue;
-    const int t = threadIdx.x;
-    const size_t wrow = static_cast<size_t>(K) >> 1, srow = static_cast<size_t>(K) >> 5;
-    // Global weight row of tile row rho: GEMM1 rows [0, 128) are the gate rows
-    // of features f0 + rho, rows [128, 256) the up rows of the same features.
+    // Tile row rho of the weights: GEMM1 rows [0, 128) are the gate rows of
+    // features f0 + rho, rows [128, 256) the up rows of the same features;
+    // as a row of expert e's block.
     const int f0 = G1 ? span * 128 : span * 256;
-    auto grow_of = [&](int rho) -> size_t {
-      if (G1) return static_cast<size_t>(e) * 2 * I + (rho < 128 ? f0 + rho : I + f0 + rho - 128);
-      return static_cast<size_t>(e) * H + f0 + rho;
+    auto erow_of = [&](int rho) -> uint32_t {
+      if (G1) return static_cast<uint32_t>(rho < 128 ? f0 + rho : I + f0 + rho - 128);
+      return static_cast<uint32_t>(f0 + rho);
     };
 
-    // ---- scale rows of the tile -> LDS (256 rows x K/32 bytes, row-major)
-    {
-      const int seg = G1 ? 128 * static_cast<int>(srow) : 256 * static_cast<int>(srow);
-      const uint8_t* s0 = s + grow_of(0) * srow;
-      for (int o = t * 16; o < seg; o += kTiledThreads * 16)
-        *reinterpret_cast<uint4*>(s_lds + o) = ld16(s0 + o);
-      if (G1) {
-        const uint8_t* s1 = s + grow_of(128) * srow;
-        for (int o = t * 16; o < seg; o += kTiledThreads * 16)
-          *reinterpret_cast<uint4*>(s_lds + seg + o) = ld16(s1 + o);
-      }
-    }
-
-    // ---- token tile loads: thread t moves chunk t%16 of rows 32i + t/16.
-    // Rows past the tile's end get an out-of-range offset (their loads return
-    // zero). The row -> slot reads are buffer loads too, so that none of them
-    // sits behind a branch.
-    const int lc = t & 15, lr = t >> 4;
+    // Token rows past the tile's end get an out-of-range offset (their loads
+    // return zero). The row -> slot reads are buffer loads too, so that none
+    // of them sits behind a branch.
     uint32_t toff[4];
     if (G1) {
       const __amdgpu_buffer_rsrc_t ssr =
           make_rsrc(sorted_slot + row0, static_cast<uint32_t>(nrows) * 4u);
       uint32_t slotv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        slotv[i] = __builtin_amdgcn_raw_buffer_load_b32(ssr, (i * 32 + lr) * 4, 0, 0);
+      for (int i = 0; i < 4; ++i) slotv[i] = bld4(ssr, (i * 32 + lr) * 4);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i * 32 + lr;
+        const int rr = i * 32 + lr;
         const uint32_t tok = slotv[i] / static_cast<uint32_t>(Kp);
-        toff[i] = tok * static_cast<uint32_t>(K) * 2u + lc * 16 + (r < nrows ? 0u : kNoRow);
+        toff[i] = tok * static_cast<uint32_t>(K) * 2u + lc * 16 + (rr < nrows ? 0u : kNoRow);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i * 32 + lr;
-        toff[i] = static_cast<uint32_t>(row0 + r) * static_cast<uint32_t>(K) * 2u + lc * 16 +
-                  (r < nrows ? 0u : kNoRow);
+        const int rr = i * 32 + lr;
+        toff[i] = static_cast<uint32_t>(row0 + rr) * static_cast<uint32_t>(K) * 2u + lc * 16 +
+                  (rr < nrows ? 0u : kNoRow);
       }
     }
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(src, src_bytes);
-    // ---- weight tile loads: thread t moves chunk t%4 of tile rows 128i + t/4
-    const int wc = t & 3, wr = t >> 2;
-    const uint8_t* wsrc[2];
+    // The expert's weight and scale rows through buffers, so that per-lane
+    // offsets are 32-bit.
+    const size_t erows = G1 ? static_cast<size_t>(2) * I : static_cast<size_t>(H);
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(w + static_cast<size_t>(e) * erows * wrow, static_cast<uint32_t>(erows * wrow));
+    const __amdgpu_buffer_rsrc_t scs =
+        make_rsrc(s + static_cast<size_t>(e) * erows * srow, static_cast<uint32_t>(erows * srow));
+    uint32_t woff[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wsrc[i] = w + grow_of(i * 128 + wr) * wrow + wc * 16;
+    for (int i = 0; i < 2; ++i) woff[i] = erow_of(i * 128 + wr) * static_cast<uint32_t>(wrow) + wc * 16;
+    const uint32_t soff = erow_of(sr) * static_cast<uint32_t>(srow);
 
     const int nkb = K >> 7;
     const int last = nkb - 1;
-    uint4 tv[4], wv[2];
-    auto load_stage = [&](int kb) {
+    uint4 tv[kRing][4], wv[kRing][2];
+    uint32_t sv[kRing];
+    auto load_stage = [&](int kb, int sl) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tv[i] = bld16(srs, toff[i] + kb * 256);
+      for (int i = 0; i < 4; ++i) tv[sl][i] = bld16(srs, toff[i] + kb * 256);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * 64);
+      for (int i = 0; i < 2; ++i) wv[sl][i] = bld16(wrs, woff[i] + kb * 64);
+      sv[sl] = bld4(scs, soff + kb * 4);
     };
-    auto store_stage = [&](int b) {
+    auto store_stage = [&](int b, int sl) {
       uint8_t* tb = tok_lds + b * kTokStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tb + tok_off(i * 32 + lr, lc)) = tv[i];
+      for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tb + tok_off(i * 32 + lr, lc)) = tv[sl][i];
       uint8_t* wb = w_lds + b * kWStage;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(wb + w_off(i * 128 + wr, wc)) = wv[i];
+      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(wb + w_off(i * 128 + wr, wc)) = wv[sl][i];
+      *reinterpret_cast<uint32_t*>(sc_lds + b * kScStage + sr * 4) = sv[sl];
     };
 
-    // ---- this wave's share
-    const int wave = wave_index();
-    const int wm = wave & 1, wn = wave >> 1;
-    const int lane = lane_id();
-    const int r = lane & 31, h = lane >> 5;
     int rho[2];  // tile weight rows of the wave's two 32-row MFMA tiles (lane r)
     if (G1) {
-      rho[0] = wn * 32 + r;         // gate
-      rho[1] = 128 + wn * 32 + r;   // up, same features
+      rho[0] = wn * 32 + r;        // gate
+      rho[1] = 128 + wn * 32 + r;  // up, same features
     } else {
       rho[0] = wn * 64 + r;
       rho[1] = wn * 64 + 32 + r;
     }
-    const uint8_t* srow_lds[2] = {s_lds + rho[0] * srow, s_lds + rho[1] * srow};
 
     f32x16_t acc[2][2];
 #pragma unroll
@@ -195,22 +202,21 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
 
-    // Prologue: stage 0 in LDS, stage 1 in flight.
-    load_stage(0);
-    __builtin_amdgcn_sched_barrier(0);
-    store_stage(0);
-    __builtin_amdgcn_sched_barrier(0);
-    load_stage(min(1, last));
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-
-    for (int kb = 0; kb < nkb; ++kb) {
+    // One K stage with register slot sl = kb % kRing: multiply the stage in
+    // LDS buffer kb & 1, move stage kb+1 (slot (sl+1) % kRing, loaded two
+    // stages ago) into the other buffer (read last in stage kb-1, which
+    // every wave finished before the previous barrier), refill slot sl with
+    // stage kb + kRing (near the end the last stage again: loaded, never
+    // used). Loads retire in issue order; the pinned order keeps each wait
+    // to the one stage it needs.
+    auto stage = [&](int kb, int sl) {
       const int b = kb & 1;
       const uint8_t* tb = tok_lds + b * kTokStage;
       const uint8_t* wb = w_lds + b * kWStage;
+      const uint8_t* sb = sc_lds + b * kScStage;
       uint32_t sdw[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(srow_lds[m] + kb * 4);
+      for (int m = 0; m < 2; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(sb + rho[m] * 4);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         bf16x8_t a[2][4];
@@ -235,18 +241,31 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(
             for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m][j], bf[n], acc[m][n]);
         }
       }
-      // Stage kb+1 into the other buffers (read last in stage kb-1, finished
-      // by every wave before the previous barrier), then start the loads of
-      // stage kb+2 (near the end the last stage again: loaded, never used).
-      // Loads retire in issue order; the pinned order keeps each wait to what
-      // it needs.
       __builtin_amdgcn_sched_barrier(0);
-      store_stage(b ^ 1);
+      store_stage(b ^ 1, (sl + 1) % kRing);
       __builtin_amdgcn_sched_barrier(0);
-      load_stage(min(kb + 2, last));
+      load_stage(min(kb + kRing, last), sl);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
+    };
+
+    // Prologue: stages 0 .. kRing-1 in flight, stage 0 in LDS.
+#pragma unroll
+    for (int sl = 0; sl < kRing; ++sl) {
+      load_stage(min(sl, last), sl);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    store_stage(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    int kb = 0;
+    for (; kb + kRing - 1 < nkb; kb += kRing) {
+#pragma unroll
+      for (int sl = 0; sl < kRing; ++sl) stage(kb + sl, sl);
+    }
+#pragma unroll
+    for (int sl = 0; sl < kRing - 1; ++sl)
+      if (kb + sl < nkb) stage(kb + sl, sl);
 
     // ---- epilogue. Lane (r, h), accumulator register 4*b4 + i holds weight
     // row 8*b4 + 4*h + i of the 32-row tile against token row 32*n + r of the
@@ -292,30 +311,183 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_kernel(
   }  // items
 }
 
-// Persistent grid: one block per CU (a block holds 96 KB of LDS and two
-// waves per SIMD), at most one block per item; a multiple of 8 so that every
-// XCD gets the same number of blocks.
-static int tiled_grid(long items) {
+// ---------------------------------------------------------------------------
+// Dense GEMM2, act tile resident in LDS (I <= 384). A block owns a 128-row
+// dense tile: it copies the tile's act rows (128 x I bf16) into LDS once and
+// then walks all H / 256 output spans. Wave (wm, wn) computes 64 W2 rows x
+// 64 tokens per span, its weights coming straight from global memory into
+// registers: K step kb of the next span is loaded into the registers of
+// step kb right after they are decoded, so the loads have about one span
+// of MFMA work to arrive and no barrier is needed between spans.
+// ---------------------------------------------------------------------------
+template <int NKB>
+__global__ __launch_bounds__(kTiledThreads, 2) void gemm2_resident_kernel(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, const uint8_t* __restrict__ w2,
+    const uint8_t* __restrict__ s2, const int32_t* __restrict__ tiles,
+    const int32_t* __restrict__ counters, int H, uint16_t* __restrict__ y) {
+  constexpr int I = NKB * 128;
+  constexpr int kRowB = I * 2;                 // act row bytes
+  constexpr int kScW = I / 128;                // scale dwords per W2 row
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kTileRows * kRowB];
+  const int ntiles = counters[kCtrGate] == 1 ? counters[kCtrGate + 3] : 0;
+  const int xcd = blockIdx.x & 7;
+  const int per = (ntiles + 7) >> 3;
+  const int nblk_x = static_cast<int>(gridDim.x) >> 3;
+  const int t = threadIdx.x;
+  const int wave = wave_index();
+  const int wm = wave & 1, wn = wave >> 1;
+  const int lane = lane_id();
+  const int r = lane & 31, h = lane >> 5;
+  const int nspan = H >> 8;
+  constexpr uint32_t wrow = I / 2, srow = I / 32;
+  // act chunk (16 bytes) c of tile row rr sits at rr * kRowB + 16 * swz(c):
+  // within each 16-chunk group the chunk index is XORed with rr & 15
+  auto a_off = [](int rr, int c) -> uint32_t {
+    return static_cast<uint32_t>(rr * kRowB + (((c & ~15) | ((c ^ rr) & 15)) << 4));
+  };
+  for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
+    const int tile = xcd * per + slot;
+    if (tile >= ntiles) break;
+    const int4 ti = reinterpret_cast<const int4*>(tiles)[tile];
+    const int e = ti.x, row0 = ti.y, nrows = ti.z;
+    // ---- act tile -> LDS (rows past nrows read as zero)
+    {
+      const __amdgpu_buffer_rsrc_t ars = make_rsrc(act, act_bytes);
+      constexpr int kChunks = kTileRows * (kRowB / 16);
+      constexpr int kPer = kChunks / kTiledThreads;
+      uint4 v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int q = i * kTiledThreads + t;
+        const int rr = q / (kRowB / 16), c = q % (kRowB / 16);
+        v[i] = bld16(ars, static_cast<uint32_t>(row0 + rr) * kRowB + c * 16 +
+                              (rr < nrows ? 0u : kNoRow));
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int q = i * kTiledThreads + t;
+        const int rr = q / (kRowB / 16), c = q % (kRowB / 16);
+        *reinterpret_cast<uint4*>(a_lds + a_off(rr, c)) = v[i];
+      }
+    }
+    // ---- weights of span 0 into registers
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(w2 + static_cast<size_t>(e) * H * wrow, static_cast<uint32_t>(H) * wrow);
+    const __amdgpu_buffer_rsrc_t scs =
+        make_rsrc(s2 + static_cast<size_t>(e) * H * srow, static_cast<uint32_t>(H) * srow);
+    uint4 wr[NKB][2][2];   // [kb][m][q]
+    uint32_t sw[NKB][2];   // [kb][m]: scale bytes of groups 4kb .. 4kb+3
+    auto load_w = [&](int sp, int kb) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t row = static_cast<uint32_t>(sp * 256 + wn * 64 + m * 32 + r);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) wr[kb][m][q] = bld16(wrs, row * wrow + kb * 64 + q * 32 + h * 16);
+        sw[kb][m] = bld4(scs, row * srow + kb * 4);
+      }
+    };
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) load_w(0, kb);
+    __syncthreads();  // act tile visible to every wave
+
+    for (int sp = 0; sp < nspan; ++sp) {
+      f32x16_t acc[2][2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
+      const int spn = min(sp + 1, nspan - 1);  // last span: reload it, unused
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+          bf16x8_t a[2][4];
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            const float scale = e8m0_scale_operand((sw[kb][m] >> (8 * (2 * q + h))) & 0xffu);
+            const uint32_t dw[4] = {wr[kb][m][q].x, wr[kb][m][q].y, wr[kb][m][q].z, wr[kb][m][q].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a[m][j] = decode_fp4x8(dw[j], scale);
+          }
+          if (q == 1) {  // step kb fully decoded: refill it with the next span
+            __builtin_amdgcn_sched_barrier(0);
+            load_w(spn, kb);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            bf16x8_t bf[2];
+#pragma unroll
+            for (int n = 0; n < 2; ++n)
+              bf[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
+                  a_lds + a_off(wm * 64 + n * 32 + r, kb * 16 + 8 * q + 4 * h + j)));
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+              for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m][j], bf[n], acc[m][n]);
+          }
+        }
+      }
+      // ---- this span's 64 x 64 outputs of the wave
+      const int fbase = sp * 256 + wn * 64;
+      const __amdgpu_buffer_rsrc_t ors =
+          make_rsrc(y + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+#pragma unroll
+          for (int b4 = 0; b4 < 4; ++b4) {
+            uint2 pk;
+            pk.x = pack_bf16x2(acc[m][n][4 * b4 + 0], acc[m][n][4 * b4 + 1]);
+            pk.y = pack_bf16x2(acc[m][n][4 * b4 + 2], acc[m][n][4 * b4 + 3]);
+            const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * H * 2 +
+                                 (fbase + 32 * m + 8 * b4 + 4 * h) * 2;
+            bst8(ors, off, pk);
+          }
+    }
+    __syncthreads();  // every wave done with the act tile before the next copy
+  }
+}
+
+// Persistent grid: `per_cu` blocks per CU (LDS and registers allow two for
+// the bf16 kernel, one for the W4A8 kernel), at most one block per item; a
+// multiple of 8 so that every XCD gets the same number of blocks.
+static int tiled_grid(long items, int per_cu) {
   long per = (items + 7) / 8;
   if (per < 1) per = 1;
-  if (per > 32) per = 32;
+  if (per > 32 * per_cu) per = 32 * per_cu;
   return static_cast<int>(8 * per);
 }
 
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st) {
   const int sub = a.B > kTileRows ? a.B / kTileRows : 1;
-  const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128));
-  hipLaunchKernelGGL(gemm_tiled_kernel<true>, dim3(grid), dim3(kTiledThreads),
-                     static_cast<size_t>(8) * a.H, st, a.x,
+  const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128), 1);
+  hipLaunchKernelGGL(gemm_tiled_kernel<true>, dim3(grid), dim3(kTiledThreads), 0, st, a.x,
                      static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H * 2), a.w13, a.s13,
                      a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp, sub, a.limit, a.act);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
-  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256));
-  hipLaunchKernelGGL(gemm_tiled_kernel<false>, dim3(grid), dim3(kTiledThreads),
-                     static_cast<size_t>(8) * a.I, st, a.act,
+  if (a.I <= 384) {  // act tile (128 x I bf16) and the weight registers fit
+    const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles), 1);
+    const uint32_t act_bytes = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2);
+#define MOE_G2R(NK)                                                                        \
+  hipLaunchKernelGGL(gemm2_resident_kernel<NK>, dim3(grid), dim3(kTiledThreads), 0, st,   \
+                     a.act, act_bytes, a.w2, a.s2, a.dense_tiles, a.counters, a.H, a.y)
+    switch (a.I / 128) {
+      case 1: MOE_G2R(1); break;
+      case 2: MOE_G2R(2); break;
+      default: MOE_G2R(3); break;
+    }
+#undef MOE_G2R
+    return hipGetLastError();
+  }
+  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256), 1);
+  hipLaunchKernelGGL(gemm_tiled_kernel<false>, dim3(grid), dim3(kTiledThreads), 0, st, a.act,
                      static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2), a.w2, a.s2,
                      a.dense_tiles, a.counters, a.sorted_slot, a.I, a.H, a.Kp, 1, a.limit, a.y);
   return hipGetLastError();
@@ -330,14 +502,8 @@ hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
 // 16-token tiles: 16 MFMAs per K stage.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int kTok8Stage = kTileRows * 128;   // E4M3 token bytes of one K stage
-constexpr int kTokScStage = kTileRows * 4;    // their scale bytes
+constexpr int kTokScStage = kTileRows * 4;    // token scale bytes of one K stage
 
-// Byte offset of 16-byte chunk c (0..7) of E4M3 token row r: 16 consecutive
-// rows read at one chunk hit 16 distinct 16-byte bank groups.
-__device__ __forceinline__ uint32_t tok8_off(int r, int c) {
-  return static_cast<uint32_t>(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
-}
 }  // namespace
 
 template <bool G1>
@@ -554,7 +720,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
 
 hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
   const int sub = a.B > kTileRows ? a.B / kTileRows : 1;
-  const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128));
+  const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128), 1);
   hipLaunchKernelGGL(gemm_tiled_a8_kernel<true>, dim3(grid), dim3(kTiledThreads),
                      static_cast<size_t>(8) * a.H, st, a.xq,
                      static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H), a.xs,
@@ -565,7 +731,7 @@ hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
-  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256));
+  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256), 1);
   hipLaunchKernelGGL(gemm_tiled_a8_kernel<false>, dim3(grid), dim3(kTiledThreads),
                      static_cast<size_t>(8) * a.I, st, reinterpret_cast<const uint8_t*>(a.act),
                      static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I), a.act_scales,
