@@ -43,8 +43,8 @@ constexpr int kTiledThreads = 512;
 constexpr int kTokStage = kTileRows * 128 * 2;     // bf16 token bytes of one K stage (32 KB)
 constexpr int kTok8Stage = kTileRows * 128;        // E4M3 token bytes of one K stage (16 KB)
 constexpr int kWStage = kTileWRows * 64;           // packed weight bytes of one K stage (16 KB)
-constexpr int kScStage = kTileWRows * 4;           // weight scale bytes of one K stage
-constexpr int kRing = 3;                           // stages of global loads in flight
+constexpr int kScGroup = kTileWRows * 16;          // weight scale bytes of four K stages
+constexpr int kRing = 4;                           // stages of global loads in flight
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -64,10 +64,12 @@ __device__ __forceinline__ uint32_t tok8_off(int r, int c) {
   return static_cast<uint32_t>(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
 }
 // Byte offset of 16-byte chunk c (0..3) of weight row rho in a stage:
-// chunk-major, so the rows of one MFMA fragment are consecutive 16-byte
-// slots.
+// chunk-major, so the 32 rows of one MFMA fragment are a permutation of 32
+// consecutive 16-byte slots (conflict-free reads); the XOR with 4c spreads
+// the four chunks of a row, written by four neighbouring lanes, over
+// distinct bank groups.
 __device__ __forceinline__ uint32_t w_off(int rho, int c) {
-  return static_cast<uint32_t>(c * (kTileWRows * 16) + rho * 16);
+  return static_cast<uint32_t>(c * (kTileWRows * 16) + ((rho ^ (c << 2)) << 4));
 }
 
 }  // namespace
@@ -83,7 +85,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     int Kp, int sub, float limit, uint16_t* __restrict__ dst) {
   __shared__ __attribute__((aligned(16))) uint8_t tok_lds[2 * kTokStage];
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kWStage];
-  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2 * kScStage];
+  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2 * kScGroup];
   const int K = G1 ? H : I;
   int ntiles;
   if (G1) {
@@ -103,8 +105,8 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
   const int lane = lane_id();
   const int r = lane & 31, h = lane >> 5;
   // thread roles in the stage copy: token chunk t%16 of rows 32i + t/16;
-  // weight chunk t%4 of tile rows 128i + t/4; the 4 scale bytes of tile row
-  // t%256 (threads t and t + 256 store the same word)
+  // weight chunk t%4 of tile rows 128i + t/4; the 16 scale bytes (four
+  // stages) of tile row t%256 (threads t and t + 256 store the same bytes)
   const int lc = t & 15, lr = t >> 4, wc = t & 3, wr = t >> 2, sr = t & 255;
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
     const int item = xcd * per + slot;
@@ -166,14 +168,18 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 
     const int nkb = K >> 7;
     const int last = nkb - 1;
+    const int lastg = last >> 2;
     uint4 tv[kRing][4], wv[kRing][2];
-    uint32_t sv[kRing];
+    uint4 sg;  // scale bytes of the next group of four stages
     auto load_stage = [&](int kb, int sl) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) tv[sl][i] = bld16(srs, toff[i] + kb * 256);
 #pragma unroll
       for (int i = 0; i < 2; ++i) wv[sl][i] = bld16(wrs, woff[i] + kb * 64);
-      sv[sl] = bld4(scs, soff + kb * 4);
+    };
+    auto load_group = [&](int g) { sg = bld16(scs, soff + g * 16); };
+    auto store_group = [&](int g) {
+      *reinterpret_cast<uint4*>(sc_lds + (g & 1) * kScGroup + sr * 16) = sg;
     };
     auto store_stage = [&](int b, int sl) {
       uint8_t* tb = tok_lds + b * kTokStage;
@@ -182,7 +188,6 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       uint8_t* wb = w_lds + b * kWStage;
 #pragma unroll
       for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(wb + w_off(i * 128 + wr, wc)) = wv[sl][i];
-      *reinterpret_cast<uint32_t*>(sc_lds + b * kScStage + sr * 4) = sv[sl];
     };
 
     int rho[2];  // tile weight rows of the wave's two 32-row MFMA tiles (lane r)
@@ -203,20 +208,22 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
         for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
 
     // One K stage with register slot sl = kb % kRing: multiply the stage in
-    // LDS buffer kb & 1, move stage kb+1 (slot (sl+1) % kRing, loaded two
-    // stages ago) into the other buffer (read last in stage kb-1, which
-    // every wave finished before the previous barrier), refill slot sl with
-    // stage kb + kRing (near the end the last stage again: loaded, never
-    // used). Loads retire in issue order; the pinned order keeps each wait
-    // to the one stage it needs.
+    // LDS buffer kb & 1, move stage kb+1 (slot (sl+1) % kRing, loaded
+    // kRing - 1 stages ago) into the other buffer (read last in stage kb-1,
+    // which every wave finished before the previous barrier), refill slot sl
+    // with stage kb + kRing (near the end the last stage again: loaded,
+    // never used). Scales move in groups of four stages (kRing = 4): the
+    // first stage of group g loads group g + 1, its last stage stores it to
+    // the other scale buffer (last read in group g - 1). Loads retire in
+    // issue order; the pinned order keeps each wait to what it needs.
     auto stage = [&](int kb, int sl) {
       const int b = kb & 1;
       const uint8_t* tb = tok_lds + b * kTokStage;
       const uint8_t* wb = w_lds + b * kWStage;
-      const uint8_t* sb = sc_lds + b * kScStage;
+      const uint8_t* sb = sc_lds + ((kb >> 2) & 1) * kScGroup + (kb & 3) * 4;
       uint32_t sdw[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(sb + rho[m] * 4);
+      for (int m = 0; m < 2; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(sb + rho[m] * 16);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         bf16x8_t a[2][4];
@@ -243,18 +250,24 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       }
       __builtin_amdgcn_sched_barrier(0);
       store_stage(b ^ 1, (sl + 1) % kRing);
+      if (sl == 3) store_group((kb >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
       load_stage(min(kb + kRing, last), sl);
+      if (sl == 0) load_group(min((kb >> 2) + 1, lastg));
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     };
 
-    // Prologue: stages 0 .. kRing-1 in flight, stage 0 in LDS.
+    // Prologue: scale group 0 and stages 0 .. kRing-1 in flight, then group
+    // 0 and stage 0 in LDS.
+    load_group(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int sl = 0; sl < kRing; ++sl) {
       load_stage(min(sl, last), sl);
       __builtin_amdgcn_sched_barrier(0);
     }
+    store_group(0);
     store_stage(0, 0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -312,30 +325,31 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Dense GEMM2, act tile resident in LDS (I <= 384). A block owns a 128-row
-// dense tile: it copies the tile's act rows (128 x I bf16) into LDS once and
-// then walks all H / 256 output spans. Wave (wm, wn) computes 64 W2 rows x
-// 64 tokens per span, its weights coming straight from global memory into
-// registers: K step kb of the next span is loaded into the registers of
-// step kb right after they are decoded, so the loads have about one span
-// of MFMA work to arrive and no barrier is needed between spans.
+// Dense GEMM2, act tile resident in LDS (I <= 384). A block (4 waves) owns a
+// 128-row dense tile: it copies the tile's act rows (128 x I bf16) into LDS
+// once and then walks all H / 256 output spans. Wave wn computes 64 W2 rows
+// x all 128 tokens per span, so every weight byte is fetched once; its
+// weights come straight from global memory into registers, and K step kb
+// of the next span is loaded into the registers of step kb right after they
+// are decoded: the loads have about one span of MFMA work to arrive, and no
+// barrier is needed between spans.
 // ---------------------------------------------------------------------------
+constexpr int kResThreads = 256;
+
 template <int NKB>
-__global__ __launch_bounds__(kTiledThreads, 2) void gemm2_resident_kernel(
+__global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ counters, int H, uint16_t* __restrict__ y) {
   constexpr int I = NKB * 128;
   constexpr int kRowB = I * 2;                 // act row bytes
-  constexpr int kScW = I / 128;                // scale dwords per W2 row
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kTileRows * kRowB];
   const int ntiles = counters[kCtrGate] == 1 ? counters[kCtrGate + 3] : 0;
   const int xcd = blockIdx.x & 7;
   const int per = (ntiles + 7) >> 3;
   const int nblk_x = static_cast<int>(gridDim.x) >> 3;
   const int t = threadIdx.x;
-  const int wave = wave_index();
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wn = wave_index();
   const int lane = lane_id();
   const int r = lane & 31, h = lane >> 5;
   const int nspan = H >> 8;
@@ -354,18 +368,18 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm2_resident_kernel(
     {
       const __amdgpu_buffer_rsrc_t ars = make_rsrc(act, act_bytes);
       constexpr int kChunks = kTileRows * (kRowB / 16);
-      constexpr int kPer = kChunks / kTiledThreads;
+      constexpr int kPer = kChunks / kResThreads;
       uint4 v[kPer];
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int q = i * kTiledThreads + t;
+        const int q = i * kResThreads + t;
         const int rr = q / (kRowB / 16), c = q % (kRowB / 16);
         v[i] = bld16(ars, static_cast<uint32_t>(row0 + rr) * kRowB + c * 16 +
                               (rr < nrows ? 0u : kNoRow));
       }
 #pragma unroll
       for (int i = 0; i < kPer; ++i) {
-        const int q = i * kTiledThreads + t;
+        const int q = i * kResThreads + t;
         const int rr = q / (kRowB / 16), c = q % (kRowB / 16);
         *reinterpret_cast<uint4*>(a_lds + a_off(rr, c)) = v[i];
       }
@@ -391,11 +405,11 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm2_resident_kernel(
     __syncthreads();  // act tile visible to every wave
 
     for (int sp = 0; sp < nspan; ++sp) {
-      f32x16_t acc[2][2];
+      f32x16_t acc[2][4];
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < 4; ++n)
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
       const int spn = min(sp + 1, nspan - 1);  // last span: reload it, unused
@@ -418,32 +432,30 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm2_resident_kernel(
           }
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            bf16x8_t bf[2];
 #pragma unroll
-            for (int n = 0; n < 2; ++n)
-              bf[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                  a_lds + a_off(wm * 64 + n * 32 + r, kb * 16 + 8 * q + 4 * h + j)));
+            for (int n = 0; n < 4; ++n) {
+              const bf16x8_t bf = as_bf16x8(*reinterpret_cast<const uint4*>(
+                  a_lds + a_off(n * 32 + r, kb * 16 + 8 * q + 4 * h + j)));
 #pragma unroll
-            for (int m = 0; m < 2; ++m)
-#pragma unroll
-              for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m][j], bf[n], acc[m][n]);
+              for (int m = 0; m < 2; ++m) acc[m][n] = mfma32x32x16(a[m][j], bf, acc[m][n]);
+            }
           }
         }
       }
-      // ---- this span's 64 x 64 outputs of the wave
+      // ---- this span's 64 x 128 outputs of the wave
       const int fbase = sp * 256 + wn * 64;
       const __amdgpu_buffer_rsrc_t ors =
           make_rsrc(y + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int n = 0; n < 2; ++n)
+        for (int n = 0; n < 4; ++n)
 #pragma unroll
           for (int b4 = 0; b4 < 4; ++b4) {
             uint2 pk;
             pk.x = pack_bf16x2(acc[m][n][4 * b4 + 0], acc[m][n][4 * b4 + 1]);
             pk.y = pack_bf16x2(acc[m][n][4 * b4 + 2], acc[m][n][4 * b4 + 3]);
-            const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * H * 2 +
+            const uint32_t off = static_cast<uint32_t>(n * 32 + r) * H * 2 +
                                  (fbase + 32 * m + 8 * b4 + 4 * h) * 2;
             bst8(ors, off, pk);
           }
@@ -476,7 +488,7 @@ hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
     const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles), 1);
     const uint32_t act_bytes = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2);
 #define MOE_G2R(NK)                                                                        \
-  hipLaunchKernelGGL(gemm2_resident_kernel<NK>, dim3(grid), dim3(kTiledThreads), 0, st,   \
+  hipLaunchKernelGGL(gemm2_resident_kernel<NK>, dim3(grid), dim3(kResThreads), 0, st,     \
                      a.act, act_bytes, a.w2, a.s2, a.dense_tiles, a.counters, a.H, a.y)
     switch (a.I / 128) {
       case 1: MOE_G2R(1); break;
