@@ -48,25 +48,28 @@ __device__ __forceinline__ void wave_copy_to_lds(uint8_t* lds, const uint8_t* sr
     *reinterpret_cast<uint4*>(lds + off) = ld16(src + off);
 }
 
-// acc[t] += W_tile_t (16 x K) * B^T for one sub-tile of token rows.
+// acc[s][t] += W_tile_t (16 x K) * B_s^T for NS sub-tiles of 16 token rows.
 // wp: lane's weight-row pointer of tile 0, offset by g*16 bytes; tile t is
 // wofs[t] bytes further (wave-uniform). ls: lane's scale row in LDS, offset by
-// g; tile t is lofs[t] bytes further. brs/boff: buffer and byte offset of the
-// lane's B row plus g*64 bytes (kNoRow for lanes past the chunk's end).
+// g; tile t is lofs[t] bytes further. brs/boff[s]: buffer and byte offset of
+// the lane's row of sub-tile s plus g*64 bytes (kNoRow for lanes past the
+// chunk's end). Each decoded weight fragment feeds all NS sub-tiles.
 // D divides nkb, so the unrolled body has no tail branches: the
 // vector-memory counter retires loads in issue order, and straight-line code
 // lets every wait cover only the step it needs.
-template <int D>
+template <int D, int NS>
 __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (&wofs)[4],
                                              const uint8_t* ls, const uint32_t (&lofs)[4], int nkb,
-                                             __amdgpu_buffer_rsrc_t brs, uint32_t boff,
-                                             f32x4_t (&acc)[4]) {
-  uint4 w[D][4], xb[D][4];
+                                             __amdgpu_buffer_rsrc_t brs, const uint32_t (&boff)[NS],
+                                             f32x4_t (&acc)[NS][4]) {
+  uint4 w[D][4], xb[D][NS][4];
   // Prologue in slot order (pinned), matching the steady-state issue order.
 #pragma unroll
   for (int d = 0; d < D; ++d) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[d][j] = bld16(brs, boff + d * 256 + j * 16);
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + d * 256 + j * 16);
 #pragma unroll
     for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + d * 64);
     __builtin_amdgcn_sched_barrier(0);
@@ -82,13 +85,18 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
     for (int t = 0; t < 4; ++t) {
       const uint32_t ww[4] = {w[d][t].x, w[d][t].y, w[d][t].z, w[d][t].w};
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[t] = mfma16x16x32(decode_fp4x8(ww[j], sc[t]), as_bf16x8(xb[d][j]), acc[t]);
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t a = decode_fp4x8(ww[j], sc[t]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[s][t] = mfma16x16x32(a, as_bf16x8(xb[d][s][j]), acc[s][t]);
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     const int nk = min(kb + D, last);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xb[d][j] = bld16(brs, boff + nk * 256 + j * 16);
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + nk * 256 + j * 16);
 #pragma unroll
     for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + nk * 64);
     __builtin_amdgcn_sched_barrier(0);
@@ -114,21 +122,24 @@ inline int ring_depth(int nkb) {
   return 1;
 }
 
-// GEMM1 + SwiGLU, decode shape. Item = (16-row unit, 32-feature group):
-// tiles are gate rows f0+[0,16), up rows I+f0+[0,16), gate f0+16+[0,16),
-// up I+f0+16+[0,16). Dynamic LDS: 4 waves x 2H bytes (the group's 32 gate
-// and 32 up scale rows).
-template <int D>
+// GEMM1 + SwiGLU, decode shape. Item = (chunk of at most 16 * NSMAX rows,
+// 32-feature group): tiles are gate rows f0+[0,16), up rows I+f0+[0,16),
+// gate f0+16+[0,16), up I+f0+16+[0,16). A chunk of more than 16 rows runs
+// both 16-row sub-tiles against each weight load, so an expert's weights
+// are streamed once per chunk. Dynamic LDS: 4 waves x 2H bytes (the group's
+// 32 gate and 32 up scale rows). `units`/`ctr`: the chunk table and the
+// counter word holding its length.
+template <int D, int NSMAX>
 __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
-    const uint8_t* __restrict__ s13, const int32_t* __restrict__ units,
+    const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int T, int H,
     int I, int Kp, float limit, uint16_t* __restrict__ act) {
   extern __shared__ uint8_t lds_scales[];
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int groups = I >> 5;
-  const int nitems = counters[kCtrNumU] * groups;
+  const int nitems = counters[ctr] * groups;
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
   const int nkb = H >> 7;
   const int blk = 32 * static_cast<int>(srow);  // 32 scale rows = H bytes
@@ -148,42 +159,62 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     wave_copy_to_lds(my, sg, blk);
     wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
     const uint8_t* wp = w13 + (row0 + r) * wrow + g * 16;
-    const bool valid = r < nrows;
-    const int tok = sorted_slot[r0 + min(r, nrows - 1)] / Kp;
-    const uint32_t boff = valid ? static_cast<uint32_t>(tok) * H * 2 + g * 64 : kNoRow;
-    f32x4_t acc[4];
+    uint32_t boff[NSMAX];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    stream_block<D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, boff, acc);
-    // rows past the unit's end fall outside the buffer: stores dropped
+    for (int s = 0; s < NSMAX; ++s) {
+      const int rr = 16 * s + r;
+      const int tok = sorted_slot[r0 + min(rr, nrows - 1)] / Kp;
+      boff[s] = rr < nrows ? static_cast<uint32_t>(tok) * H * 2 + g * 64 : kNoRow;
+    }
+    // rows past the chunk's end fall outside the buffer: stores dropped
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
-    const uint32_t aoff = static_cast<uint32_t>(r) * I * 2 + (f0 + g * 4) * 2;
+    auto store = [&](const f32x4_t (&acc)[4], int s) {
+      const uint32_t aoff = static_cast<uint32_t>(16 * s + r) * I * 2 + (f0 + g * 4) * 2;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const f32x4_t& ag = acc[2 * h];
-      const f32x4_t& au = acc[2 * h + 1];
-      uint2 pk;
-      pk.x = pack_bf16x2(swiglu(ag[0], au[0], limit), swiglu(ag[1], au[1], limit));
-      pk.y = pack_bf16x2(swiglu(ag[2], au[2], limit), swiglu(ag[3], au[3], limit));
-      bst8(ars, aoff + h * 32, pk);
+      for (int h = 0; h < 2; ++h) {
+        const f32x4_t& ag = acc[2 * h];
+        const f32x4_t& au = acc[2 * h + 1];
+        uint2 pk;
+        pk.x = pack_bf16x2(swiglu(ag[0], au[0], limit), swiglu(ag[1], au[1], limit));
+        pk.y = pack_bf16x2(swiglu(ag[2], au[2], limit), swiglu(ag[3], au[3], limit));
+        bst8(ars, aoff + h * 32, pk);
+      }
+    };
+    if (NSMAX == 1 || nrows <= 16) {
+      f32x4_t acc[1][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint32_t b1[1] = {boff[0]};
+      stream_block<D, 1>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1, acc);
+      store(acc[0], 0);
+    } else {
+      f32x4_t acc[NSMAX][4];
+#pragma unroll
+      for (int s = 0; s < NSMAX; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      stream_block<D, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, boff, acc);
+#pragma unroll
+      for (int s = 0; s < NSMAX; ++s) store(acc[s], s);
     }
   }
 }
 
-// GEMM2 split path, decode shape, long K. Item = (16-row unit, 64 output
-// rows of H). Dynamic LDS: 4 waves x 2I bytes (the 64 rows' scales).
-template <int D>
+// GEMM2 split path, decode shape, long K. Item = (chunk of at most
+// 16 * NSMAX rows, 64 output rows of H). Dynamic LDS: 4 waves x 2I bytes
+// (the 64 rows' scales).
+template <int D, int NSMAX>
 __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2,
-    const uint8_t* __restrict__ s2, const int32_t* __restrict__ units,
+    const uint8_t* __restrict__ s2, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, int H, int I, uint16_t* __restrict__ y) {
   if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
   extern __shared__ uint8_t lds_scales[];
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int quads = H >> 6;
-  const int nitems = counters[kCtrNumU] * quads;
+  const int nitems = counters[ctr] * quads;
   const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
   const int nkb = I >> 7;
   const int blk = 64 * static_cast<int>(srow);  // = 2I bytes
@@ -200,23 +231,40 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     const size_t row0 = static_cast<size_t>(e) * H + h0;
     wave_copy_to_lds(my, s2 + row0 * srow, blk);
     const uint8_t* wp = w2 + (row0 + r) * wrow + g * 16;
-    // unit-relative buffers: rows past the unit's end read 0 / drop stores
+    // chunk-relative buffers: rows past the chunk's end read 0 / drop stores
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
     const __amdgpu_buffer_rsrc_t yrs =
         make_rsrc(y + static_cast<size_t>(r0) * H, static_cast<uint32_t>(nrows) * H * 2);
-    const uint32_t boff = static_cast<uint32_t>(r) * I * 2 + g * 64;
-    f32x4_t acc[4];
+    uint32_t boff[NSMAX];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    stream_block<D>(wp, wofs, my + r * srow + g, lofs, nkb, ars, boff, acc);
-    const uint32_t yoff = static_cast<uint32_t>(r) * H * 2 + (h0 + g * 4) * 2;
+    for (int s = 0; s < NSMAX; ++s) boff[s] = static_cast<uint32_t>(16 * s + r) * I * 2 + g * 64;
+    auto store = [&](const f32x4_t (&acc)[4], int s) {
+      const uint32_t yoff = static_cast<uint32_t>(16 * s + r) * H * 2 + (h0 + g * 4) * 2;
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      uint2 pk;
-      pk.x = pack_bf16x2(acc[t][0], acc[t][1]);
-      pk.y = pack_bf16x2(acc[t][2], acc[t][3]);
-      bst8(yrs, yoff + t * 32, pk);
+      for (int t = 0; t < 4; ++t) {
+        uint2 pk;
+        pk.x = pack_bf16x2(acc[t][0], acc[t][1]);
+        pk.y = pack_bf16x2(acc[t][2], acc[t][3]);
+        bst8(yrs, yoff + t * 32, pk);
+      }
+    };
+    if (NSMAX == 1 || nrows <= 16) {
+      f32x4_t acc[1][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const uint32_t b1[1] = {boff[0]};
+      stream_block<D, 1>(wp, wofs, my + r * srow + g, lofs, nkb, ars, b1, acc);
+      store(acc[0], 0);
+    } else {
+      f32x4_t acc[NSMAX][4];
+#pragma unroll
+      for (int s = 0; s < NSMAX; ++s)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      stream_block<D, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, ars, boff, acc);
+#pragma unroll
+      for (int s = 0; s < NSMAX; ++s) store(acc[s], s);
     }
   }
 }
@@ -548,17 +596,22 @@ static int grid_for(long items) {
 hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
   if (a.a8) return a.B <= 32 ? launch_gemm1_a8(a, st) : launch_gemm1_tiled_a8(a, st);
   if (a.B <= 32) {
-    const int grid = grid_for(static_cast<long>(a.max_units16) * (a.I / 32));
+    // B = 32: the 32-row chunk table (chunks of more than 16 rows run both
+    // sub-tiles per weight load); B = 16: the 16-row units
+    const bool c32 = a.B == 32;
+    const int32_t* units = c32 ? a.vinfo : a.units16;
+    const int ctr = c32 ? kCtrNumV : kCtrNumU;
+    const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / 32));
     const size_t lds = static_cast<size_t>(4) * 2 * a.H;
-#define MOE_G1D(DD)                                                                               \
-  hipLaunchKernelGGL(gemm1_decode_kernel<DD>, dim3(grid), dim3(kGemmBlock), lds, st, a.x, a.w13,   \
-                     a.s13, a.units16, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp, a.limit,     \
-                     a.act)
-    switch (ring_depth(a.H / 128)) {
-      case 4: MOE_G1D(4); break;
-      case 3: MOE_G1D(3); break;
-      case 2: MOE_G1D(2); break;
-      default: MOE_G1D(1); break;
+#define MOE_G1D(DD, NS)                                                                           \
+  hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS>), dim3(grid), dim3(kGemmBlock), lds, st, a.x,    \
+                     a.w13, a.s13, units, ctr, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp,       \
+                     a.limit, a.act)
+    const int d = ring_depth(a.H / 128);
+    if (c32) {
+      if (d == 2) MOE_G1D(2, 2); else MOE_G1D(1, 2);
+    } else {
+      if (d == 2) MOE_G1D(2, 1); else MOE_G1D(1, 1);
     }
 #undef MOE_G1D
     return hipGetLastError();
@@ -582,16 +635,19 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
     }
 #undef MOE_G2S
   } else {
-    const int gsplit = grid_for(static_cast<long>(a.max_units16) * (a.H / 64));
+    const bool c32 = a.B == 32;
+    const int32_t* units = c32 ? a.vinfo : a.units16;
+    const int ctr = c32 ? kCtrNumV : kCtrNumU;
+    const int gsplit = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.H / 64));
     const size_t lds2 = static_cast<size_t>(4) * 2 * a.I;
-#define MOE_G2D(DD)                                                                           \
-  hipLaunchKernelGGL(gemm2_split_kernel<DD>, dim3(gsplit), dim3(kGemmBlock), lds2, st, a.act, \
-                     a.w2, a.s2, a.units16, a.counters, a.H, a.I, a.y)
-    switch (ring_depth(a.I / 128)) {
-      case 4: MOE_G2D(4); break;
-      case 3: MOE_G2D(3); break;
-      case 2: MOE_G2D(2); break;
-      default: MOE_G2D(1); break;
+#define MOE_G2D(DD, NS)                                                                         \
+  hipLaunchKernelGGL((gemm2_split_kernel<DD, NS>), dim3(gsplit), dim3(kGemmBlock), lds2, st,   \
+                     a.act, a.w2, a.s2, units, ctr, a.counters, a.H, a.I, a.y)
+    const int d = ring_depth(a.I / 128);
+    if (c32) {
+      if (d == 2) MOE_G2D(2, 2); else MOE_G2D(1, 2);
+    } else {
+      if (d == 2) MOE_G2D(2, 1); else MOE_G2D(1, 1);
     }
 #undef MOE_G2D
   }
