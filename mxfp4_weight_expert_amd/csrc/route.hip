@@ -37,11 +37,30 @@ __device__ __forceinline__ void write_shared_columns(const uint16_t* shared_logi
   }
 }
 
+// Wave-wide maximum of a 32-bit value (DPP row shifts and row broadcasts;
+// lane 63 ends with the maximum, which every lane receives).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  auto step = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x111, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x112, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x114, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x118, 0xf, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x142, 0xa, 0xf, false)));
+  v = step(v, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), 0x143, 0xc, 0xf, false)));
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(v), 63));
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a < b ? a : b; }
+
 // One wave per token. The token's logits become 64-bit keys (ordered logit
-// << 32 | ~id), NPL per lane (E_global <= 64 * NPL). Each of topk rounds takes
-// the wave-wide maximum key (DPP reduction) and removes it from its lane, so
-// keys come out in descending order: larger logit first, equal logits lower
-// id first.
+// << 32 | ~id), NPL per lane (E_global <= 64 * NPL); larger key = larger
+// logit, equal logits: lower id. Every lane keeps its four largest keys
+// below a ceiling, sorted. Each of topk rounds finds the wave's largest head
+// key (a 32-bit DPP maximum over the ordered logits, and over the ids only
+// when several lanes tie) and pops it from its lane; a lane whose list runs
+// empty rebuilds it from its keys below the key it gave last. Keys come out
+// in descending order.
 template <int NPL>
 __global__ __launch_bounds__(256) void route_logits_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ shared_logits, int T, int Eg,
@@ -59,24 +78,46 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
 #pragma unroll
   for (int j = 0; j < NPL; ++j) {
     const int idx = lane + kWave * j;
-    key[j] = idx < Eg ? ((static_cast<uint64_t>(order_bits(lv[j])) << 32) |
-                         static_cast<uint32_t>(~idx))
-                      : 0ull;
+    const uint64_t k = (static_cast<uint64_t>(order_bits(lv[j])) << 32) | static_cast<uint32_t>(~idx);
+    key[j] = idx < Eg ? k : 0ull;  // 0 is below every real key
   }
-  uint64_t lmax = 0;
+  // the lane's four largest keys below `ceil`, descending (0 = none)
+  uint64_t L[4];
+  auto build = [&](uint64_t ceil) {
 #pragma unroll
-  for (int j = 0; j < NPL; ++j) lmax = key[j] > lmax ? key[j] : lmax;
+    for (int i = 0; i < 4; ++i) L[i] = 0ull;
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      uint64_t x = key[j] < ceil ? key[j] : 0ull;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint64_t hi = max_u64(L[i], x);
+        x = min_u64(L[i], x);
+        L[i] = hi;
+      }
+    }
+  };
+  build(~0ull);
   uint64_t mine = 0;  // lane r keeps the r-th selected key
   for (int r = 0; r < topk; ++r) {
-    const uint64_t m = wave_max_u64_dpp(lmax);
+    const uint32_t h0 = static_cast<uint32_t>(L[0] >> 32), l0 = static_cast<uint32_t>(L[0]);
+    const uint32_t mh = wave_max_u32(h0);
+    const bool cand = h0 == mh;
+    const uint64_t bal = ballot(cand);
+    uint32_t ml;
+    if (__popcll(bal) == 1) {
+      ml = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(l0), __builtin_ctzll(bal)));
+    } else {
+      ml = wave_max_u32(cand ? l0 : 0u);
+    }
+    const uint64_t m = (static_cast<uint64_t>(mh) << 32) | ml;
     if (lane == r) mine = m;
-    if (lmax == m) {  // the one lane holding the winner (keys are distinct)
-      lmax = 0;
-#pragma unroll
-      for (int j = 0; j < NPL; ++j) {
-        key[j] = key[j] == m ? 0ull : key[j];
-        lmax = key[j] > lmax ? key[j] : lmax;
-      }
+    if (L[0] == m) {  // the one lane holding the winner (keys are distinct)
+      L[0] = L[1];
+      L[1] = L[2];
+      L[2] = L[3];
+      L[3] = 0ull;
+      if (L[0] == 0ull) build(m);
     }
   }
   const bool sel = lane < topk;

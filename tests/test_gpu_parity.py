@@ -179,3 +179,22 @@ def test_w4a8_config_parity(name):
     check_out(out_np(out)[toks], want, f"{s.name} sampled tokens {len(toks)}")
     del out, ws
     torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------ routing edge cases
+@pytest.mark.parametrize("E_g,topk", [(8, 2), (130, 5), (896, 16), (2048, 32)])
+def test_routing_ties_and_signed_zeros(E_g, topk):
+    """Top-k ids bit-exact under heavy ties (equal logits rank by lower id)
+    and with -0.0 and +0.0 logits comparing equal. At most 16 experts are
+    local, so most routed slots map to -1 and the GEMMs stay small."""
+    s = LayerShape(f"ties_{E_g}", T=96, E=min(16, E_g), E_g=E_g, topk=topk, H=512, I=128, B=16)
+    inp = make_inputs(s, 900 + E_g)
+    rng = np.random.default_rng(E_g)
+    lg = rng.integers(-2, 3, size=(s.T, E_g)).astype(np.float32)  # five distinct values
+    lg[0::3] = 0.0
+    lg[0::3, ::2] = -0.0                       # rows of signed zeros only
+    lg[1::3, :topk // 2 + 1] = np.float32(7.5)  # a tie straddling the top-k boundary
+    inp["logits"] = lg
+    ref = oracle.reference_forward(s, inp, compute_out=False)
+    out, ws = run(s, to_device(s, inp))
+    check_maps(s, maps_np(s, ws), ref)
