@@ -122,7 +122,8 @@ typedef struct moe_mxfp4_shape {
  *   route_ids     int32[T*topk]   selected global ids (logits mode)
  *   slot_expert   int32[T*K']     local expert of slot t*K'+k, or -1
  *   slot_w        float[T*K']     routing weight of the slot
- *   range_counts  int32[n_ranges*E'] per-slot-range expert counts, then bases
+ *   range_counts  int32[n_ranges*E'] per-slot-range expert counts, then
+ *                 each range's first row within the expert (large sorts only)
  *   counts        int32[E']       rows per expert
  *   offsets       int32[E'+1]     first row of each expert; offsets[E'] = R
  *   sorted_slot   int32[R_max]    row -> slot
@@ -159,7 +160,7 @@ typedef struct moe_mxfp4_ws_layout {
   int32_t kmax_v;          /* E' + (T*K') / B: bound on chunks */
   int32_t max_dense_tiles; /* E' + (T*K') / 128 */
   int32_t max_units16;     /* E' + (T*K') / 16 */
-  int32_t n_ranges;        /* slot ranges of the sort */
+  int32_t n_ranges;        /* slot ranges of the large sort */
   int32_t rows_pad;        /* R_max plus padding rows */
 } moe_mxfp4_ws_layout;
 

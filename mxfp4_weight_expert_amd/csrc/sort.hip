@@ -14,9 +14,9 @@
 // chunk table, placement, gate). Beyond that the slots t*K' + k are cut into
 // ranges of kRangeSlots, one wave each:
 //   count:   per-range expert histograms (LDS atomics: order-free counts);
-//   scan:    per-expert exclusive scan over ranges, expert offsets, chunks;
-//   scatter: each wave walks its range in slot order, 64 slots at a time;
-//   gate:    one wave.
+//   scan:    per-expert exclusive scan over ranges, expert offsets, chunks,
+//            and the gate (one block);
+//   scatter: each wave walks its range in slot order, 64 slots at a time.
 // Placement ranks equal experts inside a wave by ballot/popcount (a wave
 // multisplit), so rows follow slot order exactly.
 #include "common.h"
@@ -92,48 +92,62 @@ __device__ void block_scan_experts(const int32_t* s_cnt, int Ep, int B, int32_t*
   }
 }
 
-// One wave: rows R and touched experts U from the counts; Dense iff
-// R >= kGateTau * U (or forced). On Dense it writes the per-expert 128-row
-// tile list. Gate word: {path, U, R, dense tiles (0 on Split)}.
-__device__ void gate_wave(const int32_t* counts, const int32_t* offsets, int Ep, int force_path,
-                          int32_t* counters, int32_t* dense_tiles) {
-  const int lane = lane_id();
-  int U = 0, R = 0;
-  for (int e = lane; e < Ep; e += kWave) {
-    const int n = counts[e];
+// Whole block (1024 threads): rows R and touched experts U from the counts
+// (LDS); Dense iff R >= kGateTau * U (or forced). On Dense it writes the
+// per-expert 128-row tile list, experts in order. Gate word: {path, U, R,
+// dense tiles (0 on Split)}. Every thread of the block must call it.
+__device__ void block_gate(const int32_t* s_cnt, const int32_t* s_off, int Ep, int force_path,
+                           int32_t* counters, int32_t* dense_tiles) {
+  __shared__ int32_t s_u[16], s_r[16], s_t[16];
+  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
+  const int per = (Ep + 1023) / 1024;
+  const int e0 = tid * per;
+  int U = 0, R = 0, nt = 0;
+  for (int i = 0; i < per; ++i) {
+    const int e = e0 + i;
+    const int n = e < Ep ? s_cnt[e] : 0;
     U += n > 0;
     R += n;
+    nt += (n + kDenseMT - 1) / kDenseMT;
   }
-  U = wave_sum(U);
-  R = wave_sum(R);
-  int path = (U > 0 && R >= kGateTau * U) ? 1 : 0;
+  const int uw = wave_sum(U), rw = wave_sum(R), tin = wave_incl_scan(nt);
+  if (lane == kWave - 1) {
+    s_u[w] = uw;
+    s_r[w] = rw;
+    s_t[w] = tin;
+  }
+  __syncthreads();
+  int Ut = 0, Rt = 0, tbase = 0, ttot = 0;
+  for (int j = 0; j < 16; ++j) {
+    Ut += s_u[j];
+    Rt += s_r[j];
+    tbase += j < w ? s_t[j] : 0;
+    ttot += s_t[j];
+  }
+  int path = (Ut > 0 && Rt >= kGateTau * Ut) ? 1 : 0;
   if (force_path == 0 || force_path == 1) path = force_path;
-  int ntiles = 0;
   if (path == 1) {
-    for (int c = 0; c < Ep; c += kWave) {
-      const int e = c + lane;
-      const int n = e < Ep ? counts[e] : 0;
-      const int nt = (n + kDenseMT - 1) / kDenseMT;
-      const int incl = wave_incl_scan(nt);
-      const int first = ntiles + incl - nt;
-      const int off = e < Ep ? offsets[e] : 0;
-      for (int m = 0; m < nt; ++m) {
+    int tile = tbase + tin - nt;
+    for (int i = 0; i < per; ++i) {
+      const int e = e0 + i;
+      if (e >= Ep) break;
+      const int n = s_cnt[e];
+      for (int m = 0; m * kDenseMT < n; ++m) {
         int4 v;
         v.x = e;
-        v.y = off + m * kDenseMT;
+        v.y = s_off[e] + m * kDenseMT;
         v.z = min(kDenseMT, n - m * kDenseMT);
         v.w = m;
-        reinterpret_cast<int4*>(dense_tiles)[first + m] = v;
+        reinterpret_cast<int4*>(dense_tiles)[tile++] = v;
       }
-      ntiles += __shfl(incl, kWave - 1, kWave);
     }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     int4 g;
     g.x = path;
-    g.y = U;
-    g.z = R;
-    g.w = ntiles;
+    g.y = Ut;
+    g.z = Rt;
+    g.w = path == 1 ? ttot : 0;
     *reinterpret_cast<int4*>(counters + kCtrGate) = g;
   }
 }
@@ -189,8 +203,8 @@ constexpr int kSmallGroups = kSmallSlots / (kSmallWaves * kWave);  // 64-slot gr
 // 64): it counts its experts into its own 16-bit histogram (the first lane of
 // each equal-expert group adds the group size: no atomics), the block scans
 // the histograms per expert (wave bases) and over experts (offsets, chunk
-// table), then each wave places its own slots in slot order. Wave 0 then runs
-// the GEMM2 gate. Dynamic LDS: kSmallWaves * Ep 16-bit counters.
+// table), then each wave places its own slots in slot order, and the block
+// runs the GEMM2 gate. Dynamic LDS: kSmallWaves * Ep 16-bit counters.
 __global__ __launch_bounds__(1024) void sort_small_kernel(
     const int32_t* __restrict__ slot_expert, int nslots, int Ep, int B, int key_bits,
     int force_path, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -263,95 +277,96 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(
       __builtin_amdgcn_wave_barrier();
     }
   }
-  if (w == 0) gate_wave(s_cnt, s_off, Ep, force_path, counters, dense_tiles);
+  block_gate(s_cnt, s_off, Ep, force_path, counters, dense_tiles);
 }
 
 // ------------------------------------------------------------ large shapes
-__global__ __launch_bounds__(256) void sort_count_kernel(const int32_t* __restrict__ slot_expert,
-                                                         int nslots, int Ep, int n_ranges,
-                                                         int32_t* __restrict__ range_counts) {
+// One wave per block (ranges spread over the CUs): range r's expert
+// histogram in LDS, written range-major to range_counts[r][Ep].
+__global__ __launch_bounds__(64) void sort_count_kernel(const int32_t* __restrict__ slot_expert,
+                                                        int nslots, int Ep, int n_ranges,
+                                                        int32_t* __restrict__ range_counts) {
   extern __shared__ int32_t lds[];
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  const int r = blockIdx.x * 4 + w;
-  int32_t* h = lds + w * Ep;
+  const int lane = lane_id();
+  const int r = blockIdx.x;
+  int32_t* h = lds;
   for (int i = lane; i < Ep; i += kWave) h[i] = 0;
-  __syncthreads();
-  if (r < n_ranges) {
-    const int s0 = r * kRangeSlots;
-    const int s1 = min(nslots, s0 + kRangeSlots);
-    for (int s = s0 + lane; s < s1; s += kWave) {
-      const int e = slot_expert[s];
-      if (e >= 0) atomicAdd(&h[e], 1);
-    }
+  __builtin_amdgcn_wave_barrier();
+  const int s0 = r * kRangeSlots;
+  const int s1 = min(nslots, s0 + kRangeSlots);
+  for (int s = s0 + lane; s < s1; s += kWave) {
+    const int e = slot_expert[s];
+    if (e >= 0) atomicAdd(&h[e], 1);
   }
-  __syncthreads();
-  if (r < n_ranges)
-    for (int i = lane; i < Ep; i += kWave) range_counts[static_cast<size_t>(r) * Ep + i] = h[i];
+  __builtin_amdgcn_wave_barrier();
+  for (int i = lane; i < Ep; i += kWave) range_counts[static_cast<size_t>(r) * Ep + i] = h[i];
 }
 
-// One block of 1024 threads. Turns range_counts into per-range bases, writes
-// counts, offsets, the chunk table and the chunk count.
+// One block of 1024 threads. Turns range_counts ([n_ranges][Ep]) into
+// per-range bases, writes counts, offsets, the chunk table and the chunk
+// count, then runs the GEMM2 gate.
 __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ range_counts,
-                                                         int n_ranges, int Ep, int B,
+                                                         int n_ranges, int Ep, int B, int force_path,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ vinfo,
                                                          int32_t* __restrict__ units16,
-                                                         int32_t* __restrict__ counters) {
+                                                         int32_t* __restrict__ counters,
+                                                         int32_t* __restrict__ dense_tiles) {
   __shared__ int32_t s_cnt[kMaxExperts];
+  __shared__ int32_t s_off[kMaxExperts];
   const int tid = threadIdx.x;
-  // 1) per expert: exclusive scan over ranges, in place.
+  // 1) per expert: exclusive scan over the ranges, in place; neighbouring
+  // threads read neighbouring experts (coalesced), 32 ranges per round with
+  // the round's loads in flight together
   for (int e = tid; e < Ep; e += 1024) {
     int run = 0;
-    int r = 0;
-    for (; r + 8 <= n_ranges; r += 8) {
-      int c[8];
+    for (int r0 = 0; r0 < n_ranges; r0 += 32) {
+      int c[32];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) c[j] = range_counts[static_cast<size_t>(r + j) * Ep + e];
+      for (int j = 0; j < 32; ++j) c[j] = range_counts[static_cast<size_t>(min(r0 + j, n_ranges - 1)) * Ep + e];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        range_counts[static_cast<size_t>(r + j) * Ep + e] = run;
-        run += c[j];
+      for (int j = 0; j < 32; ++j) {
+        if (r0 + j < n_ranges) {
+          range_counts[static_cast<size_t>(r0 + j) * Ep + e] = run;
+          run += c[j];
+        }
       }
-    }
-    for (; r < n_ranges; ++r) {
-      const int c = range_counts[static_cast<size_t>(r) * Ep + e];
-      range_counts[static_cast<size_t>(r) * Ep + e] = run;
-      run += c;
     }
     s_cnt[e] = run;
   }
   __syncthreads();
-  // 2) expert offsets and the chunk table
-  block_scan_experts(s_cnt, Ep, B, counts, offsets, vinfo, units16, counters, nullptr);
+  // 2) expert offsets and the chunk table, then the gate
+  block_scan_experts(s_cnt, Ep, B, counts, offsets, vinfo, units16, counters, s_off);
+  __syncthreads();
+  block_gate(s_cnt, s_off, Ep, force_path, counters, dense_tiles);
 }
 
-__global__ __launch_bounds__(256) void sort_scatter_kernel(
+__global__ __launch_bounds__(64) void sort_scatter_kernel(
     const int32_t* __restrict__ slot_expert, int nslots, int Ep, int n_ranges, int key_bits,
     const int32_t* __restrict__ range_base, const int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_slot, int32_t* __restrict__ expanded_idx) {
+  constexpr int kGroups = kRangeSlots / kWave;
   extern __shared__ int32_t lds[];
-  const int w = threadIdx.x >> 6, lane = lane_id();
-  const int r = blockIdx.x * 4 + w;
-  if (r >= n_ranges) return;  // wave-uniform; no block barrier below
-  int32_t* next = lds + w * Ep;  // next free row per expert for this range
-  for (int i = lane; i < Ep; i += kWave)
-    next[i] = offsets[i] + range_base[static_cast<size_t>(r) * Ep + i];
+  const int lane = lane_id();
+  const int r = blockIdx.x;
   const int s0 = r * kRangeSlots;
   const int s1 = min(nslots, s0 + kRangeSlots);
-  for (int c = s0; c < s1; c += kWave) {
-    const int s = c + lane;
+  // the range's experts, all loads in flight at once (clamped index)
+  int ex[kGroups];
+#pragma unroll
+  for (int gi = 0; gi < kGroups; ++gi) ex[gi] = slot_expert[min(s0 + gi * kWave + lane, nslots - 1)];
+  int32_t* next = lds;  // next free row per expert for this range
+  for (int i = lane; i < Ep; i += kWave)
+    next[i] = offsets[i] + range_base[static_cast<size_t>(r) * Ep + i];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int gi = 0; gi < kGroups; ++gi) {
+    const int s = s0 + gi * kWave + lane;
     const bool in = s < s1;
-    place_slots(s, in, in ? slot_expert[s] : -1, key_bits, Ep, next, sorted_slot, expanded_idx);
+    if (s0 + gi * kWave < s1)  // wave-uniform
+      place_slots(s, in, in ? ex[gi] : -1, key_bits, Ep, next, sorted_slot, expanded_idx);
   }
-}
-
-__global__ __launch_bounds__(64) void gemm2_gate_kernel(const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ offsets,
-                                                        int Ep, int force_path,
-                                                        int32_t* __restrict__ counters,
-                                                        int32_t* __restrict__ dense_tiles) {
-  gate_wave(counts, offsets, Ep, force_path, counters, dense_tiles);
 }
 
 hipError_t launch_sort_and_gate(const SortArgs& a, hipStream_t st) {
@@ -364,23 +379,19 @@ hipError_t launch_sort_and_gate(const SortArgs& a, hipStream_t st) {
                        a.expanded_idx, a.vinfo, a.units16, a.counters, a.dense_tiles);
     return hipGetLastError();
   }
-  const int blocks = (a.n_ranges + 3) / 4;
-  const size_t lds = static_cast<size_t>(4) * a.Ep * sizeof(int32_t);
-  hipLaunchKernelGGL(sort_count_kernel, dim3(blocks), dim3(256), lds, st, a.slot_expert, a.nslots,
+  const size_t lds = static_cast<size_t>(a.Ep) * sizeof(int32_t);
+  hipLaunchKernelGGL(sort_count_kernel, dim3(a.n_ranges), dim3(64), lds, st, a.slot_expert, a.nslots,
                      a.Ep, a.n_ranges, a.range_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, st, a.range_counts, a.n_ranges,
-                     a.Ep, a.B, a.counts, a.offsets, a.vinfo, a.units16, a.counters);
+                     a.Ep, a.B, a.force_path, a.counts, a.offsets, a.vinfo, a.units16, a.counters,
+                     a.dense_tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(sort_scatter_kernel, dim3(blocks), dim3(256), lds, st, a.slot_expert,
+  hipLaunchKernelGGL(sort_scatter_kernel, dim3(a.n_ranges), dim3(64), lds, st, a.slot_expert,
                      a.nslots, a.Ep, a.n_ranges, key_bits, a.range_counts, a.offsets,
                      a.sorted_slot, a.expanded_idx);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gemm2_gate_kernel, dim3(1), dim3(64), 0, st, a.counts, a.offsets, a.Ep,
-                     a.force_path, a.counters, a.dense_tiles);
   return hipGetLastError();
 }
 

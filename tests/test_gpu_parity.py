@@ -198,3 +198,22 @@ def test_routing_ties_and_signed_zeros(E_g, topk):
     ref = oracle.reference_forward(s, inp, compute_out=False)
     out, ws = run(s, to_device(s, inp))
     check_maps(s, maps_np(s, ws), ref)
+
+
+# Slot counts above the single-block sort (8192 slots): the multi-kernel sort
+# (per-range counts, scan + gate, scatter), with a ragged last range, a range
+# count that is not a multiple of 4, and skewed routing.
+@pytest.mark.parametrize("s", [
+    LayerShape("sort_ragged", T=3001, E=40, E_g=48, topk=4, H=512, I=128, B=64, expert_offset=4),
+    LayerShape("sort_zipf", T=2500, E=96, E_g=96, topk=8, H=512, I=128, B=128, routing="zipf"),
+    LayerShape("sort_many", T=4097, E=300, E_g=300, topk=6, H=512, I=128, B=32, S=1),
+], ids=lambda s: s.name)
+def test_large_sort_maps(s):
+    say(f"[large sort] {s.name}: {s.T * s.Kp} slots")
+    inp = make_inputs(s, 321)
+    for force in ("auto", "split", "dense"):
+        ref = oracle.reference_forward(s, inp, force_path=FORCES[force], compute_out=False)
+        out, ws = run(s, to_device(s, inp), force)
+        check_maps(s, maps_np(s, ws, force), ref)
+        toks = _sample_tokens(s.T, 4, 5)
+        check_out(out_np(out)[toks], oracle.sampled_forward(s, inp, toks), f"{s.name}/{force}")
