@@ -43,8 +43,6 @@ constexpr int kTiledThreads = 512;
 constexpr int kTokStage = kTileRows * 128 * 2;     // bf16 token bytes of one K stage (32 KB)
 constexpr int kTok8Stage = kTileRows * 128;        // E4M3 token bytes of one K stage (16 KB)
 constexpr int kWStage = kTileWRows * 64;           // packed weight bytes of one K stage (16 KB)
-constexpr int kScGroup = kTileWRows * 16;          // weight scale bytes of four K stages
-constexpr int kRing = 4;                           // stages of global loads in flight
 
 __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -63,29 +61,45 @@ __device__ __forceinline__ uint32_t tok_off(int r, int c) {
 __device__ __forceinline__ uint32_t tok8_off(int r, int c) {
   return static_cast<uint32_t>(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
 }
-// Byte offset of 16-byte chunk c (0..3) of weight row rho in a stage:
-// chunk-major, so the 32 rows of one MFMA fragment are a permutation of 32
-// consecutive 16-byte slots (conflict-free reads); the XOR with 4c spreads
-// the four chunks of a row, written by four neighbouring lanes, over
-// distinct bank groups.
-__device__ __forceinline__ uint32_t w_off(int rho, int c) {
-  return static_cast<uint32_t>(c * (kTileWRows * 16) + ((rho ^ (c << 2)) << 4));
+// Byte offset of 16-byte chunk c (0..3) of weight row rho in a stage of
+// ROWS rows: chunk-major, so the 32 rows of one MFMA fragment are a
+// permutation of 32 consecutive 16-byte slots (conflict-free reads); the XOR
+// with 4c spreads the four chunks of a row, written by four neighbouring
+// lanes, over distinct bank groups.
+template <int ROWS>
+__device__ __forceinline__ uint32_t c_off(int rho, int c) {
+  return static_cast<uint32_t>(c * (ROWS * 16) + ((rho ^ (c << 2)) << 4));
 }
+__device__ __forceinline__ uint32_t w_off(int rho, int c) { return c_off<kTileWRows>(rho, c); }
 
 }  // namespace
 
-// LDS: two stages of tokens, packed weights and weight scales (98 KB). The
-// stage copy goes global -> registers -> LDS with kRing stages of loads in
-// flight, so every load has two full stages of MFMA work to arrive.
-template <bool G1>
+// LDS: two stages of tokens, packed weights and weight scales (98 KB for
+// MB = 2, 124 KB for MB = 3). The stage copy goes global -> registers -> LDS
+// with RING stages of loads in flight.
+//
+// MB is the number of 32-row weight blocks per wave: the block tile has
+// 128 * MB weight rows. For GEMM1 each 32-row block holds the gate rows
+// (rows 0..15) and the up rows (16..31) of 16 consecutive features, so that
+// a SwiGLU pair meets in one lane (accumulator registers 4b + i and
+// 4(b + 2) + i); a tile spans 64 * MB features. For GEMM2 the block's rows
+// are 128 * MB consecutive output features.
+template <bool G1, int MB>
 __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     const uint16_t* __restrict__ src, uint32_t src_bytes, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ s, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int I, int H,
     int Kp, int sub, float limit, uint16_t* __restrict__ dst) {
+  constexpr int kWR = 128 * MB;               // weight rows per tile
+  constexpr int kRingN = MB == 2 ? 4 : 3;     // stages of loads in flight = stages per scale group
+  constexpr int kWSt = kWR * 64;              // packed weight bytes of one K stage
+  constexpr int kScG = kWR * 16;              // one 16-byte scale slot per weight row
+  constexpr int kWPer = kWR * 4 / kTiledThreads;  // weight chunks per thread and stage
+  constexpr int kScPer = (kWR + kTiledThreads - 1) / kTiledThreads;
+  static_assert(kWR * 4 % kTiledThreads == 0, "weight chunks must split evenly");
   __shared__ __attribute__((aligned(16))) uint8_t tok_lds[2 * kTokStage];
-  __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kWStage];
-  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2 * kScGroup];
+  __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kWSt];
+  __shared__ __attribute__((aligned(16))) uint8_t sc_lds[2 * kScG];
   const int K = G1 ? H : I;
   int ntiles;
   if (G1) {
@@ -93,7 +107,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
   } else {
     ntiles = counters[kCtrGate] == 1 ? counters[kCtrGate + 3] : 0;
   }
-  const int nspan = G1 ? (I >> 7) : (H >> 8);  // 256-weight-row spans per tile
+  const int nspan = G1 ? I / (64 * MB) : H / kWR;  // weight-row spans per token tile
   const int nitems = ntiles * sub * nspan;
   const int xcd = blockIdx.x & 7;
   const int per = (nitems + 7) >> 3;
@@ -105,9 +119,9 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
   const int lane = lane_id();
   const int r = lane & 31, h = lane >> 5;
   // thread roles in the stage copy: token chunk t%16 of rows 32i + t/16;
-  // weight chunk t%4 of tile rows 128i + t/4; the 16 scale bytes (four
-  // stages) of tile row t%256 (threads t and t + 256 store the same bytes)
-  const int lc = t & 15, lr = t >> 4, wc = t & 3, wr = t >> 2, sr = t & 255;
+  // weight chunk t%4 of tile rows 128i + t/4; the scale slot of tile rows
+  // (t + 512i) mod kWR (threads that meet a row twice store the same bytes)
+  const int lc = t & 15, lr = t >> 4, wc = t & 3, wr = t >> 2;
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
     const int item = xcd * per + slot;
     if (item >= nitems) break;
@@ -120,12 +134,14 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     const int row0 = ti.y + st * kTileRows;
     const int nrows = min(kTileRows, ti.z - st * kTileRows);
     if (nrows <= 0) continue;
-    // Tile row rho of the weights: GEMM1 rows [0, 128) are the gate rows of
-    // features f0 + rho, rows [128, 256) the up rows of the same features;
-    // as a row of expert e's block.
-    const int f0 = G1 ? span * 128 : span * 256;
+    const int f0 = G1 ? span * 64 * MB : span * kWR;
+    // Row of expert e's weight block that tile row rho stands for.
     auto erow_of = [&](int rho) -> uint32_t {
-      if (G1) return static_cast<uint32_t>(rho < 128 ? f0 + rho : I + f0 + rho - 128);
+      if (G1) {
+        const int rr = rho & 31;
+        const int feat = f0 + 16 * (rho >> 5) + (rr & 15);
+        return static_cast<uint32_t>(rr < 16 ? feat : I + feat);
+      }
       return static_cast<uint32_t>(f0 + rho);
     };
 
@@ -161,109 +177,126 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
         make_rsrc(w + static_cast<size_t>(e) * erows * wrow, static_cast<uint32_t>(erows * wrow));
     const __amdgpu_buffer_rsrc_t scs =
         make_rsrc(s + static_cast<size_t>(e) * erows * srow, static_cast<uint32_t>(erows * srow));
-    uint32_t woff[2];
+    // tile rows 128i + wr stand for expert rows erow_of(wr) + wstep * i
+    const uint32_t woff = erow_of(wr) * static_cast<uint32_t>(wrow) + wc * 16;
+    const uint32_t wstep = (G1 ? 64u : 128u) * static_cast<uint32_t>(wrow);
+    uint32_t soff[kScPer];
+    int srho[kScPer];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) woff[i] = erow_of(i * 128 + wr) * static_cast<uint32_t>(wrow) + wc * 16;
-    const uint32_t soff = erow_of(sr) * static_cast<uint32_t>(srow);
+    for (int i = 0; i < kScPer; ++i) {
+      srho[i] = (i * kTiledThreads + t) % kWR;
+      soff[i] = erow_of(srho[i]) * static_cast<uint32_t>(srow);
+    }
 
     const int nkb = K >> 7;
     const int last = nkb - 1;
-    const int lastg = last >> 2;
-    uint4 tv[kRing][4], wv[kRing][2];
-    uint4 sg;  // scale bytes of the next group of four stages
+    const int lastg = last / kRingN;
+    uint4 tv[kRingN][4], wv[kRingN][kWPer];
+    uint4 sg[kScPer];  // scale bytes of the next group of kRingN stages
     auto load_stage = [&](int kb, int sl) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tv[sl][i] = bld16(srs, toff[i] + kb * 256);
+      for (int i = 0; i < 4; ++i) tv[sl][i] = bld16s(srs, toff[i], kb * 256);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) wv[sl][i] = bld16(wrs, woff[i] + kb * 64);
+      for (int i = 0; i < kWPer; ++i) wv[sl][i] = bld16s(wrs, woff, kb * 64 + i * wstep);
     };
-    auto load_group = [&](int g) { sg = bld16(scs, soff + g * 16); };
+    auto load_group = [&](int g) {
+#pragma unroll
+      for (int i = 0; i < kScPer; ++i) {
+        if (kRingN == 4) {
+          sg[i] = bld16(scs, soff[i] + g * 16);
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b96(scs, soff[i] + g * 12, 0, 0);
+          sg[i] = make_uint4(v[0], v[1], v[2], 0u);
+        }
+      }
+    };
     auto store_group = [&](int g) {
-      *reinterpret_cast<uint4*>(sc_lds + (g & 1) * kScGroup + sr * 16) = sg;
+#pragma unroll
+      for (int i = 0; i < kScPer; ++i)
+        *reinterpret_cast<uint4*>(sc_lds + (g & 1) * kScG + srho[i] * 16) = sg[i];
     };
     auto store_stage = [&](int b, int sl) {
       uint8_t* tb = tok_lds + b * kTokStage;
 #pragma unroll
       for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(tb + tok_off(i * 32 + lr, lc)) = tv[sl][i];
-      uint8_t* wb = w_lds + b * kWStage;
+      uint8_t* wb = w_lds + b * kWSt;
 #pragma unroll
-      for (int i = 0; i < 2; ++i) *reinterpret_cast<uint4*>(wb + w_off(i * 128 + wr, wc)) = wv[sl][i];
+      for (int i = 0; i < kWPer; ++i)
+        *reinterpret_cast<uint4*>(wb + c_off<kWR>(i * 128 + wr, wc)) = wv[sl][i];
     };
 
-    int rho[2];  // tile weight rows of the wave's two 32-row MFMA tiles (lane r)
-    if (G1) {
-      rho[0] = wn * 32 + r;        // gate
-      rho[1] = 128 + wn * 32 + r;  // up, same features
-    } else {
-      rho[0] = wn * 64 + r;
-      rho[1] = wn * 64 + 32 + r;
-    }
-
-    f32x16_t acc[2][2];
+    int rho[MB];  // tile weight rows of the wave's 32-row MFMA blocks (lane r)
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < MB; ++m) rho[m] = (wn * MB + m) * 32 + r;
+
+    f32x16_t acc[MB][2];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
 
-    // One K stage with register slot sl = kb % kRing: multiply the stage in
-    // LDS buffer kb & 1, move stage kb+1 (slot (sl+1) % kRing, loaded
-    // kRing - 1 stages ago) into the other buffer (read last in stage kb-1,
+    // One K stage with register slot sl = kb % kRingN: multiply the stage in
+    // LDS buffer kb & 1, move stage kb+1 (slot (sl+1) % kRingN, loaded
+    // kRingN - 1 stages ago) into the other buffer (read last in stage kb-1,
     // which every wave finished before the previous barrier), refill slot sl
-    // with stage kb + kRing (near the end the last stage again: loaded,
-    // never used). Scales move in groups of four stages (kRing = 4): the
-    // first stage of group g loads group g + 1, its last stage stores it to
-    // the other scale buffer (last read in group g - 1). Loads retire in
-    // issue order; the pinned order keeps each wait to what it needs.
+    // with stage kb + kRingN (near the end the last stage again: loaded,
+    // never used). Scales move in groups of kRingN stages: the first stage of
+    // group g loads group g + 1, its last stage stores it to the other scale
+    // buffer (last read in group g - 1). Loads retire in issue order; the
+    // pinned order keeps each wait to what it needs.
     auto stage = [&](int kb, int sl) {
       const int b = kb & 1;
       const uint8_t* tb = tok_lds + b * kTokStage;
-      const uint8_t* wb = w_lds + b * kWStage;
-      const uint8_t* sb = sc_lds + ((kb >> 2) & 1) * kScGroup + (kb & 3) * 4;
-      uint32_t sdw[2];
+      const uint8_t* wb = w_lds + b * kWSt;
+      const uint8_t* sb = sc_lds + ((kb / kRingN) & 1) * kScG + sl * 4;
+      uint32_t sdw[MB];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(sb + rho[m] * 16);
+      for (int m = 0; m < MB; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(sb + rho[m] * 16);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        bf16x8_t a[2][4];
+        uint4 wf[MB];
+        float scale[MB];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const uint4 wf = *reinterpret_cast<const uint4*>(wb + w_off(rho[m], 2 * q + h));
-          const float scale = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
-          const uint32_t dw[4] = {wf.x, wf.y, wf.z, wf.w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j) a[m][j] = decode_fp4x8(dw[j], scale);
+        for (int m = 0; m < MB; ++m) {
+          wf[m] = *reinterpret_cast<const uint4*>(wb + c_off<kWR>(rho[m], 2 * q + h));
+          scale[m] = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          bf16x8_t bf[2];
+          bf16x8_t a[MB], bf[2];
+#pragma unroll
+          for (int m = 0; m < MB; ++m) {
+            const uint32_t dw = j == 0 ? wf[m].x : j == 1 ? wf[m].y : j == 2 ? wf[m].z : wf[m].w;
+            a[m] = decode_fp4x8(dw, scale[m]);
+          }
 #pragma unroll
           for (int n = 0; n < 2; ++n)
             bf[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
                 tb + tok_off(wm * 64 + n * 32 + r, 8 * q + 4 * h + j)));
 #pragma unroll
-          for (int m = 0; m < 2; ++m)
+          for (int m = 0; m < MB; ++m)
 #pragma unroll
-            for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m][j], bf[n], acc[m][n]);
+            for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m], bf[n], acc[m][n]);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      store_stage(b ^ 1, (sl + 1) % kRing);
-      if (sl == 3) store_group((kb >> 2) + 1);
+      store_stage(b ^ 1, (sl + 1) % kRingN);
+      if (sl == kRingN - 1) store_group(kb / kRingN + 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_stage(min(kb + kRing, last), sl);
-      if (sl == 0) load_group(min((kb >> 2) + 1, lastg));
+      load_stage(min(kb + kRingN, last), sl);
+      if (sl == 0) load_group(min(kb / kRingN + 1, lastg));
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     };
 
-    // Prologue: scale group 0 and stages 0 .. kRing-1 in flight, then group
+    // Prologue: scale group 0 and stages 0 .. kRingN-1 in flight, then group
     // 0 and stage 0 in LDS.
     load_group(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int sl = 0; sl < kRing; ++sl) {
+    for (int sl = 0; sl < kRingN; ++sl) {
       load_stage(min(sl, last), sl);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -272,43 +305,45 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     int kb = 0;
-    for (; kb + kRing - 1 < nkb; kb += kRing) {
+    for (; kb + kRingN - 1 < nkb; kb += kRingN) {
 #pragma unroll
-      for (int sl = 0; sl < kRing; ++sl) stage(kb + sl, sl);
+      for (int sl = 0; sl < kRingN; ++sl) stage(kb + sl, sl);
     }
 #pragma unroll
-    for (int sl = 0; sl < kRing - 1; ++sl)
+    for (int sl = 0; sl < kRingN - 1; ++sl)
       if (kb + sl < nkb) stage(kb + sl, sl);
 
-    // ---- epilogue. Lane (r, h), accumulator register 4*b4 + i holds weight
-    // row 8*b4 + 4*h + i of the 32-row tile against token row 32*n + r of the
-    // wave's 64 tokens.
+    // ---- epilogue. Lane (r, h), accumulator register 4*b4 + i holds row
+    // 8*b4 + 4*h + i of the 32-row weight block against token row 32*n + r
+    // of the wave's 64 tokens.
     if (G1) {
-      const int fbase = f0 + wn * 32;
       const __amdgpu_buffer_rsrc_t ors =
           make_rsrc(dst + static_cast<size_t>(row0) * I, static_cast<uint32_t>(nrows) * I * 2);
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
+      for (int m = 0; m < MB; ++m) {
+        const int fbase = f0 + 16 * (wn * MB + m);
 #pragma unroll
-        for (int b4 = 0; b4 < 4; ++b4) {
-          const f32x16_t& g = acc[0][n];
-          const f32x16_t& u = acc[1][n];
-          uint2 pk;
-          pk.x = pack_bf16x2(swiglu(g[4 * b4 + 0], u[4 * b4 + 0], limit),
-                             swiglu(g[4 * b4 + 1], u[4 * b4 + 1], limit));
-          pk.y = pack_bf16x2(swiglu(g[4 * b4 + 2], u[4 * b4 + 2], limit),
-                             swiglu(g[4 * b4 + 3], u[4 * b4 + 3], limit));
-          const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * I * 2 +
-                               (fbase + 8 * b4 + 4 * h) * 2;
-          bst8(ors, off, pk);
+        for (int n = 0; n < 2; ++n) {
+          const f32x16_t& c = acc[m][n];
+#pragma unroll
+          for (int b4 = 0; b4 < 2; ++b4) {
+            uint2 pk;
+            pk.x = pack_bf16x2(swiglu(c[4 * b4 + 0], c[4 * b4 + 8], limit),
+                               swiglu(c[4 * b4 + 1], c[4 * b4 + 9], limit));
+            pk.y = pack_bf16x2(swiglu(c[4 * b4 + 2], c[4 * b4 + 10], limit),
+                               swiglu(c[4 * b4 + 3], c[4 * b4 + 11], limit));
+            const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * I * 2 +
+                                 (fbase + 8 * b4 + 4 * h) * 2;
+            bst8(ors, off, pk);
+          }
         }
       }
     } else {
-      const int fbase = f0 + wn * 64;
+      const int fbase = f0 + wn * 32 * MB;
       const __amdgpu_buffer_rsrc_t ors =
           make_rsrc(dst + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int n = 0; n < 2; ++n)
 #pragma unroll
@@ -476,10 +511,18 @@ static int tiled_grid(long items, int per_cu) {
 
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st) {
   const int sub = a.B > kTileRows ? a.B / kTileRows : 1;
+  const uint32_t x_bytes = static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H * 2);
+  if (a.I % 192 == 0) {  // 384-row tiles (192 features): less LDS traffic per MFMA
+    const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 192), 1);
+    hipLaunchKernelGGL((gemm_tiled_kernel<true, 3>), dim3(grid), dim3(kTiledThreads), 0, st, a.x,
+                       x_bytes, a.w13, a.s13, a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp,
+                       sub, a.limit, a.act);
+    return hipGetLastError();
+  }
   const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128), 1);
-  hipLaunchKernelGGL(gemm_tiled_kernel<true>, dim3(grid), dim3(kTiledThreads), 0, st, a.x,
-                     static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H * 2), a.w13, a.s13,
-                     a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp, sub, a.limit, a.act);
+  hipLaunchKernelGGL((gemm_tiled_kernel<true, 2>), dim3(grid), dim3(kTiledThreads), 0, st, a.x,
+                     x_bytes, a.w13, a.s13, a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp,
+                     sub, a.limit, a.act);
   return hipGetLastError();
 }
 
@@ -499,7 +542,7 @@ hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
     return hipGetLastError();
   }
   const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256), 1);
-  hipLaunchKernelGGL(gemm_tiled_kernel<false>, dim3(grid), dim3(kTiledThreads), 0, st, a.act,
+  hipLaunchKernelGGL((gemm_tiled_kernel<false, 2>), dim3(grid), dim3(kTiledThreads), 0, st, a.act,
                      static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2), a.w2, a.s2,
                      a.dense_tiles, a.counters, a.sorted_slot, a.I, a.H, a.Kp, 1, a.limit, a.y);
   return hipGetLastError();
