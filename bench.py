@@ -63,7 +63,7 @@ def measured_traffic(config: str, kernel: str):
                 rec = json.loads(line[len("traffic-json: "):])
                 if rec.get("workload") != config or not rec.get("kernel", "").startswith("moe::" + kernel.split("<")[0]):
                     continue
-                if ("<true>" in kernel) != ("<true>" in rec["kernel"]):
+                if ("<true" in kernel) != ("<true" in rec["kernel"]):
                     continue
                 h = hashlib.sha256()
                 for src in rec["src"]:
@@ -245,7 +245,7 @@ def main():
                 "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     kernel = ("gemm1_decode_a8_kernel" if a8 else "gemm1_decode_kernel") if s.B <= 32 else \
-        ("gemm_tiled_a8_kernel<true>" if a8 else "gemm_tiled_kernel<true>")
+        ("gemm_tiled_a8_kernel<true>" if a8 else "gemm_tiled_kernel<true")
     roof["traffic"] = measured_traffic(args.config, kernel)
     roof["kernel"] = kernel
     roof["kernel_us"] = round(gemm1_ms * 1e3, 2)

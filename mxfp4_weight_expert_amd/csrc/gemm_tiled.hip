@@ -48,12 +48,20 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// LDS bank swizzle of row r: an XOR over 16 chunk slots that is a bijection
+// on every 16 aligned rows and, within each row parity, on every 32 aligned
+// rows. gfx950 serves a 16-byte LDS access 32 lanes at a time over 128
+// banks (16 lanes over 64 banks on earlier parts), so 32 consecutive rows
+// read at one logical chunk fall on 32 distinct 16-byte bank groups. It
+// depends on r mod 32 only, so rows 32 apart share their lane addresses.
+__device__ __forceinline__ int row_swz(int r) { return (r ^ ((r >> 4) & 1)) & 15; }
+
 // Byte offset of 16-byte chunk c (0..15) of bf16 token row r (256-byte rows)
-// inside a stage. The XOR swizzle puts 16 consecutive rows read at one chunk
-// on 16 distinct 16-byte bank groups, and 16 consecutive chunks of one row
-// written by 16 lanes likewise.
+// inside a stage. 32 consecutive rows read at one chunk, and the 16 chunks
+// of each of two consecutive rows written by 32 lanes, hit distinct bank
+// groups.
 __device__ __forceinline__ uint32_t tok_off(int r, int c) {
-  return static_cast<uint32_t>(r * 256 + ((c ^ (r & 15)) << 4));
+  return static_cast<uint32_t>(r * 256 + ((c ^ row_swz(r)) << 4));
 }
 // Byte offset of 16-byte chunk c (0..7) of E4M3 token row r (128-byte rows):
 // 16 consecutive rows read at one chunk differ in row parity or in
@@ -62,20 +70,21 @@ __device__ __forceinline__ uint32_t tok8_off(int r, int c) {
   return static_cast<uint32_t>(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
 }
 // Byte offset of 16-byte chunk c (0..3) of weight row rho in a stage of
-// ROWS rows: chunk-major, so the 32 rows of one MFMA fragment are a
-// permutation of 32 consecutive 16-byte slots (conflict-free reads); the XOR
-// with 4c spreads the four chunks of a row, written by four neighbouring
-// lanes, over distinct bank groups.
+// ROWS rows (a multiple of 32): chunk-major, so the 32 rows of one MFMA
+// fragment are a permutation of 32 consecutive 16-byte slots (conflict-free
+// reads); the XOR with 4c ^ 8c (0, 12, 24, 20 for c = 0..3) spreads the four
+// chunks of 8 rows, written by 32 neighbouring lanes, over distinct bank
+// groups under both the 64- and the 128-bank organisation.
 template <int ROWS>
 __device__ __forceinline__ uint32_t c_off(int rho, int c) {
-  return static_cast<uint32_t>(c * (ROWS * 16) + ((rho ^ (c << 2)) << 4));
+  return static_cast<uint32_t>(c * (ROWS * 16) + ((rho ^ (c << 2) ^ (c << 3)) << 4));
 }
 __device__ __forceinline__ uint32_t w_off(int rho, int c) { return c_off<kTileWRows>(rho, c); }
 
 }  // namespace
 
-// LDS: two stages of tokens, packed weights and weight scales (98 KB for
-// MB = 2, 124 KB for MB = 3). The stage copy goes global -> registers -> LDS
+// LDS: two stages of tokens, packed weights and weight scales (104 KB for
+// MB = 2, 121 KB for MB = 3). The stage copy goes global -> registers -> LDS
 // with RING stages of loads in flight.
 //
 // MB is the number of 32-row weight blocks per wave: the block tile has
@@ -93,7 +102,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
   constexpr int kWR = 128 * MB;               // weight rows per tile
   constexpr int kRingN = MB == 2 ? 4 : 3;     // stages of loads in flight = stages per scale group
   constexpr int kWSt = kWR * 64;              // packed weight bytes of one K stage
-  constexpr int kScG = kWR * 16;              // one 16-byte scale slot per weight row
+  constexpr int kScG = kWR * 4 * kRingN;      // scale words of one group, stage-major
   constexpr int kWPer = kWR * 4 / kTiledThreads;  // weight chunks per thread and stage
   constexpr int kScPer = (kWR + kTiledThreads - 1) / kTiledThreads;
   static_assert(kWR * 4 % kTiledThreads == 0, "weight chunks must split evenly");
@@ -119,7 +128,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
   const int lane = lane_id();
   const int r = lane & 31, h = lane >> 5;
   // thread roles in the stage copy: token chunk t%16 of rows 32i + t/16;
-  // weight chunk t%4 of tile rows 128i + t/4; the scale slot of tile rows
+  // weight chunk t%4 of tile rows 128i + t/4; the scale words of tile rows
   // (t + 512i) mod kWR (threads that meet a row twice store the same bytes)
   const int lc = t & 15, lr = t >> 4, wc = t & 3, wr = t >> 2;
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
@@ -211,9 +220,13 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       }
     };
     auto store_group = [&](int g) {
+      uint32_t* sb = reinterpret_cast<uint32_t*>(sc_lds + (g & 1) * kScG);
 #pragma unroll
-      for (int i = 0; i < kScPer; ++i)
-        *reinterpret_cast<uint4*>(sc_lds + (g & 1) * kScG + srho[i] * 16) = sg[i];
+      for (int i = 0; i < kScPer; ++i) {
+        const uint32_t v[4] = {sg[i].x, sg[i].y, sg[i].z, sg[i].w};
+#pragma unroll
+        for (int q = 0; q < kRingN; ++q) sb[q * kWR + srho[i]] = v[q];
+      }
     };
     auto store_stage = [&](int b, int sl) {
       uint8_t* tb = tok_lds + b * kTokStage;
@@ -250,10 +263,11 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       const int b = kb & 1;
       const uint8_t* tb = tok_lds + b * kTokStage;
       const uint8_t* wb = w_lds + b * kWSt;
-      const uint8_t* sb = sc_lds + ((kb / kRingN) & 1) * kScG + sl * 4;
+      const uint32_t* sb =
+          reinterpret_cast<const uint32_t*>(sc_lds + ((kb / kRingN) & 1) * kScG) + sl * kWR;
       uint32_t sdw[MB];
 #pragma unroll
-      for (int m = 0; m < MB; ++m) sdw[m] = *reinterpret_cast<const uint32_t*>(sb + rho[m] * 16);
+      for (int m = 0; m < MB; ++m) sdw[m] = sb[rho[m]];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         uint4 wf[MB];
@@ -390,9 +404,9 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
   const int nspan = H >> 8;
   constexpr uint32_t wrow = I / 2, srow = I / 32;
   // act chunk (16 bytes) c of tile row rr sits at rr * kRowB + 16 * swz(c):
-  // within each 16-chunk group the chunk index is XORed with rr & 15
+  // within each 16-chunk group the chunk index is XORed with row_swz(rr)
   auto a_off = [](int rr, int c) -> uint32_t {
-    return static_cast<uint32_t>(rr * kRowB + (((c & ~15) | ((c ^ rr) & 15)) << 4));
+    return static_cast<uint32_t>(rr * kRowB + (((c & ~15) | ((c ^ row_swz(rr)) & 15)) << 4));
   };
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
     const int tile = xcd * per + slot;
