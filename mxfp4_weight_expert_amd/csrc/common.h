@@ -226,6 +226,10 @@ __device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ __forceinline__ uint4 bld16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, soff, 0));
 }
+__device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r,
+                                         off, 0, 0);
+}
 __device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, v), r,
                                         off, 0, 0);

@@ -381,7 +381,10 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 // weights come straight from global memory into registers, and K step kb
 // of the next span is loaded into the registers of step kb right after they
 // are decoded: the loads have about one span of MFMA work to arrive, and no
-// barrier is needed between spans.
+// barrier is needed between spans. Each span's outputs pass through the
+// wave's own 16 KB of LDS so that the stores write whole 128-byte pieces of
+// Y rows (16 bytes per lane) instead of 8-byte pieces of 32 rows at a time,
+// which kept the texture address queue full. LDS: 128 * I * 2 + 64 KB.
 // ---------------------------------------------------------------------------
 constexpr int kResThreads = 256;
 
@@ -393,6 +396,8 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
   constexpr int I = NKB * 128;
   constexpr int kRowB = I * 2;                 // act row bytes
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kTileRows * kRowB];
+  // per wave: its 128 x 64 output tile of one span, bf16, 128-byte rows
+  __shared__ __attribute__((aligned(16))) uint8_t o_lds[4 * kTileRows * 128];
   const int ntiles = counters[kCtrGate] == 1 ? counters[kCtrGate + 3] : 0;
   const int xcd = blockIdx.x & 7;
   const int per = (ntiles + 7) >> 3;
@@ -491,10 +496,13 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
           }
         }
       }
-      // ---- this span's 64 x 128 outputs of the wave
-      const int fbase = sp * 256 + wn * 64;
-      const __amdgpu_buffer_rsrc_t ors =
-          make_rsrc(y + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
+      // ---- this span's 64 x 128 outputs of the wave go through its LDS
+      // staging rows, so that each store writes 128-byte row pieces. Token
+      // row t holds 8 chunks of 8 features; chunk c sits in slot
+      // c ^ ((t >> 1) & 7) with its two 8-byte halves swapped when bit 4 of t
+      // is set, which puts the 32 8-byte writes of each half-wave on
+      // distinct banks.
+      uint8_t* stg = o_lds + wn * (kTileRows * 128);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -504,10 +512,22 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
             uint2 pk;
             pk.x = pack_bf16x2(acc[m][n][4 * b4 + 0], acc[m][n][4 * b4 + 1]);
             pk.y = pack_bf16x2(acc[m][n][4 * b4 + 2], acc[m][n][4 * b4 + 3]);
-            const uint32_t off = static_cast<uint32_t>(n * 32 + r) * H * 2 +
-                                 (fbase + 32 * m + 8 * b4 + 4 * h) * 2;
-            bst8(ors, off, pk);
+            const int tk = n * 32 + r;
+            const int c = 4 * m + b4;
+            *reinterpret_cast<uint2*>(stg + tk * 128 + ((c ^ ((tk >> 1) & 7)) << 4) +
+                                      ((h ^ ((tk >> 4) & 1)) << 3)) = pk;
           }
+      const int fbase = sp * 256 + wn * 64;
+      const __amdgpu_buffer_rsrc_t ors =
+          make_rsrc(y + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tk = 8 * i + (lane >> 3);
+        const int c = lane & 7;
+        uint4 v = *reinterpret_cast<const uint4*>(stg + tk * 128 + ((c ^ ((tk >> 1) & 7)) << 4));
+        if ((tk >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        bst16(ors, static_cast<uint32_t>(tk) * H * 2 + (fbase + 8 * c) * 2, v);
+      }
     }
     __syncthreads();  // every wave done with the act tile before the next copy
   }
