@@ -246,5 +246,8 @@ __device__ __forceinline__ uint32_t bld1(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }
+__device__ __forceinline__ uint32_t bld4s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, soff, 0);
+}
 
 }  // namespace moe

@@ -408,11 +408,22 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
   const int r = lane & 31, h = lane >> 5;
   const int nspan = H >> 8;
   constexpr uint32_t wrow = I / 2, srow = I / 32;
-  // act chunk (16 bytes) c of tile row rr sits at rr * kRowB + 16 * swz(c):
-  // within each 16-chunk group the chunk index is XORed with row_swz(rr)
+  // Tile row rr lives in LDS row slot (rr % 32) * 4 + rr / 32, so that the
+  // four 32-row token blocks a lane reads sit kRowB apart (immediate
+  // offsets); its 16-byte chunk c sits at chunk (c & ~15) | ((c ^ row_swz(rr))
+  // & 15), which spreads the 16 rows read at one chunk over all banks.
   auto a_off = [](int rr, int c) -> uint32_t {
-    return static_cast<uint32_t>(rr * kRowB + (((c & ~15) | ((c ^ row_swz(rr)) & 15)) << 4));
+    const int sl = ((rr & 31) << 2) | (rr >> 5);
+    return static_cast<uint32_t>(sl * kRowB + (((c & ~15) | ((c ^ row_swz(rr)) & 15)) << 4));
   };
+  // lane's read base for K sub-step (q, j) of any kb: row slot 4r, chunk
+  // 8q + 4h + j swizzled; block n and step kb add n * kRowB + kb * 256
+  const uint8_t* abase[8];
+#pragma unroll
+  for (int s8 = 0; s8 < 8; ++s8)
+    abase[s8] = a_lds + r * 4 * kRowB + ((((8 * (s8 >> 2) + 4 * h + (s8 & 3)) ^ row_swz(r)) & 15) << 4);
+  const uint32_t wv_off = static_cast<uint32_t>(r) * wrow + h * 16;
+  const uint32_t sv_off = static_cast<uint32_t>(r) * srow;
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
     const int tile = xcd * per + slot;
     if (tile >= ntiles) break;
@@ -438,7 +449,7 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
         *reinterpret_cast<uint4*>(a_lds + a_off(rr, c)) = v[i];
       }
     }
-    // ---- weights of span 0 into registers
+    // ---- weights of span 0 into registers; wave-uniform offsets in SGPRs
     const __amdgpu_buffer_rsrc_t wrs =
         make_rsrc(w2 + static_cast<size_t>(e) * H * wrow, static_cast<uint32_t>(H) * wrow);
     const __amdgpu_buffer_rsrc_t scs =
@@ -448,10 +459,10 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
     auto load_w = [&](int sp, int kb) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        const uint32_t row = static_cast<uint32_t>(sp * 256 + wn * 64 + m * 32 + r);
+        const uint32_t rb = static_cast<uint32_t>(sp * 256 + wn * 64 + m * 32);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) wr[kb][m][q] = bld16(wrs, row * wrow + kb * 64 + q * 32 + h * 16);
-        sw[kb][m] = bld4(scs, row * srow + kb * 4);
+        for (int q = 0; q < 2; ++q) wr[kb][m][q] = bld16s(wrs, wv_off, rb * wrow + kb * 64 + q * 32);
+        sw[kb][m] = bld4s(scs, sv_off, rb * srow + kb * 4);
       }
     };
 #pragma unroll
@@ -467,33 +478,70 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
       const int spn = min(sp + 1, nspan - 1);  // last span: reload it, unused
+      // Software pipeline over the 8 * NKB K sub-steps (kb, q, j): step s
+      // multiplies token fragments read during step s - 1 with weight
+      // fragments decoded during the previous (kb, q) block, while it reads
+      // the fragments of step s + 1 and decodes one quarter of the next
+      // block. Each step is its own scheduling region with the reads first
+      // and MFMAs alternating with converts.
+      constexpr int kBlocks = 2 * NKB;
+      auto decode = [&](int blk, int j, bf16x8_t (&dst)[2][4]) {
+        const int kb = blk >> 1, q = blk & 1;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+        for (int m = 0; m < 2; ++m) {
+          const float scale = e8m0_scale_operand((sw[kb][m] >> (8 * (2 * q + h))) & 0xffu);
+          const uint4 v = wr[kb][m][q];
+          const uint32_t dw = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+          dst[m][j] = decode_fp4x8(dw, scale);
+        }
+      };
+      auto read_b = [&](int stp, bf16x8_t (&dst)[4]) {
+        const int kb = stp >> 3, s8 = stp & 7;
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          bf16x8_t a[2][4];
+        for (int n = 0; n < 4; ++n)
+          dst[n] = as_bf16x8(*reinterpret_cast<const uint4*>(abase[s8] + n * kRowB + kb * 256));
+      };
+      bf16x8_t acur[2][4], anxt[2][4], bcur[4], bnxt[4];
+      __builtin_amdgcn_sched_barrier(0);
+      read_b(0, bcur);
 #pragma unroll
-          for (int m = 0; m < 2; ++m) {
-            const float scale = e8m0_scale_operand((sw[kb][m] >> (8 * (2 * q + h))) & 0xffu);
-            const uint32_t dw[4] = {wr[kb][m][q].x, wr[kb][m][q].y, wr[kb][m][q].z, wr[kb][m][q].w};
+      for (int j = 0; j < 4; ++j) decode(0, j, acur);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) a[m][j] = decode_fp4x8(dw[j], scale);
+      for (int blk = 0; blk < kBlocks; ++blk) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int stp = 4 * blk + j;
+          __builtin_amdgcn_sched_barrier(0);
+          if (stp + 1 < 4 * kBlocks) read_b(stp + 1, bnxt);
+          if (blk + 1 < kBlocks) decode(blk + 1, j, anxt);
+#pragma unroll
+          for (int n = 0; n < 4; ++n)
+#pragma unroll
+            for (int m = 0; m < 2; ++m) acc[m][n] = mfma32x32x16(acur[m][j], bcur[n], acc[m][n]);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // DS reads first
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // one VALU op
           }
-          if (q == 1) {  // step kb fully decoded: refill it with the next span
+          __builtin_amdgcn_sched_barrier(0);
+          if (stp + 1 < 4 * kBlocks) {
+#pragma unroll
+            for (int n = 0; n < 4; ++n) bcur[n] = bnxt[n];
+          }
+          // block blk + 1 = (kb, 1) is decoded once blk = (kb, 0) ends:
+          // step kb's weights are free for the next span
+          if (j == 3 && (blk & 1) == 0) {
             __builtin_amdgcn_sched_barrier(0);
-            load_w(spn, kb);
+            load_w(spn, blk >> 1);
             __builtin_amdgcn_sched_barrier(0);
           }
+        }
+        if (blk + 1 < kBlocks) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
+          for (int m = 0; m < 2; ++m)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-              const bf16x8_t bf = as_bf16x8(*reinterpret_cast<const uint4*>(
-                  a_lds + a_off(n * 32 + r, kb * 16 + 8 * q + 4 * h + j)));
-#pragma unroll
-              for (int m = 0; m < 2; ++m) acc[m][n] = mfma32x32x16(a[m][j], bf, acc[m][n]);
-            }
-          }
+            for (int j = 0; j < 4; ++j) acur[m][j] = anxt[m][j];
         }
       }
       // ---- this span's 64 x 128 outputs of the wave go through its LDS
