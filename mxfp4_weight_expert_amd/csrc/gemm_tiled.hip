@@ -100,7 +100,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int I, int H,
     int Kp, int sub, float limit, uint16_t* __restrict__ dst) {
   constexpr int kWR = 128 * MB;               // weight rows per tile
-  constexpr int kRingN = MB == 2 ? 4 : 3;     // stages of loads in flight = stages per scale group
+  constexpr int kRingN = MB == 2 ? 4 : 2;     // stages of loads in flight = stages per scale group
   constexpr int kWSt = kWR * 64;              // packed weight bytes of one K stage
   constexpr int kScG = kWR * 4 * kRingN;      // scale words of one group, stage-major
   constexpr int kWPer = kWR * 4 / kTiledThreads;  // weight chunks per thread and stage
@@ -213,9 +213,12 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       for (int i = 0; i < kScPer; ++i) {
         if (kRingN == 4) {
           sg[i] = bld16(scs, soff[i] + g * 16);
-        } else {
+        } else if (kRingN == 3) {
           const auto v = __builtin_amdgcn_raw_buffer_load_b96(scs, soff[i] + g * 12, 0, 0);
           sg[i] = make_uint4(v[0], v[1], v[2], 0u);
+        } else {
+          const auto v = __builtin_amdgcn_raw_buffer_load_b64(scs, soff[i] + g * 8, 0, 0);
+          sg[i] = make_uint4(v[0], v[1], 0u, 0u);
         }
       }
     };
@@ -265,34 +268,70 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       const uint8_t* wb = w_lds + b * kWSt;
       const uint32_t* sb =
           reinterpret_cast<const uint32_t*>(sc_lds + ((kb / kRingN) & 1) * kScG) + sl * kWR;
+      // Eight K sub-steps (q, j) of 16: step t multiplies weight fragments
+      // decoded during step t - 1 with token fragments read during step
+      // t - 1, while it reads the tokens of step t + 1 and decodes its weight
+      // fragments. Each step is a scheduling region of its own, with the
+      // reads first and the MFMAs alternating with the converts.
       uint32_t sdw[MB];
 #pragma unroll
       for (int m = 0; m < MB; ++m) sdw[m] = sb[rho[m]];
+      uint4 wq[2][MB];
+      float scale[2][MB];
+      bf16x8_t ac[MB], an[MB], bc[2], bn[2];
+      auto read_tok = [&](int t8, bf16x8_t (&dst)[2]) {
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        uint4 wf[MB];
-        float scale[MB];
+        for (int n = 0; n < 2; ++n)
+          dst[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
+              tb + tok_off(wm * 64 + n * 32 + r, 8 * (t8 >> 2) + 4 * h + (t8 & 3))));
+      };
+      auto read_w = [&](int q) {
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-          wf[m] = *reinterpret_cast<const uint4*>(wb + c_off<kWR>(rho[m], 2 * q + h));
-          scale[m] = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
+          wq[q][m] = *reinterpret_cast<const uint4*>(wb + c_off<kWR>(rho[m], 2 * q + h));
+          scale[q][m] = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
+        }
+      };
+      auto dec = [&](int t8, bf16x8_t (&dst)[MB]) {
+        const int q = t8 >> 2, j = t8 & 3;
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+          const uint4 v = wq[q][m];
+          const uint32_t dw = j == 0 ? v.x : j == 1 ? v.y : j == 2 ? v.z : v.w;
+          dst[m] = decode_fp4x8(dw, scale[q][m]);
+        }
+      };
+      read_w(0);
+      read_tok(0, bc);
+      dec(0, ac);
+#pragma unroll
+      for (int t8 = 0; t8 < 8; ++t8) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (t8 == 0) read_w(1);
+        if (t8 < 7) {
+          read_tok(t8 + 1, bn);
+          dec(t8 + 1, an);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x8_t a[MB], bf[2];
+        for (int m = 0; m < MB; ++m)
 #pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const uint32_t dw = j == 0 ? wf[m].x : j == 1 ? wf[m].y : j == 2 ? wf[m].z : wf[m].w;
-            a[m] = decode_fp4x8(dw, scale[m]);
-          }
+          for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(ac[m], bc[n], acc[m][n]);
+        if (t8 == 0) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2 + MB, 0);  // LDS reads
+        } else {
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
 #pragma unroll
-          for (int n = 0; n < 2; ++n)
-            bf[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
-                tb + tok_off(wm * 64 + n * 32 + r, 8 * q + 4 * h + j)));
+        for (int k = 0; k < 2 * MB; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU ops
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (t8 < 7) {
 #pragma unroll
-          for (int m = 0; m < MB; ++m)
+          for (int m = 0; m < MB; ++m) ac[m] = an[m];
 #pragma unroll
-            for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(a[m], bf[n], acc[m][n]);
+          for (int n = 0; n < 2; ++n) bc[n] = bn[n];
         }
       }
       __builtin_amdgcn_sched_barrier(0);
