@@ -243,6 +243,9 @@ __device__ __forceinline__ void bst1(__amdgpu_buffer_rsrc_t r, uint32_t off, uin
 __device__ __forceinline__ uint32_t bld1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }
+__device__ __forceinline__ uint32_t bld1s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, off, soff, 0);
+}
 __device__ __forceinline__ uint32_t bld4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
 }

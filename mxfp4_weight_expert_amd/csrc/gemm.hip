@@ -57,12 +57,12 @@ __device__ __forceinline__ void wave_copy_to_lds(uint8_t* lds, const uint8_t* sr
 // D divides nkb, so the unrolled body has no tail branches: the
 // vector-memory counter retires loads in issue order, and straight-line code
 // lets every wait cover only the step it needs.
-template <int D, int NS>
-__device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (&wofs)[4],
-                                             const uint8_t* ls, const uint32_t (&lofs)[4], int nkb,
+template <int D, int NS, int NT = 4>
+__device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (&wofs)[NT],
+                                             const uint8_t* ls, const uint32_t (&lofs)[NT], int nkb,
                                              __amdgpu_buffer_rsrc_t brs, const uint32_t (&boff)[NS],
-                                             f32x4_t (&acc)[NS][4]) {
-  uint4 w[D][4], xb[D][NS][4];
+                                             f32x4_t (&acc)[NS][NT]) {
+  uint4 w[D][NT], xb[D][NS][4];
   // Prologue in slot order (pinned), matching the steady-state issue order.
 #pragma unroll
   for (int d = 0; d < D; ++d) {
@@ -71,18 +71,18 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + d * 256 + j * 16);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + d * 64);
+    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + d * 64);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int last = nkb - 1;
   // One ring step: multiply slot d (step kb), then refill it with step
   // kb + D (near the end the last step again; those loads are never used).
   auto step = [&](int kb, int d) {
-    float sc[4];
+    float sc[NT];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) sc[t] = e8m0_scale_operand(ls[lofs[t] + kb * 4]);
+    for (int t = 0; t < NT; ++t) sc[t] = e8m0_scale_operand(ls[lofs[t] + kb * 4]);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < NT; ++t) {
       const uint32_t ww[4] = {w[d][t].x, w[d][t].y, w[d][t].z, w[d][t].w};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -98,7 +98,7 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + nk * 256 + j * 16);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + nk * 64);
+    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + nk * 64);
     __builtin_amdgcn_sched_barrier(0);
   };
   // The first ring cycle is peeled: the loop is then entered with loads
@@ -123,35 +123,41 @@ inline int ring_depth(int nkb) {
 }
 
 // GEMM1 + SwiGLU, decode shape. Item = (chunk of at most 16 * NSMAX rows,
-// 32-feature group): tiles are gate rows f0+[0,16), up rows I+f0+[0,16),
-// gate f0+16+[0,16), up I+f0+16+[0,16). A chunk of more than 16 rows runs
-// both 16-row sub-tiles against each weight load, so an expert's weights
-// are streamed once per chunk. Dynamic LDS: 4 waves x 2H bytes (the group's
-// 32 gate and 32 up scale rows). `units`/`ctr`: the chunk table and the
-// counter word holding its length.
-template <int D, int NSMAX>
+// group of 16 * TP features): tile 2p holds gate rows f0 + 16p + [0, 16),
+// tile 2p + 1 the up rows I + f0 + 16p + [0, 16). A chunk of more than 16
+// rows runs both 16-row sub-tiles against each weight load, so an expert's
+// weights are streamed once per chunk; a wider feature group cuts how often
+// the chunk's token rows are re-read (once per group). Dynamic LDS: 4 waves
+// x TP * H bytes (the group's gate and up scale rows). `units`/`ctr`: the
+// chunk table and the counter word holding its length.
+template <int D, int NSMAX, int TP>
 __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int T, int H,
     int I, int Kp, float limit, uint16_t* __restrict__ act) {
+  constexpr int NT = 2 * TP;
   extern __shared__ uint8_t lds_scales[];
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
-  const int groups = I >> 5;
+  const int groups = I / (16 * TP);
   const int nitems = counters[ctr] * groups;
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
   const int nkb = H >> 7;
-  const int blk = 32 * static_cast<int>(srow);  // 32 scale rows = H bytes
+  const int blk = 16 * TP * static_cast<int>(srow);  // the group's gate (or up) scale rows
   uint8_t* my = lds_scales + wave_index() * 2 * blk;
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(T) * H * 2));
-  const uint32_t wofs[4] = {0u, static_cast<uint32_t>(I * wrow), static_cast<uint32_t>(16 * wrow),
-                            static_cast<uint32_t>((I + 16) * wrow)};
-  const uint32_t lofs[4] = {0u, static_cast<uint32_t>(blk), static_cast<uint32_t>(16 * srow),
-                            static_cast<uint32_t>(blk + 16 * srow)};
+  uint32_t wofs[NT], lofs[NT];
+#pragma unroll
+  for (int p = 0; p < TP; ++p) {
+    wofs[2 * p] = static_cast<uint32_t>(16 * p * wrow);
+    wofs[2 * p + 1] = static_cast<uint32_t>((I + 16 * p) * wrow);
+    lofs[2 * p] = static_cast<uint32_t>(16 * p * srow);
+    lofs[2 * p + 1] = static_cast<uint32_t>(blk + 16 * p * srow);
+  }
   for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
     const int u = item / groups;
-    const int f0 = (item - u * groups) * 32;
+    const int f0 = (item - u * groups) * 16 * TP;
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * 2 * I + f0;
@@ -169,32 +175,32 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     // rows past the chunk's end fall outside the buffer: stores dropped
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
-    auto store = [&](const f32x4_t (&acc)[4], int s) {
+    auto store = [&](const f32x4_t (&acc)[NT], int s) {
       const uint32_t aoff = static_cast<uint32_t>(16 * s + r) * I * 2 + (f0 + g * 4) * 2;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const f32x4_t& ag = acc[2 * h];
-        const f32x4_t& au = acc[2 * h + 1];
+      for (int p = 0; p < TP; ++p) {
+        const f32x4_t& ag = acc[2 * p];
+        const f32x4_t& au = acc[2 * p + 1];
         uint2 pk;
         pk.x = pack_bf16x2(swiglu(ag[0], au[0], limit), swiglu(ag[1], au[1], limit));
         pk.y = pack_bf16x2(swiglu(ag[2], au[2], limit), swiglu(ag[3], au[3], limit));
-        bst8(ars, aoff + h * 32, pk);
+        bst8(ars, aoff + p * 32, pk);
       }
     };
     if (NSMAX == 1 || nrows <= 16) {
-      f32x4_t acc[1][4];
+      f32x4_t acc[1][NT];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < NT; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint32_t b1[1] = {boff[0]};
-      stream_block<D, 1>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1, acc);
+      stream_block<D, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1, acc);
       store(acc[0], 0);
     } else {
-      f32x4_t acc[NSMAX][4];
+      f32x4_t acc[NSMAX][NT];
 #pragma unroll
       for (int s = 0; s < NSMAX; ++s)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      stream_block<D, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, boff, acc);
+        for (int t = 0; t < NT; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      stream_block<D, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, boff, acc);
 #pragma unroll
       for (int s = 0; s < NSMAX; ++s) store(acc[s], s);
     }
@@ -587,6 +593,10 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
 #define MOE_STREAM_GRID (256 * 3)
 #endif
 
+#ifndef MOE_G1_TP
+#define MOE_G1_TP 2
+#endif
+
 static int grid_for(long items) {
   long blocks = (items + 3) / 4;
   if (blocks < 1) blocks = 1;
@@ -601,11 +611,12 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
     const bool c32 = a.B == 32;
     const int32_t* units = c32 ? a.vinfo : a.units16;
     const int ctr = c32 ? kCtrNumV : kCtrNumU;
-    const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / 32));
-    const size_t lds = static_cast<size_t>(4) * 2 * a.H;
+    constexpr int kTP = MOE_G1_TP;  // 16-feature tile pairs per wave
+    const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / (16 * kTP)));
+    const size_t lds = static_cast<size_t>(4) * kTP * a.H;
 #define MOE_G1D(DD, NS)                                                                           \
-  hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS>), dim3(grid), dim3(kGemmBlock), lds, st, a.x,    \
-                     a.w13, a.s13, units, ctr, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp,       \
+  hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, kTP>), dim3(grid), dim3(kGemmBlock), lds, st,   \
+                     a.x, a.w13, a.s13, units, ctr, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp,  \
                      a.limit, a.act)
     const int d = ring_depth(a.H / 128);
     if (c32) {

@@ -253,6 +253,14 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[m][n][v] = 0.0f;
 
+    // operands of the sub-step deferred to the next stage (zero before the
+    // first stage: its group 0 then adds nothing)
+    bf16x8_t ac[MB], bc[2];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) ac[m] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+#pragma unroll
+    for (int n = 0; n < 2; ++n) bc[n] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+
     // One K stage with register slot sl = kb % kRingN: multiply the stage in
     // LDS buffer kb & 1, move stage kb+1 (slot (sl+1) % kRingN, loaded
     // kRingN - 1 stages ago) into the other buffer (read last in stage kb-1,
@@ -268,29 +276,23 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       const uint8_t* wb = w_lds + b * kWSt;
       const uint32_t* sb =
           reinterpret_cast<const uint32_t*>(sc_lds + ((kb / kRingN) & 1) * kScG) + sl * kWR;
-      // Eight K sub-steps (q, j) of 16: step t multiplies weight fragments
-      // decoded during step t - 1 with token fragments read during step
-      // t - 1, while it reads the tokens of step t + 1 and decodes its weight
-      // fragments. Each step is a scheduling region of its own, with the
-      // reads first and the MFMAs alternating with the converts.
+      // Eight K sub-steps (q, j) of 16, software-pipelined: the operands of
+      // a sub-step are read and decoded one group of MFMAs ahead. Group 0
+      // multiplies the previous stage's last sub-step (its operands are in
+      // registers, so it needs no barrier) while this stage's scales, packed
+      // weights and first tokens arrive; group g = 1..7 multiplies sub-step
+      // g - 1 and prepares sub-step g; sub-step 7 waits in (ac, bc) for the
+      // next stage's group 0. Each group is a scheduling region of its own,
+      // with the LDS reads first and the MFMAs alternating with converts.
       uint32_t sdw[MB];
-#pragma unroll
-      for (int m = 0; m < MB; ++m) sdw[m] = sb[rho[m]];
       uint4 wq[2][MB];
       float scale[2][MB];
-      bf16x8_t ac[MB], an[MB], bc[2], bn[2];
+      bf16x8_t an[MB], bn[2];
       auto read_tok = [&](int t8, bf16x8_t (&dst)[2]) {
 #pragma unroll
         for (int n = 0; n < 2; ++n)
           dst[n] = as_bf16x8(*reinterpret_cast<const uint4*>(
               tb + tok_off(wm * 64 + n * 32 + r, 8 * (t8 >> 2) + 4 * h + (t8 & 3))));
-      };
-      auto read_w = [&](int q) {
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          wq[q][m] = *reinterpret_cast<const uint4*>(wb + c_off<kWR>(rho[m], 2 * q + h));
-          scale[q][m] = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
-        }
       };
       auto dec = [&](int t8, bf16x8_t (&dst)[MB]) {
         const int q = t8 >> 2, j = t8 & 3;
@@ -301,38 +303,53 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
           dst[m] = decode_fp4x8(dw, scale[q][m]);
         }
       };
-      read_w(0);
-      read_tok(0, bc);
-      dec(0, ac);
-#pragma unroll
-      for (int t8 = 0; t8 < 8; ++t8) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (t8 == 0) read_w(1);
-        if (t8 < 7) {
-          read_tok(t8 + 1, bn);
-          dec(t8 + 1, an);
-        }
+      auto mfmas = [&]() {
 #pragma unroll
         for (int m = 0; m < MB; ++m)
 #pragma unroll
           for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(ac[m], bc[n], acc[m][n]);
-        if (t8 == 0) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2 + MB, 0);  // LDS reads
-        } else {
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
+      };
+      auto rotate = [&]() {
+#pragma unroll
+        for (int m = 0; m < MB; ++m) ac[m] = an[m];
+#pragma unroll
+        for (int n = 0; n < 2; ++n) bc[n] = bn[n];
+      };
+      // group 0
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int m = 0; m < MB; ++m) sdw[m] = sb[rho[m]];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          wq[q][m] = *reinterpret_cast<const uint4*>(wb + c_off<kWR>(rho[m], 2 * q + h));
+      read_tok(0, bn);
+      mfmas();
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          scale[q][m] = e8m0_scale_operand((sdw[m] >> (8 * (2 * q + h))) & 0xffu);
+      dec(0, an);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3 * MB + 2, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 2 * MB, 0);      // MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      rotate();
+#pragma unroll
+      for (int t8 = 0; t8 < 7; ++t8) {
+        __builtin_amdgcn_sched_barrier(0);
+        read_tok(t8 + 1, bn);
+        dec(t8 + 1, an);
+        mfmas();
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
 #pragma unroll
         for (int k = 0; k < 2 * MB; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
           __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // two VALU ops
         }
         __builtin_amdgcn_sched_barrier(0);
-        if (t8 < 7) {
-#pragma unroll
-          for (int m = 0; m < MB; ++m) ac[m] = an[m];
-#pragma unroll
-          for (int n = 0; n < 2; ++n) bc[n] = bn[n];
-        }
+        rotate();
       }
       __builtin_amdgcn_sched_barrier(0);
       store_stage(b ^ 1, (sl + 1) % kRingN);
@@ -365,6 +382,11 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 #pragma unroll
     for (int sl = 0; sl < kRingN - 1; ++sl)
       if (kb + sl < nkb) stage(kb + sl, sl);
+    // the last stage's deferred sub-step
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[m][n] = mfma32x32x16(ac[m], bc[n], acc[m][n]);
 
     // ---- epilogue. Lane (r, h), accumulator register 4*b4 + i holds row
     // 8*b4 + 4*h + i of the 32-row weight block against token row 32*n + r
@@ -906,14 +928,188 @@ hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Dense GEMM2 of the W4A8 path, act tile resident in LDS (I <= 512): the
+// structure of gemm2_resident_kernel with the scaled 16x16x128 MFMA. A block
+// (4 waves) owns a 128-row dense tile: its MXFP8 act rows (128 x I E4M3
+// bytes) and their scales go to LDS once, then it walks all H / 256 output
+// spans. Wave wn takes 64 W2 rows per span as four 16-row tiles against the
+// eight 16-token tiles; the E2M1 weights and their E8M0 scales feed the MFMA
+// as they are, straight from global memory into registers, refilled for the
+// next span as soon as a K step is done. Token fragments are read one MFMA
+// group ahead; outputs go through the wave's LDS staging rows like the bf16
+// kernel's. LDS: 128 * I * 33 / 32 + 64 KB.
+// ---------------------------------------------------------------------------
+template <int NKB>
+__global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
+    const uint8_t* __restrict__ actq, uint32_t actq_bytes, const uint8_t* __restrict__ acts,
+    uint32_t acts_bytes, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
+    const int32_t* __restrict__ tiles, const int32_t* __restrict__ counters, int H,
+    uint16_t* __restrict__ y) {
+  constexpr int I = NKB * 128;
+  constexpr int kRowB = I;  // E4M3 act bytes per row
+  __shared__ __attribute__((aligned(16))) uint8_t a_lds[kTileRows * kRowB];
+  // act scales, [kb][row][4]: the four 32-K scale bytes of K step kb
+  __shared__ __attribute__((aligned(16))) uint8_t as_lds[NKB * kTileRows * 4];
+  __shared__ __attribute__((aligned(16))) uint8_t o_lds[4 * kTileRows * 128];
+  const int ntiles = counters[kCtrGate] == 1 ? counters[kCtrGate + 3] : 0;
+  const int xcd = blockIdx.x & 7;
+  const int per = (ntiles + 7) >> 3;
+  const int nblk_x = static_cast<int>(gridDim.x) >> 3;
+  const int t = threadIdx.x;
+  const int wn = wave_index();
+  const int lane = lane_id();
+  const int c = lane & 15, g = lane >> 4;
+  const int nspan = H >> 8;
+  constexpr uint32_t wrow = I / 2, srow = I / 32;
+  // act chunk q (16 bytes; 8 per K step) of tile row rr: within each K
+  // step's 8 chunks the index is XORed with (rr >> 1) & 7, which puts the 16
+  // rows of one MFMA fragment on 16 distinct 16-byte bank groups
+  auto a_off = [](int rr, int q) -> uint32_t {
+    return static_cast<uint32_t>(rr * kRowB + (((q & ~7) | ((q ^ (rr >> 1)) & 7)) << 4));
+  };
+  // lane's fragment bases (token c of a 16-token tile, chunks g and 4 + g of
+  // a K step); tile nt and step kb add nt * 16 * kRowB + kb * 128
+  const uint8_t* xb0 = a_lds + c * kRowB + (((g ^ (c >> 1)) & 7) << 4);
+  const uint8_t* xb1 = a_lds + c * kRowB + ((((4 + g) ^ (c >> 1)) & 7) << 4);
+  const uint8_t* sbase = as_lds + c * 4 + g;  // + (kb * 128 + nt * 16) * 4
+  const uint32_t wv_off = static_cast<uint32_t>(c) * wrow + g * 16;
+  const uint32_t sv_off = static_cast<uint32_t>(c) * srow + g;
+  for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
+    const int tile = xcd * per + slot;
+    if (tile >= ntiles) break;
+    const int4 ti = reinterpret_cast<const int4*>(tiles)[tile];
+    const int e = ti.x, row0 = ti.y, nrows = ti.z;
+    // ---- act tile and its scales -> LDS (rows past nrows read as zero)
+    {
+      const __amdgpu_buffer_rsrc_t ars = make_rsrc(actq, actq_bytes);
+      constexpr int kCh = kRowB / 16;
+      constexpr int kPer = kTileRows * kCh / 256;
+      uint4 v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int q = i * 256 + t;
+        const int rr = q / kCh, cq = q % kCh;
+        v[i] = bld16(ars, static_cast<uint32_t>(row0 + rr) * kRowB + cq * 16 +
+                              (rr < nrows ? 0u : kNoRow));
+      }
+      const __amdgpu_buffer_rsrc_t srs = make_rsrc(acts, acts_bytes);
+      for (int q = t; q < kTileRows * NKB; q += 256) {
+        const int rr = q / NKB, kb = q % NKB;
+        const uint32_t wv = bld4(srs, static_cast<uint32_t>(row0 + rr) * srow + kb * 4 +
+                                          (rr < nrows ? 0u : kNoRow));
+        *reinterpret_cast<uint32_t*>(as_lds + (kb * kTileRows + rr) * 4) = wv;
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int q = i * 256 + t;
+        const int rr = q / kCh, cq = q % kCh;
+        *reinterpret_cast<uint4*>(a_lds + a_off(rr, cq)) = v[i];
+      }
+    }
+    const __amdgpu_buffer_rsrc_t wrs =
+        make_rsrc(w2 + static_cast<size_t>(e) * H * wrow, static_cast<uint32_t>(H) * wrow);
+    const __amdgpu_buffer_rsrc_t scs =
+        make_rsrc(s2 + static_cast<size_t>(e) * H * srow, static_cast<uint32_t>(H) * srow);
+    uint4 wf[NKB][4];      // [kb][mt]: 32 E2M1 codes of row c, K block g
+    uint32_t ws[NKB][4];   // [kb][mt]: their E8M0 scale
+    auto load_w = [&](int sp, int kb) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const uint32_t rb = static_cast<uint32_t>(sp * 256 + wn * 64 + mt * 16);
+        wf[kb][mt] = bld16s(wrs, wv_off, rb * wrow + kb * 64);
+        ws[kb][mt] = bld1s(scs, sv_off, rb * srow + kb * 4);
+      }
+    };
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) load_w(0, kb);
+    __syncthreads();  // act tile visible to every wave
+
+    for (int sp = 0; sp < nspan; ++sp) {
+      f32x4_t acc[4][8];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int spn = min(sp + 1, nspan - 1);  // last span: reload it, unused
+      // step st = (kb, nt): token fragments read one step ahead
+      uint4 x0c, x1c, x0n, x1n;
+      uint32_t bsc, bsn;
+      auto read_x = [&](int st, uint4& x0, uint4& x1, uint32_t& bs) {
+        const int kb = st >> 3, nt = st & 7;
+        x0 = *reinterpret_cast<const uint4*>(xb0 + nt * 16 * kRowB + kb * 128);
+        x1 = *reinterpret_cast<const uint4*>(xb1 + nt * 16 * kRowB + kb * 128);
+        bs = sbase[(kb * kTileRows + nt * 16) * 4];
+      };
+      __builtin_amdgcn_sched_barrier(0);
+      read_x(0, x0c, x1c, bsc);
+#pragma unroll
+      for (int st = 0; st < 8 * NKB; ++st) {
+        const int kb = st >> 3, nt = st & 7;
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 < 8 * NKB) read_x(st + 1, x0n, x1n, bsn);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt][nt] = mfma_f4xf8(wf[kb][mt], ws[kb][mt], x0c, x1c, bsc, acc[mt][nt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        if (nt == 7) {  // step kb done: refill it with the next span
+          load_w(spn, kb);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        x0c = x0n;
+        x1c = x1n;
+        bsc = bsn;
+      }
+      // ---- this span's 64 x 128 outputs through the wave's LDS staging rows
+      // (token row t: 8 chunks of 8 features; chunk c8 in slot
+      // c8 ^ ((t >> 1) & 7), halves swapped when bit 4 of t is set)
+      uint8_t* stg = o_lds + wn * (kTileRows * 128);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          uint2 pk;
+          pk.x = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
+          pk.y = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
+          const int tk = nt * 16 + c;
+          const int c8 = 2 * mt + (g >> 1);
+          *reinterpret_cast<uint2*>(stg + tk * 128 + ((c8 ^ ((tk >> 1) & 7)) << 4) +
+                                    (((g & 1) ^ ((tk >> 4) & 1)) << 3)) = pk;
+        }
+      const int fbase = sp * 256 + wn * 64;
+      const __amdgpu_buffer_rsrc_t ors =
+          make_rsrc(y + static_cast<size_t>(row0) * H, static_cast<uint32_t>(nrows) * H * 2);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int tk = 8 * i + (lane >> 3);
+        const int c8 = lane & 7;
+        uint4 v = *reinterpret_cast<const uint4*>(stg + tk * 128 + ((c8 ^ ((tk >> 1) & 7)) << 4));
+        if ((tk >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
+        bst16(ors, static_cast<uint32_t>(tk) * H * 2 + (fbase + 8 * c8) * 2, v);
+      }
+    }
+    __syncthreads();  // every wave done with the act tile before the next copy
+  }
+}
+
 hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
-  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256), 1);
-  hipLaunchKernelGGL(gemm_tiled_a8_kernel<false>, dim3(grid), dim3(kTiledThreads),
-                     static_cast<size_t>(8) * a.I, st, reinterpret_cast<const uint8_t*>(a.act),
-                     static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I), a.act_scales,
-                     static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / 32), a.w2, a.s2,
-                     a.dense_tiles, a.counters, a.sorted_slot, a.I, a.H, a.Kp, 1, a.limit, nullptr,
-                     nullptr, a.y);
+  // the W4A8 path admits I <= 512 only, so the act tile always fits in LDS
+  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles), 1);
+  const uint8_t* actq = reinterpret_cast<const uint8_t*>(a.act);
+  const uint32_t qb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I);
+  const uint32_t sb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / 32);
+#define MOE_G2RA(NK)                                                                          \
+  hipLaunchKernelGGL(gemm2_resident_a8_kernel<NK>, dim3(grid), dim3(256), 0, st, actq, qb,   \
+                     a.act_scales, sb, a.w2, a.s2, a.dense_tiles, a.counters, a.H, a.y)
+  switch (a.I / 128) {
+    case 1: MOE_G2RA(1); break;
+    case 2: MOE_G2RA(2); break;
+    case 3: MOE_G2RA(3); break;
+    default: MOE_G2RA(4); break;
+  }
+#undef MOE_G2RA
   return hipGetLastError();
 }
 
