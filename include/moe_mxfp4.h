@@ -185,10 +185,11 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_shape* shape, moe_mxfp4_ws_layout
  *   topk_ids_dev       int32 [T, topk] global ids (-1 = masked), or NULL
  *   topk_w_dev         float [T, topk], or NULL (given together with ids)
  *   shared_logits_dev  bf16 [T, S] (needed when S > 0, else ignored)
- *   w13_dev            uint8 [E', 2I, H/2]: rows [0, I) gate, [I, 2I) up
- *   s13_dev            uint8 [E', 2I, H/32]
- *   w2_dev             uint8 [E', H, I/2]
- *   s2_dev             uint8 [E', H, I/32]
+ *   w13_dev            uint8 [E', 2I, H/2]: rows [0, I) gate, [I, 2I) up,
+ *                      in the packed layout of moe_mxfp4_prepack
+ *   s13_dev            uint8 [E', 2I, H/32] (row-major, not packed)
+ *   w2_dev             uint8 [E', H, I/2], packed like w13_dev
+ *   s2_dev             uint8 [E', H, I/32] (row-major, not packed)
  * Output (device): out_dev bf16 [T, H]. Tokens with no local expert get 0.
  * Workspace: workspace_dev, 256-byte aligned, >= moe_mxfp4_query's size;
  * the call overwrites it and its contents after the call are the maps
@@ -229,6 +230,27 @@ int moe_mxfp4_forward_timed(const void* x_dev, const float* router_logits_dev,
                             const uint8_t* s13_dev, const uint8_t* w2_dev, const uint8_t* s2_dev,
                             const moe_mxfp4_shape* shape, void* out_dev, void* workspace_dev,
                             uint64_t workspace_bytes, void* stream, void* const* stage_events);
+
+/*
+ * Reorder a row-major nibble-packed weight matrix (rows x row_bytes bytes,
+ * e.g. w13 as [E' * 2I, H/2] or w2 as [E' * H, I/2]) into the packed layout
+ * the forward calls read: blocks of 16 rows x 64 bytes (16 rows x 128 K
+ * elements, 1 KB each); the blocks of one 16-row group follow each other in
+ * K order, and the groups follow each other in row order. Byte b of row r
+ * moves to ((r / 16) * (row_bytes / 64) + b / 64) * 1024 + (r % 16) * 64 + b % 64.
+ * The same bytes, only moved: a one-time step when weights are loaded,
+ * like the repack the Marlin MoE kernel page describes for its weights, so
+ * that every 16-lane weight load of the GEMMs reads 1 KB of contiguous
+ * memory instead of 64 bytes from each of 16 rows.
+ *
+ * w_dev and w_packed_dev: device buffers of rows * row_bytes bytes, 16-byte
+ * aligned, not overlapping; the caller owns both. Enqueued on `stream`.
+ * Errors: MOE_ERR_INVALID (null or overlapping pointers, misalignment,
+ * rows or row_bytes not positive), MOE_ERR_UNSUPPORTED (rows % 16 != 0 or
+ * row_bytes % 64 != 0), MOE_ERR_HIP (launch failure).
+ */
+int moe_mxfp4_prepack(const uint8_t* w_dev, uint8_t* w_packed_dev, int64_t rows,
+                      int64_t row_bytes, void* stream);
 
 /* Static text for a return code. */
 const char* moe_mxfp4_strerror(int code);

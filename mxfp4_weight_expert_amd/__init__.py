@@ -12,7 +12,7 @@ import os
 from dataclasses import dataclass
 
 __all__ = ["Shape", "query", "workspace_layout", "forward", "forward_timed", "strerror", "lib_path",
-           "MoeError", "read_maps", "ADTYPE", "GEMM2_PATH", "load_library"]
+           "MoeError", "read_maps", "ADTYPE", "GEMM2_PATH", "load_library", "prepack"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoe_mxfp4.so")
@@ -71,6 +71,8 @@ def load_library():
     lib.moe_mxfp4_forward.restype = ctypes.c_int
     lib.moe_mxfp4_forward_timed.argtypes = lib.moe_mxfp4_forward.argtypes + [ctypes.c_void_p]
     lib.moe_mxfp4_forward_timed.restype = ctypes.c_int
+    lib.moe_mxfp4_prepack.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
+    lib.moe_mxfp4_prepack.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -154,11 +156,37 @@ def _call(fn, x, w13, s13, w2, s2, shape, router_logits, topk_ids, topk_w, share
     return out
 
 
+def prepack(w, rows: int = None, out=None, stream=None):
+    """Weights in the packed layout the forward calls read (moe_mxfp4_prepack).
+
+    w: contiguous uint8 device tensor, a row-major matrix of `rows` rows
+    (default: the product of all but the last dimension) of nibble-packed
+    E2M1 codes, e.g. w13 [E', 2I, H/2] or w2 [E', H, I/2]. Returns a new
+    tensor of the same shape (or fills `out`)."""
+    import torch
+
+    if not w.is_contiguous() or w.dtype != torch.uint8:
+        raise ValueError("w must be a contiguous uint8 tensor")
+    row_bytes = w.shape[-1]
+    if rows is None:
+        rows = w.numel() // row_bytes
+    if out is None:
+        out = torch.empty_like(w)
+    if stream is None:
+        stream = torch.cuda.current_stream(w.device).cuda_stream
+    rc = load_library().moe_mxfp4_prepack(_ptr(w), _ptr(out), ctypes.c_int64(rows),
+                                          ctypes.c_int64(row_bytes), ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_mxfp4_prepack")
+    return out
+
+
 def forward(x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=None, topk_w=None,
             shared_logits=None, out=None, workspace=None, stream=None):
     """Run the layer; returns out (bf16 [T, H]).
 
-    x bf16 [T, H]; w13/s13/w2/s2 uint8 as in the C header; router_logits
+    x bf16 [T, H]; w13/s13/w2/s2 uint8 as in the C header (w13 and w2 in
+    the packed layout of prepack); router_logits
     float32 [T, E_global] or (topk_ids int32 [T, topk], topk_w float32
     [T, topk]); shared_logits bf16 [T, S]. workspace: a uint8 CUDA tensor of
     at least query(shape) bytes (allocated here when None). All tensors must

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmoe_mxfp4.so")
 SOURCES = ["api.hip", "route.hip", "sort.hip", "quant.hip", "gemm.hip", "gemm_tiled.hip",
-           "finalize.hip"]
+           "finalize.hip", "pack.hip"]
 ARCH = "gfx950"
 
 

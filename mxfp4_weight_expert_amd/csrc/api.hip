@@ -108,6 +108,25 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_shape* shape, moe_mxfp4_ws_layout
   return MOE_OK;
 }
 
+int moe_mxfp4_prepack(const uint8_t* w_dev, uint8_t* w_packed_dev, int64_t rows,
+                      int64_t row_bytes, void* stream) {
+  if (w_dev == nullptr || w_packed_dev == nullptr || rows <= 0 || row_bytes <= 0)
+    return MOE_ERR_INVALID;
+  if ((reinterpret_cast<uintptr_t>(w_dev) & 15) != 0 ||
+      (reinterpret_cast<uintptr_t>(w_packed_dev) & 15) != 0)
+    return MOE_ERR_INVALID;
+  if (rows % 16 != 0 || row_bytes % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows > (int64_t{1} << 40) / row_bytes) return MOE_ERR_UNSUPPORTED;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w_dev);
+  const uintptr_t b = reinterpret_cast<uintptr_t>(w_packed_dev);
+  const uintptr_t n = static_cast<uintptr_t>(rows * row_bytes);
+  if (a < b + n && b < a + n) return MOE_ERR_INVALID;
+  return moe::launch_prepack(w_dev, w_packed_dev, rows, row_bytes,
+                             static_cast<hipStream_t>(stream)) == hipSuccess
+             ? MOE_OK
+             : MOE_ERR_HIP;
+}
+
 const char* moe_mxfp4_strerror(int code) {
   switch (code) {
     case MOE_OK: return "ok";

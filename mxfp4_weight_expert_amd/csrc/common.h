@@ -213,6 +213,13 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
 // ------------------------------------------------------------ buffer access
 // Raw buffer loads and stores return zero / are dropped for offsets at or
 // beyond the descriptor's size, without touching memory.
+// Packed weight layout (moe_mxfp4_prepack): 1 KB blocks of 16 rows x 64
+// bytes, the blocks of a 16-row group in K order. A lane's 16-byte piece at
+// byte b of row r (r % 16 = rr, 16-aligned row r0 = r - rr) sits at
+// (r0 / 16) * nks * 1024 + (b / 64) * 1024 + rr * 64 + b % 64, nks = row
+// bytes / 64: a 16-row group is nks KB, a 64-byte K step 1 KB.
+constexpr uint32_t kPkBlock = 1024;
+
 constexpr uint32_t kNoRow = 0x80000000u;  // buffer offset beyond any operand (< 2 GiB)
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
@@ -229,6 +236,10 @@ __device__ __forceinline__ uint4 bld16s(__amdgpu_buffer_rsrc_t r, uint32_t off, 
 __device__ __forceinline__ void bst16(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r,
                                          off, 0, 0);
+}
+__device__ __forceinline__ void bst16s(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t soff, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r,
+                                         off, soff, 0);
 }
 __device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, v), r,

@@ -71,7 +71,7 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + d * 256 + j * 16);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + d * 64);
+    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int last = nkb - 1;
@@ -98,7 +98,7 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + nk * 256 + j * 16);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + nk * 64);
+    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + nk * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   };
   // The first ring cycle is peeled: the loop is then entered with loads
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     const uint8_t* sg = s13 + row0 * srow;
     wave_copy_to_lds(my, sg, blk);
     wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
-    const uint8_t* wp = w13 + (row0 + r) * wrow + g * 16;
+    const uint8_t* wp = w13 + row0 * wrow + r * 64 + g * 16;  // packed layout
     uint32_t boff[NSMAX];
 #pragma unroll
     for (int s = 0; s < NSMAX; ++s) {
@@ -236,7 +236,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * H + h0;
     wave_copy_to_lds(my, s2 + row0 * srow, blk);
-    const uint8_t* wp = w2 + (row0 + r) * wrow + g * 16;
+    const uint8_t* wp = w2 + row0 * wrow + r * 64 + g * 16;  // packed layout
     // chunk-relative buffers: rows past the chunk's end read 0 / drop stores
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * H + h0 * 16 + r;
-    const uint8_t* wp = w2 + row0 * wrow + g * 16;
+    const uint8_t* wp = w2 + (row0 - r) * wrow + r * 64 + g * 16;  // packed layout
     const uint8_t* sp = s2 + row0 * srow;
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
     for (int a = 0; a < kStreamAhead; ++a) {
       const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
       sc[a] = ld16(sp + ti * sstride);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
         sc[a] = ld16(sp + ti * sstride);
         res[a].x = pack_bf16x2(acc[0], acc[1]);
         res[a].y = pack_bf16x2(acc[2], acc[3]);
@@ -398,7 +398,7 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
     xb[d][1] = bld16(xrs, xoff + d * 128 + 64);
     xsb[d] = bld1(srs, soff + d * 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + d * 64);
+    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int last = nkb - 1;
@@ -412,7 +412,7 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
     xb[d][1] = bld16(xrs, xoff + nk * 128 + 64);
     xsb[d] = bld1(srs, soff + nk * 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + nk * 64);
+    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + nk * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   };
 #pragma unroll
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     const uint8_t* sg = s13 + row0 * srow;
     wave_copy_to_lds(my, sg, blk);
     wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
-    const uint8_t* wp = w13 + (row0 + r) * wrow + g * 16;
+    const uint8_t* wp = w13 + row0 * wrow + r * 64 + g * 16;  // packed layout
     const bool valid = r < nrows;
     const uint32_t tok = static_cast<uint32_t>(sorted_slot[r0 + min(r, nrows - 1)] / Kp);
     const uint32_t xoff = valid ? tok * static_cast<uint32_t>(H) + g * 16 : kNoRow;
@@ -531,7 +531,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * H + h0 * 16 + r;
-    const uint8_t* wp = w2 + row0 * wrow + g * 16;
+    const uint8_t* wp = w2 + (row0 - r) * wrow + r * 64 + g * 16;  // packed layout
     const uint8_t* sp = s2 + row0 * srow;
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc(actq + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I);
@@ -557,7 +557,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
     for (int a = 0; a < kStreamAhead; ++a) {
       const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
       sc[a] = ld16(sp + ti * sstride);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -574,7 +574,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * 64);
+        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
         sc[a] = ld16(sp + ti * sstride);
         res[a].x = pack_bf16x2(acc[0], acc[1]);
         res[a].y = pack_bf16x2(acc[2], acc[3]);

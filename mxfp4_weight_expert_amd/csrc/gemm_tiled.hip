@@ -187,7 +187,9 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     const __amdgpu_buffer_rsrc_t scs =
         make_rsrc(s + static_cast<size_t>(e) * erows * srow, static_cast<uint32_t>(erows * srow));
     // tile rows 128i + wr stand for expert rows erow_of(wr) + wstep * i
-    const uint32_t woff = erow_of(wr) * static_cast<uint32_t>(wrow) + wc * 16;
+    // packed layout: 16-row groups of wrow * 16 bytes, 1 KB per 64-byte K step
+    const uint32_t er = erow_of(wr);
+    const uint32_t woff = (er & ~15u) * static_cast<uint32_t>(wrow) + (er & 15u) * 64 + wc * 16;
     const uint32_t wstep = (G1 ? 64u : 128u) * static_cast<uint32_t>(wrow);
     uint32_t soff[kScPer];
     int srho[kScPer];
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) tv[sl][i] = bld16s(srs, toff[i], kb * 256);
 #pragma unroll
-      for (int i = 0; i < kWPer; ++i) wv[sl][i] = bld16s(wrs, woff, kb * 64 + i * wstep);
+      for (int i = 0; i < kWPer; ++i) wv[sl][i] = bld16s(wrs, woff, kb * kPkBlock + i * wstep);
     };
     auto load_group = [&](int g) {
 #pragma unroll
@@ -483,7 +485,9 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
 #pragma unroll
   for (int s8 = 0; s8 < 8; ++s8)
     abase[s8] = a_lds + r * 4 * kRowB + ((((8 * (s8 >> 2) + 4 * h + (s8 & 3)) ^ row_swz(r)) & 15) << 4);
-  const uint32_t wv_off = static_cast<uint32_t>(r) * wrow + h * 16;
+  // packed layout: lane row r of a 32-row block lies in 16-row group r / 16
+  const uint32_t wv_off =
+      static_cast<uint32_t>(r >> 4) * 16 * wrow + static_cast<uint32_t>(r & 15) * 64 + h * 16;
   const uint32_t sv_off = static_cast<uint32_t>(r) * srow;
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
     const int tile = xcd * per + slot;
@@ -522,7 +526,8 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
       for (int m = 0; m < 2; ++m) {
         const uint32_t rb = static_cast<uint32_t>(sp * 256 + wn * 64 + m * 32);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) wr[kb][m][q] = bld16s(wrs, wv_off, rb * wrow + kb * 64 + q * 32);
+        for (int q = 0; q < 2; ++q)
+          wr[kb][m][q] = bld16s(wrs, wv_off, rb * wrow + kb * kPkBlock + q * 32);
         sw[kb][m] = bld4s(scs, sv_off, rb * srow + kb * 4);
       }
     };
@@ -793,7 +798,10 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
     const int wc = t & 3, wr = t >> 2;
     const uint8_t* wsrc[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) wsrc[i] = w + grow_of(i * 128 + wr) * wrow + wc * 16;
+    for (int i = 0; i < 2; ++i) {  // packed layout
+      const size_t gr = grow_of(i * 128 + wr);
+      wsrc[i] = w + (gr & ~static_cast<size_t>(15)) * wrow + (gr & 15) * 64 + wc * 16;
+    }
 
     const int nkb = K >> 7;
     const int last = nkb - 1;
@@ -804,7 +812,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
       for (int i = 0; i < 2; ++i) tv[i] = bld16(srs, toff[i] + kb * 128);
       sv = bld4(ssc, soff + kb * 4);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * 64);
+      for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * kPkBlock);
     };
     auto store_stage = [&](int b) {
       uint8_t* tb = tok_lds + b * kTok8Stage;
@@ -973,7 +981,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
   const uint8_t* xb0 = a_lds + c * kRowB + (((g ^ (c >> 1)) & 7) << 4);
   const uint8_t* xb1 = a_lds + c * kRowB + ((((4 + g) ^ (c >> 1)) & 7) << 4);
   const uint8_t* sbase = as_lds + c * 4 + g;  // + (kb * 128 + nt * 16) * 4
-  const uint32_t wv_off = static_cast<uint32_t>(c) * wrow + g * 16;
+  const uint32_t wv_off = static_cast<uint32_t>(c) * 64 + g * 16;  // packed layout
   const uint32_t sv_off = static_cast<uint32_t>(c) * srow + g;
   for (int slot = blockIdx.x >> 3; slot < per; slot += nblk_x) {
     const int tile = xcd * per + slot;
@@ -1017,7 +1025,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const uint32_t rb = static_cast<uint32_t>(sp * 256 + wn * 64 + mt * 16);
-        wf[kb][mt] = bld16s(wrs, wv_off, rb * wrow + kb * 64);
+        wf[kb][mt] = bld16s(wrs, wv_off, rb * wrow + kb * kPkBlock);
         ws[kb][mt] = bld1s(scs, sv_off, rb * srow + kb * 4);
       }
     };

@@ -80,5 +80,7 @@ struct FinalizeArgs {
   uint16_t* out;
 };
 hipError_t launch_finalize(const FinalizeArgs& a, hipStream_t st);
+hipError_t launch_prepack(const uint8_t* src, uint8_t* dst, int64_t rows, int64_t row_bytes,
+                          hipStream_t st);
 
 }  // namespace moe

@@ -36,9 +36,9 @@ def bf16_dev(bits: np.ndarray) -> torch.Tensor:
 def to_device(s: LayerShape, inp: dict) -> dict:
     d = {
         "x": bf16_dev(inp["x"]),
-        "w13": torch.from_numpy(inp["w13"]).cuda(),
+        "w13": moe.prepack(torch.from_numpy(inp["w13"]).cuda()),
         "s13": torch.from_numpy(inp["s13"]).cuda(),
-        "w2": torch.from_numpy(inp["w2"]).cuda(),
+        "w2": moe.prepack(torch.from_numpy(inp["w2"]).cuda()),
         "s2": torch.from_numpy(inp["s2"]).cuda(),
         "shared": bf16_dev(inp["shared"]) if s.S > 0 else None,
     }

@@ -25,8 +25,8 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     lib = moe.load_library()
     names = _declared_functions()
-    assert names == ["moe_mxfp4_forward", "moe_mxfp4_forward_timed", "moe_mxfp4_query",
-                     "moe_mxfp4_strerror", "moe_mxfp4_workspace_layout"]
+    assert names == ["moe_mxfp4_forward", "moe_mxfp4_forward_timed", "moe_mxfp4_prepack",
+                     "moe_mxfp4_query", "moe_mxfp4_strerror", "moe_mxfp4_workspace_layout"]
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", moe.lib_path], capture_output=True, text=True)
@@ -114,6 +114,23 @@ def test_forward_rejects_before_launch():
     assert _fwd(_shape(S=1), shared=None) == 1           # shared experts need logits
     assert _fwd(_shape(H=100)) == 2
     assert _fwd(_shape(T=0), ws=None) == 0               # empty call: nothing to do
+
+
+def test_prepack_rejects_before_launch():
+    lib = moe.load_library()
+    P = ctypes.c_void_p
+
+    def pk(src, dst, rows, row_bytes):
+        return lib.moe_mxfp4_prepack(P(src) if src else None, P(dst) if dst else None,
+                                     ctypes.c_int64(rows), ctypes.c_int64(row_bytes), None)
+
+    assert pk(None, 1 << 20, 16, 64) == 1                # null source
+    assert pk(1 << 20, None, 16, 64) == 1                # null destination
+    assert pk(1 << 20, (1 << 20) + 8, 16, 64) == 1       # misaligned destination
+    assert pk(1 << 20, (1 << 20) + 512, 16, 64) == 1     # overlapping buffers
+    assert pk(1 << 20, 1 << 24, 0, 64) == 1              # no rows
+    assert pk(1 << 20, 1 << 24, 8, 64) == 2              # rows not a multiple of 16
+    assert pk(1 << 20, 1 << 24, 16, 48) == 2             # row bytes not a multiple of 64
 
 
 def test_strerror():

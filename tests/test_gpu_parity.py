@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import oracle
+import mxfp4_weight_expert_amd as moe
 from workloads import CONFIGS, CONFIG_ORDER, LayerShape, config_seed, make_inputs
 
 from gpu_util import bf16_dev, check_maps, check_out, maps_np, out_np, run, say, to_device
@@ -217,3 +218,15 @@ def test_large_sort_maps(s):
         check_maps(s, maps_np(s, ws, force), ref)
         toks = _sample_tokens(s.T, 4, 5)
         check_out(out_np(out)[toks], oracle.sampled_forward(s, inp, toks), f"{s.name}/{force}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,row_bytes", [(16, 64), (48, 192), (256, 1792), (768, 1792)])
+def test_prepack_layout(rows, row_bytes):
+    """Prepacked weights: block (row group g, K step k) holds rows 16g..16g+15,
+    bytes 64k..64k+63 of the row-major matrix, row-major inside the block."""
+    rng = np.random.default_rng(rows + row_bytes)
+    w = rng.integers(0, 256, size=(rows, row_bytes), dtype=np.uint8)
+    got = moe.prepack(torch.from_numpy(w).cuda()).cpu().numpy().reshape(-1)
+    want = w.reshape(rows // 16, 16, row_bytes // 64, 64).transpose(0, 2, 1, 3).reshape(-1)
+    assert np.array_equal(got, want)
