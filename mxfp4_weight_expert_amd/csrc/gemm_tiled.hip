@@ -854,19 +854,37 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
       const uint8_t* wb = w_lds + b * kWStage;
       uint4 af[4];
       uint32_t as[4];
+      // token fragments of tile nt + 1 are read while tile nt's MFMAs run
+      uint4 x0c, x1c, x0n, x1n;
+      uint32_t bsc, bsn;
+      auto read_x = [&](int nt, uint4& x0, uint4& x1, uint32_t& bs) {
+        const int tr = wm * 64 + nt * 16 + c;
+        x0 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, g));
+        x1 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, 4 + g));
+        bs = tsb[tr * 4 + g];
+      };
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         af[mt] = *reinterpret_cast<const uint4*>(wb + w_off(rho[mt], g));
         as[mt] = s_lds[rho[mt] * srow + kb * 4 + g];
       }
+      read_x(0, x0c, x1c, bsc);
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
-        const int tr = wm * 64 + nt * 16 + c;
-        const uint4 x0 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, g));
-        const uint4 x1 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, 4 + g));
-        const uint32_t bs = tsb[tr * 4 + g];
+        __builtin_amdgcn_sched_barrier(0);
+        if (nt < 3) read_x(nt + 1, x0n, x1n, bsn);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) acc[mt][nt] = mfma_f4xf8(af[mt], as[mt], x0, x1, bs, acc[mt][nt]);
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt][nt] = mfma_f4xf8(af[mt], as[mt], x0c, x1c, bsc, acc[mt][nt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
+        __builtin_amdgcn_sched_barrier(0);
+        if (nt < 3) {
+          x0c = x0n;
+          x1c = x1n;
+          bsc = bsn;
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       store_stage(b ^ 1);
