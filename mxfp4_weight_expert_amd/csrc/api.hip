@@ -6,6 +6,7 @@
 // buffer, 256-byte aligned pieces, padding rows after the last chunk); the
 // shape limits are this library's own (the page's static_asserts fix
 // H % 512 and I % 128, which are kept).
+#include <algorithm>
 #include <cmath>
 
 #include "common.h"
@@ -228,6 +229,17 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   ga.B = s.block_n;
   ga.kmax_v = L.kmax_v;
   ga.max_dense_tiles = L.max_dense_tiles;
+  {
+    // The gate picks the dense path only when R >= 64 U, so it then has at
+    // most R / 128 + U <= R_max / 128 + R_max / 64 tiles: a decode shape
+    // launches a small dense grid that exits at once. A forced dense path
+    // can have up to max_dense_tiles.
+    const int64_t rmax = static_cast<int64_t>(s.T) * (s.topk + s.S);
+    const int64_t bound = rmax / 128 + rmax / 64 + 1;
+    ga.dense_grid_tiles = s.force_gemm2_path == MOE_GEMM2_AUTO
+                              ? static_cast<int>(std::min<int64_t>(L.max_dense_tiles, bound))
+                              : L.max_dense_tiles;
+  }
   ga.max_units16 = L.max_units16;
   ga.limit = s.swiglu_limit;
   ga.act = reinterpret_cast<uint16_t*>(at(L.act));

@@ -676,7 +676,7 @@ hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
   if (a.I <= 384) {  // act tile (128 x I bf16) and the weight registers fit
-    const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles), 1);
+    const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles), 1);
     const uint32_t act_bytes = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2);
 #define MOE_G2R(NK)                                                                        \
   hipLaunchKernelGGL(gemm2_resident_kernel<NK>, dim3(grid), dim3(kResThreads), 0, st,     \
@@ -689,7 +689,7 @@ hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
 #undef MOE_G2R
     return hipGetLastError();
   }
-  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles) * (a.H / 256), 1);
+  const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles) * (a.H / 256), 1);
   hipLaunchKernelGGL((gemm_tiled_kernel<false, 2>), dim3(grid), dim3(kTiledThreads), 0, st, a.act,
                      static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2), a.w2, a.s2,
                      a.dense_tiles, a.counters, a.sorted_slot, a.I, a.H, a.Kp, 1, a.limit, a.y);
@@ -1122,7 +1122,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
 
 hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
   // the W4A8 path admits I <= 512 only, so the act tile always fits in LDS
-  const int grid = tiled_grid(static_cast<long>(a.max_dense_tiles), 1);
+  const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles), 1);
   const uint8_t* actq = reinterpret_cast<const uint8_t*>(a.act);
   const uint32_t qb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I);
   const uint32_t sb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / 32);

@@ -47,6 +47,7 @@ struct GemmArgs {
   const int32_t* counters;
   const int32_t* sorted_slot;
   int T, H, I, Kp, B, kmax_v, max_dense_tiles, max_units16, rows_pad;
+  int dense_grid_tiles;  // tiles the dense GEMM2 grid is sized for (the kernels loop past it)
   float limit;
   uint16_t* act;  // [rows_pad, I] bf16 (W4A16), or E4M3 codes (W4A8)
   uint16_t* y;    // [rows_pad, H] bf16
