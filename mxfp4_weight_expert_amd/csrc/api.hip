@@ -220,6 +220,7 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   ga.units16 = sa.units16;
   ga.dense_tiles = sa.dense_tiles;
   ga.counters = sa.counters;
+  ga.counts = sa.counts;
   ga.sorted_slot = sa.sorted_slot;
   ga.T = s.T;
   ga.rows_pad = L.rows_pad;

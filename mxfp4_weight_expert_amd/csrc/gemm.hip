@@ -53,11 +53,12 @@ __device__ __forceinline__ void wave_copy_to_lds(uint8_t* lds, const uint8_t* sr
 // wofs[t] bytes further (wave-uniform). ls: lane's scale row in LDS, offset by
 // g; tile t is lofs[t] bytes further. brs/boff[s]: buffer and byte offset of
 // the lane's row of sub-tile s plus g*64 bytes (kNoRow for lanes past the
-// chunk's end). Each decoded weight fragment feeds all NS sub-tiles.
+// chunk's end). Each decoded weight fragment feeds all NS sub-tiles. NTW:
+// the weights are read once in this call (non-temporal loads).
 // D divides nkb, so the unrolled body has no tail branches: the
 // vector-memory counter retires loads in issue order, and straight-line code
 // lets every wait cover only the step it needs.
-template <int D, int NS, int NT = 4>
+template <bool NTW, int D, int NS, int NT = 4>
 __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (&wofs)[NT],
                                              const uint8_t* ls, const uint32_t (&lofs)[NT], int nkb,
                                              __amdgpu_buffer_rsrc_t brs, const uint32_t (&boff)[NS],
@@ -71,7 +72,7 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + d * 256 + j * 16);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + d * kPkBlock);
+    for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int last = nkb - 1;
@@ -98,7 +99,7 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 #pragma unroll
       for (int j = 0; j < 4; ++j) xb[d][s][j] = bld16(brs, boff[s] + nk * 256 + j * 16);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) w[d][t] = ld16(wp + wofs[t] + nk * kPkBlock);
+    for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + nk * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   };
   // The first ring cycle is peeled: the loop is then entered with loads
@@ -129,12 +130,14 @@ inline int ring_depth(int nkb) {
 // weights are streamed once per chunk; a wider feature group cuts how often
 // the chunk's token rows are re-read (once per group). Dynamic LDS: 4 waves
 // x TP * H bytes (the group's gate and up scale rows). `units`/`ctr`: the
-// chunk table and the counter word holding its length.
+// chunk table and the counter word holding its length; `counts`: rows per
+// expert (an expert of at most 16 * NSMAX rows has its weights read once).
 template <int D, int NSMAX, int TP>
 __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
-    const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int T, int H,
+    const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ sorted_slot, int T, int H,
     int I, int Kp, float limit, uint16_t* __restrict__ act) {
   constexpr int NT = 2 * TP;
   extern __shared__ uint8_t lds_scales[];
@@ -165,6 +168,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     wave_copy_to_lds(my, sg, blk);
     wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
     const uint8_t* wp = w13 + row0 * wrow + r * 64 + g * 16;  // packed layout
+    const bool once = counts[e] <= 16 * NSMAX;  // the expert's only chunk
     uint32_t boff[NSMAX];
 #pragma unroll
     for (int s = 0; s < NSMAX; ++s) {
@@ -192,7 +196,10 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint32_t b1[1] = {boff[0]};
-      stream_block<D, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1, acc);
+      auto run = [&](auto ntw) {
+        stream_block<decltype(ntw)::value, D, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1, acc);
+      };
+      if (once) run(BoolC<true>{}); else run(BoolC<false>{});
       store(acc[0], 0);
     } else {
       f32x4_t acc[NSMAX][NT];
@@ -200,7 +207,11 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
       for (int s = 0; s < NSMAX; ++s)
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      stream_block<D, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, boff, acc);
+      auto run = [&](auto ntw) {
+        stream_block<decltype(ntw)::value, D, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs,
+                                                         boff, acc);
+      };
+      if (once) run(BoolC<true>{}); else run(BoolC<false>{});
 #pragma unroll
       for (int s = 0; s < NSMAX; ++s) store(acc[s], s);
     }
@@ -214,7 +225,8 @@ template <int D, int NSMAX>
 __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int32_t* __restrict__ units, int ctr,
-    const int32_t* __restrict__ counters, int H, int I, uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ counters, const int32_t* __restrict__ counts, int H, int I,
+    uint16_t* __restrict__ y) {
   if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
   extern __shared__ uint8_t lds_scales[];
   const int lane = lane_id();
@@ -237,6 +249,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     const size_t row0 = static_cast<size_t>(e) * H + h0;
     wave_copy_to_lds(my, s2 + row0 * srow, blk);
     const uint8_t* wp = w2 + row0 * wrow + r * 64 + g * 16;  // packed layout
+    const bool once = counts[e] <= 16 * NSMAX;  // the expert's only chunk
     // chunk-relative buffers: rows past the chunk's end read 0 / drop stores
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
@@ -260,7 +273,10 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint32_t b1[1] = {boff[0]};
-      stream_block<D, 1>(wp, wofs, my + r * srow + g, lofs, nkb, ars, b1, acc);
+      auto run = [&](auto ntw) {
+        stream_block<decltype(ntw)::value, D, 1>(wp, wofs, my + r * srow + g, lofs, nkb, ars, b1, acc);
+      };
+      if (once) run(BoolC<true>{}); else run(BoolC<false>{});
       store(acc[0], 0);
     } else {
       f32x4_t acc[NSMAX][4];
@@ -268,7 +284,11 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
       for (int s = 0; s < NSMAX; ++s)
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      stream_block<D, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, ars, boff, acc);
+      auto run = [&](auto ntw) {
+        stream_block<decltype(ntw)::value, D, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, ars, boff,
+                                                     acc);
+      };
+      if (once) run(BoolC<true>{}); else run(BoolC<false>{});
 #pragma unroll
       for (int s = 0; s < NSMAX; ++s) store(acc[s], s);
     }
@@ -294,7 +314,8 @@ template <int NKB>
 __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int32_t* __restrict__ units,
-    const int32_t* __restrict__ counters, int H, int I, uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ counters, const int32_t* __restrict__ counts, int H, int I,
+    uint16_t* __restrict__ y) {
   if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
@@ -328,46 +349,51 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) xa[kb][j] = bld16(ars, boff + kb * 256 + j * 16);
     __builtin_amdgcn_sched_barrier(0);
-    uint4 w[kStreamAhead][NKB];
-    uint4 sc[kStreamAhead];  // the lane row's scale bytes (I/32 <= 16)
-    // prologue in slot order (pinned): the loop head then sees the same
-    // pending-load order on entry as on every later iteration
-#pragma unroll
-    for (int a = 0; a < kStreamAhead; ++a) {
-      const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
-      sc[a] = ld16(sp + ti * sstride);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
-      uint2 res[kStreamAhead];
-#pragma unroll
+    // weights read once in this call (the expert's only unit): non-temporal
+    auto seg = [&](auto ntw) {
+      constexpr bool NTW = decltype(ntw)::value;
+      uint4 w[kStreamAhead][NKB];
+      uint4 sc[kStreamAhead];  // the lane row's scale bytes (I/32 <= 16)
+      // prologue in slot order (pinned): the loop head then sees the same
+      // pending-load order on entry as on every later iteration
+  #pragma unroll
       for (int a = 0; a < kStreamAhead; ++a) {
-        const int i = i0 + a;
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const float s = e8m0_scale_operand((sw[kb] >> (8 * g)) & 0xffu);
-          const uint32_t ww[4] = {w[a][kb].x, w[a][kb].y, w[a][kb].z, w[a][kb].w};
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc = mfma16x16x32(decode_fp4x8(ww[j], s), as_bf16x8(xa[kb][j]), acc);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
+        const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
         sc[a] = ld16(sp + ti * sstride);
-        res[a].x = pack_bf16x2(acc[0], acc[1]);
-        res[a].y = pack_bf16x2(acc[2], acc[3]);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int a = 0; a < kStreamAhead; ++a)
-        bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
-    }
+      for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
+        uint2 res[kStreamAhead];
+  #pragma unroll
+        for (int a = 0; a < kStreamAhead; ++a) {
+          const int i = i0 + a;
+          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) {
+            const float s = e8m0_scale_operand((sw[kb] >> (8 * g)) & 0xffu);
+            const uint32_t ww[4] = {w[a][kb].x, w[a][kb].y, w[a][kb].z, w[a][kb].w};
+  #pragma unroll
+            for (int j = 0; j < 4; ++j)
+              acc = mfma16x16x32(decode_fp4x8(ww[j], s), as_bf16x8(xa[kb][j]), acc);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
+          sc[a] = ld16(sp + ti * sstride);
+          res[a].x = pack_bf16x2(acc[0], acc[1]);
+          res[a].y = pack_bf16x2(acc[2], acc[3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  #pragma unroll
+        for (int a = 0; a < kStreamAhead; ++a)
+          bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
+      }
+    };
+    if (counts[e] <= 16) seg(BoolC<true>{}); else seg(BoolC<false>{});
     t += nt;
   }
 }
@@ -384,7 +410,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
 // acc[t] += W_tile_t * Xq^T over nkb steps. xrs/xoff: buffer and byte offset
 // of the lane's E4M3 row plus 16g (kNoRow past the unit's end); srs/soff:
 // the row's scale bytes plus g (kNoRow likewise).
-template <int D>
+template <bool NTW, int D>
 __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_t (&wofs)[4],
                                                 const uint8_t* ls, const uint32_t (&lofs)[4],
                                                 int nkb, __amdgpu_buffer_rsrc_t xrs, uint32_t xoff,
@@ -398,7 +424,7 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
     xb[d][1] = bld16(xrs, xoff + d * 128 + 64);
     xsb[d] = bld1(srs, soff + d * 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + d * kPkBlock);
+    for (int t = 0; t < 4; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
   const int last = nkb - 1;
@@ -412,7 +438,7 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
     xb[d][1] = bld16(xrs, xoff + nk * 128 + 64);
     xsb[d] = bld1(srs, soff + nk * 4);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) w[d][t] = ld16(wp + wofs[t] + nk * kPkBlock);
+    for (int t = 0; t < 4; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + nk * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   };
 #pragma unroll
@@ -451,8 +477,8 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const int32_t* __restrict__ units, const int32_t* __restrict__ counters,
-    const int32_t* __restrict__ sorted_slot, int T, int H, int I, int Kp, float limit,
-    uint8_t* __restrict__ actq, uint8_t* __restrict__ acts) {
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slot, int T, int H,
+    int I, int Kp, float limit, uint8_t* __restrict__ actq, uint8_t* __restrict__ acts) {
   extern __shared__ uint8_t lds_scales[];
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
@@ -486,7 +512,12 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     f32x4_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    stream_block_a8<D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff, srs, soff, acc);
+    auto run = [&](auto ntw) {
+      stream_block_a8<decltype(ntw)::value, D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff, srs,
+                                               soff, acc);
+    };
+    // weights read once in this call (the expert's only unit): non-temporal
+    if (counts[e] <= 16) run(BoolC<true>{}); else run(BoolC<false>{});
     // lane (r, g): features f0 + 16h + 4g + v of token row r0 + r
     float a[8];
 #pragma unroll
@@ -510,8 +541,8 @@ template <int NKB>
 __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
     const uint8_t* __restrict__ actq, const uint8_t* __restrict__ acts,
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
-    const int32_t* __restrict__ units, const int32_t* __restrict__ counters, int H, int I,
-    uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ units, const int32_t* __restrict__ counters,
+    const int32_t* __restrict__ counts, int H, int I, uint16_t* __restrict__ y) {
   if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
@@ -551,39 +582,44 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
       xsa[kb] = bld1(ars, aoff + kb * 4);
     }
     __builtin_amdgcn_sched_barrier(0);
-    uint4 w[kStreamAhead][NKB];
-    uint4 sc[kStreamAhead];
-#pragma unroll
-    for (int a = 0; a < kStreamAhead; ++a) {
-      const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
-      sc[a] = ld16(sp + ti * sstride);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
-      uint2 res[kStreamAhead];
-#pragma unroll
+    // weights read once in this call (the expert's only unit): non-temporal
+    auto seg = [&](auto ntw) {
+      constexpr bool NTW = decltype(ntw)::value;
+      uint4 w[kStreamAhead][NKB];
+      uint4 sc[kStreamAhead];
+  #pragma unroll
       for (int a = 0; a < kStreamAhead; ++a) {
-        const int i = i0 + a;
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          acc = mfma_f4xf8(w[a][kb], (sw[kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb], acc);
-        __builtin_amdgcn_sched_barrier(0);
-        const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ld16(wp + ti * tstride + kb * kPkBlock);
+        const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
+  #pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
         sc[a] = ld16(sp + ti * sstride);
-        res[a].x = pack_bf16x2(acc[0], acc[1]);
-        res[a].y = pack_bf16x2(acc[2], acc[3]);
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int a = 0; a < kStreamAhead; ++a)
-        bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
-    }
+      for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
+        uint2 res[kStreamAhead];
+  #pragma unroll
+        for (int a = 0; a < kStreamAhead; ++a) {
+          const int i = i0 + a;
+          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb)
+            acc = mfma_f4xf8(w[a][kb], (sw[kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb], acc);
+          __builtin_amdgcn_sched_barrier(0);
+          const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
+  #pragma unroll
+          for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
+          sc[a] = ld16(sp + ti * sstride);
+          res[a].x = pack_bf16x2(acc[0], acc[1]);
+          res[a].y = pack_bf16x2(acc[2], acc[3]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+  #pragma unroll
+        for (int a = 0; a < kStreamAhead; ++a)
+          bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
+      }
+    };
+    if (counts[e] <= 16) seg(BoolC<true>{}); else seg(BoolC<false>{});
     t += nt;
   }
 }
@@ -616,8 +652,8 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
     const size_t lds = static_cast<size_t>(4) * kTP * a.H;
 #define MOE_G1D(DD, NS)                                                                           \
   hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, kTP>), dim3(grid), dim3(kGemmBlock), lds, st,   \
-                     a.x, a.w13, a.s13, units, ctr, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp,  \
-                     a.limit, a.act)
+                     a.x, a.w13, a.s13, units, ctr, a.counters, a.counts, a.sorted_slot, a.T, a.H,   \
+                     a.I, a.Kp, a.limit, a.act)
     const int d = ring_depth(a.H / 128);
     if (c32) {
       if (d == 2) MOE_G1D(2, 2); else MOE_G1D(1, 2);
@@ -637,7 +673,7 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
     const int gstream = MOE_STREAM_GRID;
 #define MOE_G2S(NK)                                                                      \
   hipLaunchKernelGGL(gemm2_stream_kernel<NK>, dim3(gstream), dim3(kGemmBlock), 0, st,   \
-                     a.act, a.w2, a.s2, a.units16, a.counters, a.H, a.I, a.y)
+                     a.act, a.w2, a.s2, a.units16, a.counters, a.counts, a.H, a.I, a.y)
     switch (nkb2) {
       case 1: MOE_G2S(1); break;
       case 2: MOE_G2S(2); break;
@@ -653,7 +689,7 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
     const size_t lds2 = static_cast<size_t>(4) * 2 * a.I;
 #define MOE_G2D(DD, NS)                                                                         \
   hipLaunchKernelGGL((gemm2_split_kernel<DD, NS>), dim3(gsplit), dim3(kGemmBlock), lds2, st,   \
-                     a.act, a.w2, a.s2, units, ctr, a.counters, a.H, a.I, a.y)
+                     a.act, a.w2, a.s2, units, ctr, a.counters, a.counts, a.H, a.I, a.y)
     const int d = ring_depth(a.I / 128);
     if (c32) {
       if (d == 2) MOE_G2D(2, 2); else MOE_G2D(1, 2);
@@ -673,7 +709,8 @@ hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
   uint8_t* actq = reinterpret_cast<uint8_t*>(a.act);
 #define MOE_G1A(DD)                                                                              \
   hipLaunchKernelGGL(gemm1_decode_a8_kernel<DD>, dim3(grid), dim3(kGemmBlock), lds, st, a.xq,    \
-                     a.xs, a.w13, a.s13, a.units16, a.counters, a.sorted_slot, a.T, a.H, a.I, a.Kp, \
+                     a.xs, a.w13, a.s13, a.units16, a.counters, a.counts, a.sorted_slot, a.T, a.H,  \
+                     a.I, a.Kp,                                                                 \
                      a.limit, actq, a.act_scales)
   switch (ring_depth(a.H / 128)) {
     case 4: MOE_G1A(4); break;
@@ -690,7 +727,7 @@ hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st) {
   const int gstream = MOE_STREAM_GRID;
 #define MOE_G2SA(NK)                                                                       \
   hipLaunchKernelGGL(gemm2_stream_a8_kernel<NK>, dim3(gstream), dim3(kGemmBlock), 0, st,  \
-                     actq, a.act_scales, a.w2, a.s2, a.units16, a.counters, a.H, a.I, a.y)
+                     actq, a.act_scales, a.w2, a.s2, a.units16, a.counters, a.counts, a.H, a.I, a.y)
   switch (a.I / 128) {
     case 1: MOE_G2SA(1); break;
     case 2: MOE_G2SA(2); break;

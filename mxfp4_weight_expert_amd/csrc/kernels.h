@@ -45,6 +45,7 @@ struct GemmArgs {
   const int32_t* units16;
   const int32_t* dense_tiles;
   const int32_t* counters;
+  const int32_t* counts;  // [Ep] rows per local expert
   const int32_t* sorted_slot;
   int T, H, I, Kp, B, kmax_v, max_dense_tiles, max_units16, rows_pad;
   int dense_grid_tiles;  // tiles the dense GEMM2 grid is sized for (the kernels loop past it)
