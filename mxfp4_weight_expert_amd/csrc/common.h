@@ -262,6 +262,12 @@ __device__ __forceinline__ void bst16s(__amdgpu_buffer_rsrc_t r, uint32_t off, u
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r,
                                          off, soff, 0);
 }
+// Non-temporal 16-byte buffer store (cache-policy operand 2), for data
+// written once and read once much later, past what the caches hold.
+__device__ __forceinline__ void bst16nt(__amdgpu_buffer_rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(__attribute__((ext_vector_type(4))) uint32_t, v), r,
+                                         off, 0, 2);
+}
 __device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(__attribute__((ext_vector_type(2))) uint32_t, v), r,
                                         off, 0, 0);

@@ -14,7 +14,9 @@ namespace moe {
 // Grid: T x nblk blocks; block (t, b) covers 16-byte vectors [b*256, b*256 + 256)
 // of token t's output row. Wave 0 first compacts the token's valid columns
 // (row >= 0) into LDS, keeping their order, so the accumulation loop has no
-// branches and issues its row loads back to back.
+// branches and issues its row loads back to back. Every row of y is read
+// exactly once per call, so the loads are non-temporal (at 32k tokens y is
+// 3.8 GB, far past what the caches hold: 836 -> 768 us on MI355X).
 __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restrict__ y,
                                                        const int32_t* __restrict__ expanded_idx,
                                                        const float* __restrict__ slot_w, int Kp,
@@ -54,11 +56,11 @@ __global__ __launch_bounds__(256) void finalize_kernel(const uint16_t* __restric
   for (; k + 8 <= n; k += 8) {
     uint4 v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = ld16(yc + static_cast<size_t>(s_row[k + u]) * H);
+    for (int u = 0; u < 8; ++u) v[u] = ldw16<true>(yc + static_cast<size_t>(s_row[k + u]) * H);
 #pragma unroll
     for (int u = 0; u < 8; ++u) add(v[u], s_w[k + u]);
   }
-  for (; k < n; ++k) add(ld16(yc + static_cast<size_t>(s_row[k]) * H), s_w[k]);
+  for (; k < n; ++k) add(ldw16<true>(yc + static_cast<size_t>(s_row[k]) * H), s_w[k]);
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);
   o.y = pack_bf16x2(acc[2], acc[3]);

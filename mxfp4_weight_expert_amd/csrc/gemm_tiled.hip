@@ -447,7 +447,10 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 // barrier is needed between spans. Each span's outputs pass through the
 // wave's own 16 KB of LDS so that the stores write whole 128-byte pieces of
 // Y rows (16 bytes per lane) instead of 8-byte pieces of 32 rows at a time,
-// which kept the texture address queue full. LDS: 128 * I * 2 + 64 KB.
+// which kept the texture address queue full. Y is written once and read
+// once by the finalize, after far more than the caches hold has passed
+// (3.8 GB at 32k tokens), so the stores are non-temporal. LDS: 128 * I * 2
+// + 64 KB.
 // ---------------------------------------------------------------------------
 constexpr int kResThreads = 256;
 
@@ -640,7 +643,7 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
         const int c = lane & 7;
         uint4 v = *reinterpret_cast<const uint4*>(stg + tk * 128 + ((c ^ ((tk >> 1) & 7)) << 4));
         if ((tk >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-        bst16(ors, static_cast<uint32_t>(tk) * H * 2 + (fbase + 8 * c) * 2, v);
+        bst16nt(ors, static_cast<uint32_t>(tk) * H * 2 + (fbase + 8 * c) * 2, v);
       }
     }
     __syncthreads();  // every wave done with the act tile before the next copy
@@ -1113,7 +1116,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
         const int c8 = lane & 7;
         uint4 v = *reinterpret_cast<const uint4*>(stg + tk * 128 + ((c8 ^ ((tk >> 1) & 7)) << 4));
         if ((tk >> 4) & 1) v = make_uint4(v.z, v.w, v.x, v.y);
-        bst16(ors, static_cast<uint32_t>(tk) * H * 2 + (fbase + 8 * c8) * 2, v);
+        bst16nt(ors, static_cast<uint32_t>(tk) * H * 2 + (fbase + 8 * c8) * 2, v);
       }
     }
     __syncthreads();  // every wave done with the act tile before the next copy
