@@ -227,6 +227,7 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   ga.H = s.H;
   ga.I = s.I;
   ga.Kp = Kp;
+  ga.Ep = Ep;
   ga.B = s.block_n;
   ga.kmax_v = L.kmax_v;
   ga.max_dense_tiles = L.max_dense_tiles;

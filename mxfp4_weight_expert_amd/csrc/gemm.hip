@@ -113,6 +113,95 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
   }
 }
 
+// Token tile of one K step in LDS, shared by the four waves of a block
+// (they work on the same chunk): up to 32 rows x 256 bytes. 16-byte chunk c
+// of tile row rr sits at rr * 256 + 16 * (c ^ tswz(rr)): the 32 lanes that
+// read one fragment (rows r = 0..15, chunks 4g + j, g = 0..1) and the 32
+// lanes that write two rows fall on distinct 16-byte bank groups of a
+// 512-byte bank line.
+constexpr int kTokLdsStep = 32 * 256;
+__device__ __forceinline__ uint32_t tswz(int rr) {
+  const uint32_t m = static_cast<uint32_t>(rr >> 1) & 7u;
+  return (m & 3u) | ((m & 4u) << 1);
+}
+__device__ __forceinline__ uint32_t tlds_off(int rr, int c) {
+  return static_cast<uint32_t>(rr * 256) + ((static_cast<uint32_t>(c) ^ tswz(rr)) << 4);
+}
+
+// stream_block with the token fragments read from a block-shared LDS tile
+// (two buffers of kTokLdsStep at tl) instead of per-wave loads, so a token
+// row is fetched once per block and K step instead of once per wave. Every
+// wave of the block must call it with the same nkb and NS: one barrier per
+// K step. Thread t loads 16-byte chunk t % 16 of tile rows t / 16 + 16 i
+// (i < NS) from trs at toff[i] (out of range past the chunk's end, which
+// reads zero), D = 2 steps ahead like the weights, and stores it to the
+// other LDS buffer one step before it is read.
+template <bool NTW, int NS, int NT = 4>
+__device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32_t (&wofs)[NT],
+                                                 const uint8_t* ls, const uint32_t (&lofs)[NT],
+                                                 int nkb, __amdgpu_buffer_rsrc_t trs,
+                                                 const uint32_t (&toff)[NS], uint8_t* tl,
+                                                 f32x4_t (&acc)[NS][NT]) {
+  constexpr int D = 2;
+  const int lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
+  uint4 w[D][NT], tv[D][NS];
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) tv[d][i] = bld16(trs, toff[i] + d * 256);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) *reinterpret_cast<uint4*>(tl + tlds_off(lr + 16 * i, lc)) = tv[0][i];
+  __syncthreads();
+  const int last = nkb - 1;
+  auto step = [&](int kb, int d) {
+    const uint8_t* tb = tl + (kb & 1) * kTokLdsStep;
+    uint4 xb[NS][4];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xb[s][j] = *reinterpret_cast<const uint4*>(tb + tlds_off(16 * s + r, 4 * g + j));
+    float sc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) sc[t] = e8m0_scale_operand(ls[lofs[t] + kb * 4]);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t ww[4] = {w[d][t].x, w[d][t].y, w[d][t].z, w[d][t].w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16x8_t a = decode_fp4x8(ww[j], sc[t]);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) acc[s][t] = mfma16x16x32(a, as_bf16x8(xb[s][j]), acc[s][t]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // step kb + 1's tile (loaded one step ago) into the buffer read in step
+    // kb - 1, which every wave left before the last barrier
+    uint8_t* nb = tl + ((kb + 1) & 1) * kTokLdsStep;
+#pragma unroll
+    for (int i = 0; i < NS; ++i) *reinterpret_cast<uint4*>(nb + tlds_off(lr + 16 * i, lc)) = tv[(d + 1) % D][i];
+    const int nk = min(kb + D, last);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) tv[d][i] = bld16(trs, toff[i] + nk * 256);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + nk * kPkBlock);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) step(d, d);
+  for (int kb0 = D; kb0 < nkb; kb0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(kb0 + d, d);
+  }
+}
+
 #ifndef MOE_MAX_RING_DEPTH
 #define MOE_MAX_RING_DEPTH 2
 #endif
@@ -132,7 +221,10 @@ inline int ring_depth(int nkb) {
 // x TP * H bytes (the group's gate and up scale rows). `units`/`ctr`: the
 // chunk table and the counter word holding its length; `counts`: rows per
 // expert (an expert of at most 16 * NSMAX rows has its weights read once).
-template <int D, int NSMAX, int TP>
+// TL: token tiles shared through LDS (stream_block_lds, D = 2); the dynamic
+// LDS then starts with the two token buffers. The four waves of a block
+// always hold items of the same chunk (groups is a multiple of 4).
+template <int D, int NSMAX, int TP, bool TL>
 __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
@@ -148,8 +240,10 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
   const int nkb = H >> 7;
   const int blk = 16 * TP * static_cast<int>(srow);  // the group's gate (or up) scale rows
-  uint8_t* my = lds_scales + wave_index() * 2 * blk;
+  uint8_t* tl = lds_scales;
+  uint8_t* my = lds_scales + (TL ? 2 * kTokLdsStep : 0) + wave_index() * 2 * blk;
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(T) * H * 2));
+  const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
   uint32_t wofs[NT], lofs[NT];
 #pragma unroll
   for (int p = 0; p < TP; ++p) {
@@ -176,6 +270,15 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
       const int tok = sorted_slot[r0 + min(rr, nrows - 1)] / Kp;
       boff[s] = rr < nrows ? static_cast<uint32_t>(tok) * H * 2 + g * 64 : kNoRow;
     }
+    uint32_t toff[NSMAX];  // this thread's rows of the block's token tile
+    if (TL) {
+#pragma unroll
+      for (int i = 0; i < NSMAX; ++i) {
+        const int rr = lr + 16 * i;
+        const int tok = sorted_slot[r0 + min(rr, nrows - 1)] / Kp;
+        toff[i] = rr < nrows ? static_cast<uint32_t>(tok) * H * 2 + lc * 16 : kNoRow;
+      }
+    }
     // rows past the chunk's end fall outside the buffer: stores dropped
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
@@ -196,8 +299,14 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint32_t b1[1] = {boff[0]};
+      const uint32_t t1[1] = {toff[0]};
       auto run = [&](auto ntw) {
-        stream_block<decltype(ntw)::value, D, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1, acc);
+        if constexpr (TL)
+          stream_block_lds<decltype(ntw)::value, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, t1,
+                                                        tl, acc);
+        else
+          stream_block<decltype(ntw)::value, D, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1,
+                                                       acc);
       };
       if (once) run(BoolC<true>{}); else run(BoolC<false>{});
       store(acc[0], 0);
@@ -208,8 +317,12 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       auto run = [&](auto ntw) {
-        stream_block<decltype(ntw)::value, D, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs,
-                                                         boff, acc);
+        if constexpr (TL)
+          stream_block_lds<decltype(ntw)::value, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs,
+                                                            toff, tl, acc);
+        else
+          stream_block<decltype(ntw)::value, D, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs,
+                                                           boff, acc);
       };
       if (once) run(BoolC<true>{}); else run(BoolC<false>{});
 #pragma unroll
@@ -220,8 +333,9 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
 
 // GEMM2 split path, decode shape, long K. Item = (chunk of at most
 // 16 * NSMAX rows, 64 output rows of H). Dynamic LDS: 4 waves x 2I bytes
-// (the 64 rows' scales).
-template <int D, int NSMAX>
+// (the 64 rows' scales), after the two token buffers when TL (as in
+// gemm1_decode_kernel; H / 64 items per chunk, a multiple of 4).
+template <int D, int NSMAX, bool TL>
 __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int32_t* __restrict__ units, int ctr,
@@ -236,7 +350,9 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
   const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
   const int nkb = I >> 7;
   const int blk = 64 * static_cast<int>(srow);  // = 2I bytes
-  uint8_t* my = lds_scales + wave_index() * blk;
+  uint8_t* tl = lds_scales;
+  uint8_t* my = lds_scales + (TL ? 2 * kTokLdsStep : 0) + wave_index() * blk;
+  const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
   const uint32_t wofs[4] = {0u, static_cast<uint32_t>(16 * wrow), static_cast<uint32_t>(32 * wrow),
                             static_cast<uint32_t>(48 * wrow)};
   const uint32_t lofs[4] = {0u, static_cast<uint32_t>(16 * srow), static_cast<uint32_t>(32 * srow),
@@ -258,6 +374,9 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     uint32_t boff[NSMAX];
 #pragma unroll
     for (int s = 0; s < NSMAX; ++s) boff[s] = static_cast<uint32_t>(16 * s + r) * I * 2 + g * 64;
+    uint32_t toff[NSMAX];  // this thread's rows of the block's act tile (zero past nrows)
+#pragma unroll
+    for (int i = 0; i < NSMAX; ++i) toff[i] = static_cast<uint32_t>(lr + 16 * i) * I * 2 + lc * 16;
     auto store = [&](const f32x4_t (&acc)[4], int s) {
       const uint32_t yoff = static_cast<uint32_t>(16 * s + r) * H * 2 + (h0 + g * 4) * 2;
 #pragma unroll
@@ -273,8 +392,13 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
 #pragma unroll
       for (int t = 0; t < 4; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       const uint32_t b1[1] = {boff[0]};
+      const uint32_t t1[1] = {toff[0]};
       auto run = [&](auto ntw) {
-        stream_block<decltype(ntw)::value, D, 1>(wp, wofs, my + r * srow + g, lofs, nkb, ars, b1, acc);
+        if constexpr (TL)
+          stream_block_lds<decltype(ntw)::value, 1>(wp, wofs, my + r * srow + g, lofs, nkb, ars, t1, tl,
+                                                    acc);
+        else
+          stream_block<decltype(ntw)::value, D, 1>(wp, wofs, my + r * srow + g, lofs, nkb, ars, b1, acc);
       };
       if (once) run(BoolC<true>{}); else run(BoolC<false>{});
       store(acc[0], 0);
@@ -285,8 +409,12 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
 #pragma unroll
         for (int t = 0; t < 4; ++t) acc[s][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       auto run = [&](auto ntw) {
-        stream_block<decltype(ntw)::value, D, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, ars, boff,
-                                                     acc);
+        if constexpr (TL)
+          stream_block_lds<decltype(ntw)::value, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, ars, toff,
+                                                        tl, acc);
+        else
+          stream_block<decltype(ntw)::value, D, NSMAX>(wp, wofs, my + r * srow + g, lofs, nkb, ars, boff,
+                                                       acc);
       };
       if (once) run(BoolC<true>{}); else run(BoolC<false>{});
 #pragma unroll
@@ -632,6 +760,15 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
 #ifndef MOE_G1_TP
 #define MOE_G1_TP 2
 #endif
+// Token tiles through LDS (stream_block_lds) pay off once chunks carry
+// several rows: on MI355X they took the T512 E256 H7168 GEMMs from 925 / 518
+// to 692 / 414 us and the Zipf-routed T256 EP decode GEMM1 from 68 to 50 us,
+// but cost 1% at the T64 E896 decode (about one row per expert), where the
+// per-step barrier buys nothing. Chosen by the average rows per local expert
+// (T K' / E', known on the host), and only with a two-step ring.
+static bool token_tiles_in_lds(const GemmArgs& a, int ring) {
+  return ring == 2 && static_cast<long>(a.T) * a.Kp >= 2L * a.Ep;
+}
 
 static int grid_for(long items) {
   long blocks = (items + 3) / 4;
@@ -649,16 +786,17 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
     const int ctr = c32 ? kCtrNumV : kCtrNumU;
     constexpr int kTP = MOE_G1_TP;  // 16-feature tile pairs per wave
     const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / (16 * kTP)));
-    const size_t lds = static_cast<size_t>(4) * kTP * a.H;
-#define MOE_G1D(DD, NS)                                                                           \
-  hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, kTP>), dim3(grid), dim3(kGemmBlock), lds, st,   \
+    const int d = ring_depth(a.H / 128);
+    const bool tl = token_tiles_in_lds(a, d);
+    const size_t lds = static_cast<size_t>(4) * kTP * a.H + (tl ? 2 * kTokLdsStep : 0);
+#define MOE_G1D(DD, NS, TL)                                                                       \
+  hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, kTP, TL>), dim3(grid), dim3(kGemmBlock), lds, st, \
                      a.x, a.w13, a.s13, units, ctr, a.counters, a.counts, a.sorted_slot, a.T, a.H,   \
                      a.I, a.Kp, a.limit, a.act)
-    const int d = ring_depth(a.H / 128);
     if (c32) {
-      if (d == 2) MOE_G1D(2, 2); else MOE_G1D(1, 2);
+      if (tl) MOE_G1D(2, 2, true); else if (d == 2) MOE_G1D(2, 2, false); else MOE_G1D(1, 2, false);
     } else {
-      if (d == 2) MOE_G1D(2, 1); else MOE_G1D(1, 1);
+      if (tl) MOE_G1D(2, 1, true); else if (d == 2) MOE_G1D(2, 1, false); else MOE_G1D(1, 1, false);
     }
 #undef MOE_G1D
     return hipGetLastError();
@@ -686,15 +824,16 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
     const int32_t* units = c32 ? a.vinfo : a.units16;
     const int ctr = c32 ? kCtrNumV : kCtrNumU;
     const int gsplit = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.H / 64));
-    const size_t lds2 = static_cast<size_t>(4) * 2 * a.I;
-#define MOE_G2D(DD, NS)                                                                         \
-  hipLaunchKernelGGL((gemm2_split_kernel<DD, NS>), dim3(gsplit), dim3(kGemmBlock), lds2, st,   \
-                     a.act, a.w2, a.s2, units, ctr, a.counters, a.counts, a.H, a.I, a.y)
     const int d = ring_depth(a.I / 128);
+    const bool tl = token_tiles_in_lds(a, d);
+    const size_t lds2 = static_cast<size_t>(4) * 2 * a.I + (tl ? 2 * kTokLdsStep : 0);
+#define MOE_G2D(DD, NS, TL)                                                                     \
+  hipLaunchKernelGGL((gemm2_split_kernel<DD, NS, TL>), dim3(gsplit), dim3(kGemmBlock), lds2, st, \
+                     a.act, a.w2, a.s2, units, ctr, a.counters, a.counts, a.H, a.I, a.y)
     if (c32) {
-      if (d == 2) MOE_G2D(2, 2); else MOE_G2D(1, 2);
+      if (tl) MOE_G2D(2, 2, true); else if (d == 2) MOE_G2D(2, 2, false); else MOE_G2D(1, 2, false);
     } else {
-      if (d == 2) MOE_G2D(2, 1); else MOE_G2D(1, 1);
+      if (tl) MOE_G2D(2, 1, true); else if (d == 2) MOE_G2D(2, 1, false); else MOE_G2D(1, 1, false);
     }
 #undef MOE_G2D
   }

@@ -48,6 +48,7 @@ struct GemmArgs {
   const int32_t* counts;  // [Ep] rows per local expert
   const int32_t* sorted_slot;
   int T, H, I, Kp, B, kmax_v, max_dense_tiles, max_units16, rows_pad;
+  int Ep;  // local experts including the shared ones
   int dense_grid_tiles;  // tiles the dense GEMM2 grid is sized for (the kernels loop past it)
   float limit;
   uint16_t* act;  // [rows_pad, I] bf16 (W4A16), or E4M3 codes (W4A8)

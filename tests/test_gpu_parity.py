@@ -38,6 +38,12 @@ SMALL = [
     LayerShape("ids_mode", T=29, E=16, E_g=40, topk=5, H=512, I=128, B=16, expert_offset=10,
                mode="ids"),
     LayerShape("one_token", T=1, E=32, E_g=32, topk=8, H=512, I=128, B=16),
+    # split GEMM2 over long K (I > 512): odd step count (one-step ring, per-wave
+    # token loads), sparse rows (per-wave token loads), and dense rows with
+    # chunks of 17-32 rows (token tiles through LDS, two 16-row sub-tiles)
+    LayerShape("split_k_odd", T=40, E=16, E_g=16, topk=4, H=512, I=640, B=32),
+    LayerShape("split_sparse", T=8, E=64, E_g=64, topk=4, H=512, I=1024, B=16),
+    LayerShape("split_dense_b32", T=64, E=8, E_g=8, topk=2, H=1024, I=1024, B=32, swiglu_limit=5.0),
 ]
 
 
