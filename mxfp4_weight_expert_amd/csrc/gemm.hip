@@ -577,6 +577,77 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
   }
 }
 
+// Block-shared E4M3 token tile of one K step in LDS for the W4A8 stream:
+// 16 rows x 128 code bytes, then the rows' four scale bytes. Chunk c (0..7)
+// of row rr sits at rr * 128 + 16 * (c ^ (((rr >> 2) & 3) << 1)): the 32
+// lanes of a fragment read (rows r, chunk g or 4 + g, g = 0..1) and of a
+// four-row write fall on distinct 16-byte bank groups.
+constexpr int kTok8LdsStep = 16 * 128 + 16 * 4;
+__device__ __forceinline__ uint32_t t8lds_off(int rr, int c) {
+  return static_cast<uint32_t>(rr * 128) + ((static_cast<uint32_t>(c) ^ ((static_cast<uint32_t>(rr >> 2) & 3u) << 1)) << 4);
+}
+
+// stream_block_a8 with the token codes and scales read from a block-shared
+// LDS tile (two buffers of kTok8LdsStep at tl), as stream_block_lds does for
+// bf16 tokens: one barrier per K step, every wave of the block calls it with
+// the same nkb. Threads t < 128 load code chunk t % 8 of tile row t / 8
+// (xrs at toff, zero past the unit's end), threads 128..143 the scale dword
+// of tile row t - 128 (srs at tsoff); the rest load nothing (out-of-range
+// offsets) and store nothing.
+template <bool NTW>
+__device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uint32_t (&wofs)[4],
+                                                    const uint8_t* ls, const uint32_t (&lofs)[4],
+                                                    int nkb, __amdgpu_buffer_rsrc_t xrs, uint32_t toff,
+                                                    __amdgpu_buffer_rsrc_t srs, uint32_t tsoff,
+                                                    uint8_t* tl, f32x4_t (&acc)[4]) {
+  constexpr int D = 2;
+  const int lane = lane_id();
+  const int r = lane & 15, g = lane >> 4;
+  const int t = static_cast<int>(threadIdx.x);
+  const bool code_role = t < 128, scale_role = t >= 128 && t < 144;
+  const uint32_t st_off = code_role ? t8lds_off(t >> 3, t & 7) : 16 * 128 + (t - 128) * 4;
+  uint4 w[D][4], tv[D];
+  uint32_t ts[D];
+  auto put = [&](uint8_t* buf, int d) {
+    if (code_role) *reinterpret_cast<uint4*>(buf + st_off) = tv[d];
+    if (scale_role) *reinterpret_cast<uint32_t*>(buf + st_off) = ts[d];
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) {
+    tv[d] = bld16(xrs, toff + d * 128);
+    ts[d] = bld4(srs, tsoff + d * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[d][q] = ldw16<NTW>(wp + wofs[q] + d * kPkBlock);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  put(tl, 0);
+  __syncthreads();
+  const int last = nkb - 1;
+  auto step = [&](int kb, int d) {
+    const uint8_t* tb = tl + (kb & 1) * kTok8LdsStep;
+    const uint4 x0 = *reinterpret_cast<const uint4*>(tb + t8lds_off(r, g));
+    const uint4 x1 = *reinterpret_cast<const uint4*>(tb + t8lds_off(r, 4 + g));
+    const uint32_t xsb = tb[16 * 128 + r * 4 + g];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[q] = mfma_f4xf8(w[d][q], ls[lofs[q] + kb * 4], x0, x1, xsb, acc[q]);
+    __builtin_amdgcn_sched_barrier(0);
+    put(tl + ((kb + 1) & 1) * kTok8LdsStep, (d + 1) % D);
+    const int nk = min(kb + D, last);
+    tv[d] = bld16(xrs, toff + nk * 128);
+    ts[d] = bld4(srs, tsoff + nk * 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w[d][q] = ldw16<NTW>(wp + wofs[q] + nk * kPkBlock);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) step(d, d);
+  for (int kb0 = D; kb0 < nkb; kb0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) step(kb0 + d, d);
+  }
+}
+
 // The 32 act values of one token row and one 32-feature group, spread as 8
 // values over the four lanes r, r + 16, r + 32, r + 48: MXFP8-quantise them
 // (block amax over the four lanes) and store the lane's two 4-byte runs at
@@ -599,8 +670,9 @@ __device__ __forceinline__ void quant_store_act(const float (&a)[8], __amdgpu_bu
 
 // GEMM1 + SwiGLU + act quantisation, W4A8, decode shape. Items and LDS as
 // in gemm1_decode_kernel; the 32-feature group of an item is exactly one
-// MXFP8 block of act.
-template <int D>
+// MXFP8 block of act. TL: token tiles through LDS (stream_block_a8_lds,
+// D = 2), after the scale blocks in the dynamic LDS.
+template <int D, bool TL>
 __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
@@ -623,6 +695,8 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
   const uint32_t lofs[4] = {0u, static_cast<uint32_t>(blk), static_cast<uint32_t>(16 * srow),
                             static_cast<uint32_t>(blk + 16 * srow)};
   const uint32_t srow_a = static_cast<uint32_t>(I) >> 5;
+  uint8_t* tl = lds_scales + 4 * 2 * blk;
+  const int tt = static_cast<int>(threadIdx.x);
   for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
     const int u = item / groups;
     const int f0 = (item - u * groups) * 32;
@@ -641,8 +715,20 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     auto run = [&](auto ntw) {
-      stream_block_a8<decltype(ntw)::value, D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff, srs,
-                                               soff, acc);
+      if constexpr (TL) {
+        // this thread's row of the block's token tile: codes (t < 128) or scales
+        const int rr = tt < 128 ? tt >> 3 : tt - 128;
+        const uint32_t ttok = static_cast<uint32_t>(sorted_slot[r0 + min(rr, nrows - 1)] / Kp);
+        const bool tv_ok = rr < nrows;
+        const uint32_t toff = tt < 128 && tv_ok ? ttok * static_cast<uint32_t>(H) + (tt & 7) * 16 : kNoRow;
+        const uint32_t tsoff =
+            tt >= 128 && tt < 144 && tv_ok ? ttok * static_cast<uint32_t>(srow) : kNoRow;
+        stream_block_a8_lds<decltype(ntw)::value>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, toff, srs,
+                                                  tsoff, tl, acc);
+      } else {
+        stream_block_a8<decltype(ntw)::value, D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff, srs,
+                                                 soff, acc);
+      }
     };
     // weights read once in this call (the expert's only unit): non-temporal
     if (counts[e] <= 16) run(BoolC<true>{}); else run(BoolC<false>{});
@@ -844,18 +930,24 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
   const int grid = grid_for(static_cast<long>(a.max_units16) * (a.I / 32));
-  const size_t lds = static_cast<size_t>(4) * 2 * a.H;
+  const int ring = ring_depth(a.H / 128) >= 2 ? 2 : 1;
+  const bool tl = token_tiles_in_lds(a, ring);
+  const size_t lds = static_cast<size_t>(4) * 2 * a.H + (tl ? 2 * kTok8LdsStep : 0);
   uint8_t* actq = reinterpret_cast<uint8_t*>(a.act);
-#define MOE_G1A(DD)                                                                              \
-  hipLaunchKernelGGL(gemm1_decode_a8_kernel<DD>, dim3(grid), dim3(kGemmBlock), lds, st, a.xq,    \
+#define MOE_G1A(DD, TL)                                                                          \
+  hipLaunchKernelGGL((gemm1_decode_a8_kernel<DD, TL>), dim3(grid), dim3(kGemmBlock), lds, st, a.xq, \
                      a.xs, a.w13, a.s13, a.units16, a.counters, a.counts, a.sorted_slot, a.T, a.H,  \
                      a.I, a.Kp,                                                                 \
                      a.limit, actq, a.act_scales)
-  switch (ring_depth(a.H / 128)) {
-    case 4: MOE_G1A(4); break;
-    case 3: MOE_G1A(3); break;
-    case 2: MOE_G1A(2); break;
-    default: MOE_G1A(1); break;
+  if (tl) {
+    MOE_G1A(2, true);
+  } else {
+    switch (ring_depth(a.H / 128)) {
+      case 4: MOE_G1A(4, false); break;
+      case 3: MOE_G1A(3, false); break;
+      case 2: MOE_G1A(2, false); break;
+      default: MOE_G1A(1, false); break;
+    }
   }
 #undef MOE_G1A
   return hipGetLastError();

@@ -170,7 +170,7 @@ def test_w4a8_quant_special_values():
     _check_xq(maps_np(s, ws), ref)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill"])
+@pytest.mark.parametrize("name", ["decode", "decode_ep", "prefill"])
 def test_w4a8_config_parity(name):
     s = CONFIGS[name].replace(a_dtype="mxfp8", name=name + "_w4a8")
     say(f"[w4a8 config] {s.name}")
