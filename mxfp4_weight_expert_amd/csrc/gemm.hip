@@ -114,12 +114,16 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 }
 
 // Token tile of one K step in LDS, shared by the four waves of a block
-// (they work on the same chunk): up to 32 rows x 256 bytes. 16-byte chunk c
+// (they work on the same chunk): 16 * NS rows x 256 bytes
+// (tok_lds_step<NS>). 16-byte chunk c
 // of tile row rr sits at rr * 256 + 16 * (c ^ tswz(rr)): the 32 lanes that
 // read one fragment (rows r = 0..15, chunks 4g + j, g = 0..1) and the 32
 // lanes that write two rows fall on distinct 16-byte bank groups of a
 // 512-byte bank line.
-constexpr int kTokLdsStep = 32 * 256;
+template <int NS>
+constexpr int tok_lds_step() {
+  return 16 * NS * 256;
+}
 __device__ __forceinline__ uint32_t tswz(int rr) {
   const uint32_t m = static_cast<uint32_t>(rr >> 1) & 7u;
   return (m & 3u) | ((m & 4u) << 1);
@@ -129,7 +133,7 @@ __device__ __forceinline__ uint32_t tlds_off(int rr, int c) {
 }
 
 // stream_block with the token fragments read from a block-shared LDS tile
-// (two buffers of kTokLdsStep at tl) instead of per-wave loads, so a token
+// (two buffers of tok_lds_step<NS>() at tl) instead of per-wave loads, so a token
 // row is fetched once per block and K step instead of once per wave. Every
 // wave of the block must call it with the same nkb and NS: one barrier per
 // K step. Thread t loads 16-byte chunk t % 16 of tile rows t / 16 + 16 i
@@ -160,7 +164,7 @@ __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32
   __syncthreads();
   const int last = nkb - 1;
   auto step = [&](int kb, int d) {
-    const uint8_t* tb = tl + (kb & 1) * kTokLdsStep;
+    const uint8_t* tb = tl + (kb & 1) * tok_lds_step<NS>();
     uint4 xb[NS][4];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
@@ -183,7 +187,7 @@ __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32
     __builtin_amdgcn_sched_barrier(0);
     // step kb + 1's tile (loaded one step ago) into the buffer read in step
     // kb - 1, which every wave left before the last barrier
-    uint8_t* nb = tl + ((kb + 1) & 1) * kTokLdsStep;
+    uint8_t* nb = tl + ((kb + 1) & 1) * tok_lds_step<NS>();
 #pragma unroll
     for (int i = 0; i < NS; ++i) *reinterpret_cast<uint4*>(nb + tlds_off(lr + 16 * i, lc)) = tv[(d + 1) % D][i];
     const int nk = min(kb + D, last);
@@ -225,14 +229,13 @@ inline int ring_depth(int nkb) {
 // LDS then starts with the two token buffers. The four waves of a block
 // always hold items of the same chunk (groups is a multiple of 4).
 template <int D, int NSMAX, int TP, bool TL>
-__global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
+__device__ __forceinline__ void gemm1_decode_items(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ sorted_slot, int T, int H,
-    int I, int Kp, float limit, uint16_t* __restrict__ act) {
+    int I, int Kp, float limit, uint16_t* __restrict__ act, uint8_t* lds_scales) {
   constexpr int NT = 2 * TP;
-  extern __shared__ uint8_t lds_scales[];
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int groups = I / (16 * TP);
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
   const int nkb = H >> 7;
   const int blk = 16 * TP * static_cast<int>(srow);  // the group's gate (or up) scale rows
   uint8_t* tl = lds_scales;
-  uint8_t* my = lds_scales + (TL ? 2 * kTokLdsStep : 0) + wave_index() * 2 * blk;
+  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<NSMAX>() : 0) + wave_index() * 2 * blk;
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(T) * H * 2));
   const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
   uint32_t wofs[NT], lofs[NT];
@@ -331,6 +334,31 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
   }
 }
 
+// Items of 32 features (TP = 2) re-read the chunk's tokens half as often as
+// items of 16; items of 16 give twice the parallelism. With fewer 32-feature
+// items than the waves the chip holds at once (a few touched experts with
+// many rows, as in the Zipf-routed T256 EP decode: 42 against 51 us on
+// MI355X), the kernel takes 16-feature items; otherwise 32 (T64 decode 146
+// against 161 us, T512 shared-expert layer 690 against 744 us). The choice
+// is read on the device from the chunk count and is the same for every
+// block. Dynamic LDS is sized for TP = 2.
+constexpr int kNarrowItemsBelow = 4096;
+template <int D, int NSMAX, bool TL>
+__global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
+    const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
+    const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ sorted_slot, int T, int H, int I, int Kp, float limit,
+    uint16_t* __restrict__ act) {
+  extern __shared__ uint8_t lds_scales[];
+  if (counters[ctr] * (I / 32) < kNarrowItemsBelow)
+    gemm1_decode_items<D, NSMAX, 1, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
+                                        I, Kp, limit, act, lds_scales);
+  else
+    gemm1_decode_items<D, NSMAX, 2, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
+                                        I, Kp, limit, act, lds_scales);
+}
+
 // GEMM2 split path, decode shape, long K. Item = (chunk of at most
 // 16 * NSMAX rows, 64 output rows of H). Dynamic LDS: 4 waves x 2I bytes
 // (the 64 rows' scales), after the two token buffers when TL (as in
@@ -351,7 +379,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
   const int nkb = I >> 7;
   const int blk = 64 * static_cast<int>(srow);  // = 2I bytes
   uint8_t* tl = lds_scales;
-  uint8_t* my = lds_scales + (TL ? 2 * kTokLdsStep : 0) + wave_index() * blk;
+  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<NSMAX>() : 0) + wave_index() * blk;
   const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
   const uint32_t wofs[4] = {0u, static_cast<uint32_t>(16 * wrow), static_cast<uint32_t>(32 * wrow),
                             static_cast<uint32_t>(48 * wrow)};
@@ -843,9 +871,6 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
 #define MOE_STREAM_GRID (256 * 3)
 #endif
 
-#ifndef MOE_G1_TP
-#define MOE_G1_TP 2
-#endif
 // Token tiles through LDS (stream_block_lds) pay off once chunks carry
 // several rows: on MI355X they took the T512 E256 H7168 GEMMs from 925 / 518
 // to 692 / 414 us and the Zipf-routed T256 EP decode GEMM1 from 68 to 50 us,
@@ -870,13 +895,14 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
     const bool c32 = a.B == 32;
     const int32_t* units = c32 ? a.vinfo : a.units16;
     const int ctr = c32 ? kCtrNumV : kCtrNumU;
-    constexpr int kTP = MOE_G1_TP;  // 16-feature tile pairs per wave
-    const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / (16 * kTP)));
+    // grid for the 16-feature items (the larger count); LDS for the 32-feature ones
+    const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / 16));
     const int d = ring_depth(a.H / 128);
     const bool tl = token_tiles_in_lds(a, d);
-    const size_t lds = static_cast<size_t>(4) * kTP * a.H + (tl ? 2 * kTokLdsStep : 0);
+    const size_t lds =
+        static_cast<size_t>(4) * 2 * a.H + (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
 #define MOE_G1D(DD, NS, TL)                                                                       \
-  hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, kTP, TL>), dim3(grid), dim3(kGemmBlock), lds, st, \
+  hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, TL>), dim3(grid), dim3(kGemmBlock), lds, st,      \
                      a.x, a.w13, a.s13, units, ctr, a.counters, a.counts, a.sorted_slot, a.T, a.H,   \
                      a.I, a.Kp, a.limit, a.act)
     if (c32) {
@@ -912,7 +938,8 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
     const int gsplit = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.H / 64));
     const int d = ring_depth(a.I / 128);
     const bool tl = token_tiles_in_lds(a, d);
-    const size_t lds2 = static_cast<size_t>(4) * 2 * a.I + (tl ? 2 * kTokLdsStep : 0);
+    const size_t lds2 =
+        static_cast<size_t>(4) * 2 * a.I + (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
 #define MOE_G2D(DD, NS, TL)                                                                     \
   hipLaunchKernelGGL((gemm2_split_kernel<DD, NS, TL>), dim3(gsplit), dim3(kGemmBlock), lds2, st, \
                      a.act, a.w2, a.s2, units, ctr, a.counters, a.counts, a.H, a.I, a.y)
