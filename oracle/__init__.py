@@ -23,12 +23,12 @@ Functions whose result has no pin other than the oracle itself say
 from .mx import (E2M1_MAGNITUDES, e2m1_decode, e8m0_decode, dequant_mxfp4,
                  quant_mxfp8, dequant_mxfp8, e4m3_decode)
 from .moe import (route_topk_softmax, shared_append, local_map, sort_align,
-                  kmax_v, gate_word, dense_tiles, expert_glu, reference_forward,
+                  kmax_v, gate_word, dense_tiles, expert_glu, situ, reference_forward,
                   sampled_forward, GATE_TAU, DENSE_MT, bf16_bits_to_f64)
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "quant_mxfp8",
     "dequant_mxfp8", "e4m3_decode", "route_topk_softmax", "shared_append", "local_map",
-    "sort_align", "kmax_v", "gate_word", "dense_tiles", "expert_glu", "reference_forward",
+    "sort_align", "kmax_v", "gate_word", "dense_tiles", "expert_glu", "situ", "reference_forward",
     "sampled_forward", "GATE_TAU", "DENSE_MT", "bf16_bits_to_f64",
 ]

@@ -161,8 +161,24 @@ def dense_tiles(counts: np.ndarray, offsets: np.ndarray, mt: int = DENSE_MT) -> 
     return np.array(out, dtype=np.int32).reshape(-1, 4)
 
 
+def situ(g: np.ndarray, u: np.ndarray, beta: float, linear_beta: float) -> np.ndarray:
+    """SiTU activation of the gate half g and the up half u, float64.
+
+    [SHAPE] section 4 gives SiTU as the activation of the K3.1 decode kernel,
+    printed only for beta = 4, linear beta = 25: the gate factor
+    2 tanh(g/4) (1 + tanh(g/2)) and the up factor 25 tanh(u/25), multiplied.
+    Since 1 + tanh(v/2) = 2 sigmoid(v), the gate factor is
+    beta tanh(g/beta) sigmoid(g): SiLU with its linear factor g soft-capped
+    at beta by tanh (beta -> infinity gives g sigmoid(g)). Reading for other
+    constants: the sigmoid does not depend on beta, and the up factor is
+    linear_beta tanh(u / linear_beta).
+    """
+    return (beta * np.tanh(g / beta) * _sigmoid(g)) * (linear_beta * np.tanh(u / linear_beta))
+
+
 def expert_glu(xr: np.ndarray, W13: np.ndarray, W2: np.ndarray, limit: float = 0.0,
-               act_mxfp8: bool = False) -> np.ndarray:
+               act_mxfp8: bool = False, act: str = "swiglu", beta: float = 4.0,
+               linear_beta: float = 25.0) -> np.ndarray:
     """One expert's gated MLP on its rows, float64.
 
     [CUTLASS] sections 4 (GEMM1 output is (rows, 2n); SiLU on the first half
@@ -171,20 +187,30 @@ def expert_glu(xr: np.ndarray, W13: np.ndarray, W2: np.ndarray, limit: float = 0
     act = silu(g) * u, y = act W2^T.
     With limit > 0 the clamped SwiGLU of [SHAPE] section 4 and the Marlin
     page's swiglu limit: g = min(g, limit), u = clip(u, -limit, limit).
+    With act = "situ" the activation is situ(g, u, beta, linear_beta)
+    instead (the limit does not apply).
     With act_mxfp8 the activation is MXFP8-quantised along I before GEMM2.
     xr [n, H], W13 [2I, H], W2 [H, I] -> y [n, H].
     """
     I = W13.shape[0] // 2
     h = xr @ W13.T
     g, u = h[:, :I], h[:, I:]
-    if limit > 0:
-        g = np.minimum(g, limit)
-        u = np.clip(u, -limit, limit)
-    act = g * _sigmoid(g) * u
+    if act == "situ":
+        act = situ(g, u, beta, linear_beta)
+    else:
+        if limit > 0:
+            g = np.minimum(g, limit)
+            u = np.clip(u, -limit, limit)
+        act = g * _sigmoid(g) * u
     if act_mxfp8:
         q, s = quant_mxfp8(act)
         act = dequant_mxfp8(q, s)
     return act @ W2.T
+
+
+def _act_kw(s) -> dict:
+    """The shape's activation as expert_glu keyword arguments."""
+    return dict(act=s.activation, beta=s.act_beta, linear_beta=s.act_linear_beta)
 
 
 def _routing(shape, inp):
@@ -246,7 +272,8 @@ def reference_forward(shape, inp: dict, force_path: int = -1, compute_out: bool 
         tok = rows // s.Kp
         W13 = dequant_mxfp4(inp["w13"][e], inp["s13"][e])
         W2 = dequant_mxfp4(inp["w2"][e], inp["s2"][e])
-        y = expert_glu(xa[tok], W13, W2, s.swiglu_limit, s.a_dtype == "mxfp8")
+        y = expert_glu(xa[tok], W13, W2, s.swiglu_limit, s.a_dtype == "mxfp8",
+                       **_act_kw(s))
         np.add.at(out, tok, wflat[rows][:, None] * y)
     res["out"] = out
     return res
@@ -277,6 +304,7 @@ def sampled_forward(shape, inp: dict, tokens) -> np.ndarray:
                 cache[e] = (dequant_mxfp4(inp["w13"][e], inp["s13"][e]),
                             dequant_mxfp4(inp["w2"][e], inp["s2"][e]))
             W13, W2 = cache[e]
-            y = expert_glu(xa[i: i + 1], W13, W2, s.swiglu_limit, s.a_dtype == "mxfp8")
+            y = expert_glu(xa[i: i + 1], W13, W2, s.swiglu_limit, s.a_dtype == "mxfp8",
+                           **_act_kw(s))
             out[i] += slot_w[i, k] * y[0]
     return out

@@ -326,8 +326,10 @@ def _onehot_layer():
     return H, I, E, S, pg, pu, cgv, 1.0, 6.0, wts
 
 
-def _closed_form_out(x, ids, w, shared_w, E, offset, limit, H, I, pg, pu, cgv, cu, c2):
+def _closed_form_out(x, ids, w, shared_w, E, offset, limit, H, I, pg, pu, cgv, cu, c2,
+                     act=("swiglu",)):
     silu = lambda v: v / (1.0 + math.exp(-v))
+    sig = lambda v: 1.0 / (1.0 + math.exp(-v))
     T = x.shape[0]
     out = np.zeros((T, H))
     for t in range(T):
@@ -339,6 +341,10 @@ def _closed_form_out(x, ids, w, shared_w, E, offset, limit, H, I, pg, pu, cgv, c
                 i = h % I
                 g = cgv(e) * x[t, pg(e, i)]
                 u = cu * x[t, pu(e, i)]
+                if act[0] == "situ":
+                    beta, lb = act[1], act[2]
+                    out[t, h] += wt * c2 * (beta * math.tanh(g / beta) * sig(g)) * (lb * math.tanh(u / lb))
+                    continue
                 if limit > 0:
                     g = min(g, limit)
                     u = max(-limit, min(u, limit))
@@ -347,7 +353,7 @@ def _closed_form_out(x, ids, w, shared_w, E, offset, limit, H, I, pg, pu, cgv, c
 
 
 @pytest.mark.parametrize("limit", [0.0, 1.25])
-def test_whole_layer_closed_form(limit):
+def test_whole_layer_closed_form(limit, act=("swiglu",)):
     H, I, E, S, pg, pu, cgv, cu, c2, wts = _onehot_layer()
     offset, E_g, topk, T = 2, 8, 3, 5
     rng = np.random.default_rng(31)
@@ -357,16 +363,59 @@ def test_whole_layer_closed_form(limit):
     sh = f32_to_bf16_bits(np.array([[0.0], [2.0], [-2.0], [1.0], [0.5]], np.float32))
     shape = LayerShape("cf", T=T, E=E, E_g=E_g, topk=topk, H=H, I=I, B=2, S=S,
                        expert_offset=offset, swiglu_limit=limit, shared_scale=0.5, mode="ids")
+    if act[0] == "situ":
+        shape = shape.replace(activation="situ", act_beta=act[1], act_linear_beta=act[2])
     inp = dict(x=f32_to_bf16_bits(x), logits=np.zeros((T, E_g), np.float32), shared=sh,
                topk_ids=ids, topk_w=w, **wts)
     got = oracle.reference_forward(shape, inp)["out"]
     shared_w = scipy.special.expit(oracle.bf16_bits_to_f64(sh)) * 0.5
     want = _closed_form_out(x.astype(np.float64), ids, w.astype(np.float64), shared_w, E, offset,
-                            limit, H, I, pg, pu, cgv, cu, c2)
+                            limit, H, I, pg, pu, cgv, cu, c2, act)
     assert np.max(np.abs(got - want)) <= 1e-12 * max(1.0, np.max(np.abs(want)))
     if limit > 0:  # the clamp must actually bite in this example
         g_all = [cgv(e) * abs(x[t, pg(e, i)]) for t in range(T) for e in range(E + S) for i in range(I)]
         assert max(g_all) > limit
+
+
+# ------------------------------------------------------------------ SiTU
+# [SHAPE] section 4 prints the SiTU activation of the K3.1 kernel for
+# beta = 4 and linear beta = 25 only: gate factor 2 tanh(g/4)(1 + tanh(g/2)),
+# up factor 25 tanh(u/25). The oracle's general form beta tanh(g/beta)
+# sigmoid(g) * lb tanh(u/lb) must reproduce that instance, and must reduce
+# to SwiGLU when both caps go to infinity.
+
+def test_situ_matches_printed_instance():
+    g, u = np.meshgrid(np.linspace(-60, 60, 241), np.linspace(-80, 80, 161))
+    printed = (2.0 * np.tanh(g * 0.25) * (1.0 + np.tanh(g * 0.5))) * (25.0 * np.tanh(u * 0.04))
+    got = oracle.situ(g, u, 4.0, 25.0)
+    assert np.max(np.abs(got - printed)) <= 1e-12 * np.max(np.abs(printed))
+
+
+def test_situ_reduces_to_swiglu_without_caps():
+    rng = np.random.default_rng(5)
+    g, u = rng.normal(0, 5, 1000), rng.normal(0, 5, 1000)
+    swiglu = g * scipy.special.expit(g) * u
+    got = oracle.situ(g, u, 1e9, 1e9)
+    assert np.allclose(got, swiglu, rtol=1e-9, atol=1e-12)
+
+
+def test_situ_caps_symmetry_and_zero():
+    beta, lb = 4.0, 25.0
+    g = np.linspace(-50, 50, 1001)
+    one = np.ones_like(g)
+    # odd in u, zero at g = 0, bounded by beta * lb
+    assert np.allclose(oracle.situ(g, -3 * one, beta, lb), -oracle.situ(g, 3 * one, beta, lb))
+    assert oracle.situ(np.zeros(1), np.ones(1), beta, lb)[0] == 0.0
+    assert np.all(np.abs(oracle.situ(g, 1e6 * one, beta, lb)) <= beta * lb * (1 + 1e-12))
+    # the gate factor tends to beta for large g and to 0 for very negative g
+    big = oracle.situ(np.array([200.0]), np.array([lb * np.arctanh(0.5)]), beta, lb)[0]
+    assert abs(big - beta * 0.5 * lb) <= 1e-9
+    assert abs(oracle.situ(np.array([-200.0]), np.array([1.0]), beta, lb)[0]) < 1e-60
+
+
+@pytest.mark.parametrize("beta,lb", [(4.0, 25.0), (1.5, 0.75)])
+def test_whole_layer_closed_form_situ(beta, lb):
+    test_whole_layer_closed_form(0.0, ("situ", beta, lb))
 
 
 def test_dense_glu_reduction_matches_torch():
@@ -401,6 +450,7 @@ SMALL = [
     LayerShape("s4", T=13, E=7, E_g=20, topk=5, H=64, I=32, B=2, expert_offset=3, mode="ids"),
     LayerShape("s5", T=7, E=4, E_g=4, topk=2, H=64, I=64, B=16, a_dtype="mxfp8", S=1,
                swiglu_limit=2.0),
+    LayerShape("s6_situ", T=10, E=6, E_g=6, topk=3, H=64, I=32, B=2, S=1, activation="situ"),
 ]
 
 
@@ -451,6 +501,14 @@ def _closed_form_error(limit=1.25):
     return False
 
 
+def _situ_closed_form_error():
+    try:
+        test_whole_layer_closed_form_situ(1.5, 0.75)
+    except AssertionError:
+        return True
+    return False
+
+
 def test_planted_mistakes_are_caught(monkeypatch):
     assert not _closed_form_error()
     # 1. swapped nibble order
@@ -465,9 +523,9 @@ def test_planted_mistakes_are_caught(monkeypatch):
     # 2. gate and up halves swapped
     orig_glu = omoe.expert_glu
 
-    def glu_swapped(xr, W13, W2, limit=0.0, act_mxfp8=False):
+    def glu_swapped(xr, W13, W2, limit=0.0, act_mxfp8=False, **act):
         I = W13.shape[0] // 2
-        return orig_glu(xr, np.concatenate([W13[I:], W13[:I]]), W2, limit, act_mxfp8)
+        return orig_glu(xr, np.concatenate([W13[I:], W13[:I]]), W2, limit, act_mxfp8, **act)
     monkeypatch.setattr(omoe, "expert_glu", glu_swapped)
     assert _closed_form_error()
     monkeypatch.setattr(omoe, "expert_glu", orig_glu)
@@ -483,7 +541,7 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert _closed_form_error()
     monkeypatch.setattr(omoe, "dequant_mxfp4", orig_deq)
     # 4. gate clamped from below as well as above
-    def glu_clamp_both(xr, W13, W2, limit=0.0, act_mxfp8=False):
+    def glu_clamp_both(xr, W13, W2, limit=0.0, act_mxfp8=False, **act):
         I = W13.shape[0] // 2
         h = xr @ W13.T
         g, u = h[:, :I], h[:, I:]
@@ -498,6 +556,12 @@ def test_planted_mistakes_are_caught(monkeypatch):
     monkeypatch.setattr(omoe, "local_map", lambda ids, E, off: orig_lm(ids, E, 0))
     assert _closed_form_error()
     monkeypatch.setattr(omoe, "local_map", orig_lm)
+    # 7. SiTU caps swapped (beta on the up half, linear beta on the gate)
+    orig_situ = omoe.situ
+    monkeypatch.setattr(omoe, "situ", lambda g, u, b, lb: orig_situ(g, u, lb, b))
+    assert _situ_closed_form_error()
+    monkeypatch.setattr(omoe, "situ", orig_situ)
+    assert not _situ_closed_form_error()
     # 6. shared weight without the sigmoid
     orig_sig = omoe._sigmoid
     monkeypatch.setattr(omoe, "shared_append",

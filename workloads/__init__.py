@@ -43,7 +43,10 @@ class LayerShape:
     B: int
     S: int = 0
     expert_offset: int = 0
-    swiglu_limit: float = 0.0  # <= 0 means no clamp
+    swiglu_limit: float = 0.0  # <= 0 means no clamp (SwiGLU only)
+    activation: str = "swiglu"  # "swiglu" or "situ"
+    act_beta: float = 4.0  # SiTU gate cap beta
+    act_linear_beta: float = 25.0  # SiTU up cap (linear beta)
     shared_scale: float = 1.0
     a_dtype: str = "bf16"  # "bf16" (W4A16) or "mxfp8" (W4A8)
     routing: str = "normal"  # "normal" logits N(0,1), "zipf" skewed logits
