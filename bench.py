@@ -37,6 +37,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--a-dtype", default="bf16", choices=["bf16", "mxfp8"],
                    help="activation format: bf16 (W4A16) or mxfp8 (W4A8)")
+    p.add_argument("--activation", default=None, choices=["swiglu", "situ"],
+                   help="GEMM1 epilogue (default: the workload's; situ uses beta 4, linear beta 25)")
     p.add_argument("--config", default="decode",
                    help="tiny | decode | decode_ep | shared_clamp | prefill")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -82,6 +84,8 @@ def workload_name(s) -> str:
     parts += [f"H={s.H}", f"I={s.I}", f"BlockN={s.B}"]
     if s.swiglu_limit > 0:
         parts.append(f"clamp={s.swiglu_limit:g}")
+    if s.activation == "situ":
+        parts.append(f"SiTU(beta={s.act_beta:g}, linear_beta={s.act_linear_beta:g})")
     if s.routing == "zipf":
         parts.append(f"zipf={s.zipf_s:g}")
     act = "W4A8 MXFP8 (E4M3) activations" if s.a_dtype == "mxfp8" else "W4A16 bf16 activations"
@@ -132,6 +136,8 @@ def main():
 
     moe.load_library()  # fails loudly if the HIP library is not built
     s = CONFIGS[args.config].replace(a_dtype=args.a_dtype)
+    if args.activation:
+        s = s.replace(activation=args.activation)
     a8 = s.a_dtype == "mxfp8"
     dev_id = 0
     torch.cuda.set_device(dev_id)
@@ -140,7 +146,8 @@ def main():
     inp = make_inputs(s, config_seed(args.config))
     shp = moe.Shape(T=s.T, E=s.E, E_global=s.E_g, topk=s.topk, H=s.H, I=s.I, block_n=s.B, S=s.S,
                     expert_offset=s.expert_offset, swiglu_limit=s.swiglu_limit,
-                    shared_scale=s.shared_scale, a_dtype=s.a_dtype)
+                    shared_scale=s.shared_scale, a_dtype=s.a_dtype, activation=s.activation,
+                    act_beta=s.act_beta, act_linear_beta=s.act_linear_beta)
 
     def bf16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)

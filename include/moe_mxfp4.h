@@ -52,6 +52,9 @@ extern "C" {
 
 /* Activation kinds. */
 #define MOE_ACT_SWIGLU 0 /* act = silu(g) * u on the gate half g, up half u */
+#define MOE_ACT_SITU 1   /* act = beta tanh(g/beta) sigmoid(g) * lb tanh(u/lb): the
+                            SiTU activation of the Kimi-K3.1 decode page, section 4
+                            (printed there for beta = 4, lb = 25) */
 
 /* Activation (A operand) formats. */
 #define MOE_ADTYPE_BF16 0  /* W4A16: bf16 activations, bf16 MFMA */
@@ -81,7 +84,7 @@ extern "C" {
  *                   decode GEMM1 (tokens on the MFMA N side); 64, 128 or 256
  *                   the prefill GEMM1 (tokens on the M side)
  *   expert_offset   global id of local expert 0
- *   activation      MOE_ACT_SWIGLU
+ *   activation      MOE_ACT_SWIGLU or MOE_ACT_SITU
  *   a_dtype         MOE_ADTYPE_BF16 or MOE_ADTYPE_MXFP8 (W4A8; needs I <= 512).
  *                   W4A8 quantises x to MXFP8 and the SwiGLU output act to
  *                   MXFP8 (per 32 along I) before GEMM2; the GEMMs run on
@@ -91,6 +94,9 @@ extern "C" {
  *                   before silu(gate) * up; <= 0: no clamp
  *   shared_scale    multiplier of the shared-expert sigmoid (1/ep_size on
  *                   the page; 1.0 on one GPU)
+ *   act_beta        SiTU gate cap beta (> 0, finite; the K3.1 value is 4)
+ *   act_linear_beta SiTU up cap (> 0, finite; the K3.1 value is 25). Both
+ *                   are read only for MOE_ACT_SITU, which ignores swiglu_limit
  */
 typedef struct moe_mxfp4_shape {
   int32_t T;
@@ -107,6 +113,8 @@ typedef struct moe_mxfp4_shape {
   int32_t force_gemm2_path;
   float swiglu_limit;
   float shared_scale;
+  float act_beta;
+  float act_linear_beta;
 } moe_mxfp4_shape;
 
 /*

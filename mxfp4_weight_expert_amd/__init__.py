@@ -21,6 +21,7 @@ MOE_OK = 0
 NUM_STAGES = 5  # route, sort + gate, GEMM1, GEMM2, finalize
 STAGE_NAMES = ("route", "sort_gate", "gemm1", "gemm2", "finalize")
 ADTYPE = {"bf16": 0, "mxfp8": 1}
+ACTIVATION = {"swiglu": 0, "situ": 1}
 GEMM2_PATH = {"auto": -1, "split": 0, "dense": 1}
 
 
@@ -34,7 +35,9 @@ class _Shape(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "T", "E", "E_global", "topk", "S", "H", "I", "block_n", "expert_offset", "activation",
         "a_dtype", "force_gemm2_path")] + [("swiglu_limit", ctypes.c_float),
-                                            ("shared_scale", ctypes.c_float)]
+                                            ("shared_scale", ctypes.c_float),
+                                            ("act_beta", ctypes.c_float),
+                                            ("act_linear_beta", ctypes.c_float)]
 
 
 _LAYOUT_U64 = ("total_bytes", "counters", "route_ids", "slot_expert", "slot_w", "range_counts",
@@ -94,12 +97,16 @@ class Shape:
     shared_scale: float = 1.0
     a_dtype: str = "bf16"
     force_gemm2_path: str = "auto"
+    activation: str = "swiglu"  # or "situ"
+    act_beta: float = 4.0  # SiTU caps (read only for "situ")
+    act_linear_beta: float = 25.0
 
     def to_c(self) -> _Shape:
         return _Shape(self.T, self.E, self.E_global, self.topk, self.S, self.H, self.I,
-                      self.block_n, self.expert_offset, 0, ADTYPE[self.a_dtype],
-                      GEMM2_PATH[self.force_gemm2_path], float(self.swiglu_limit),
-                      float(self.shared_scale))
+                      self.block_n, self.expert_offset, ACTIVATION[self.activation],
+                      ADTYPE[self.a_dtype], GEMM2_PATH[self.force_gemm2_path],
+                      float(self.swiglu_limit), float(self.shared_scale), float(self.act_beta),
+                      float(self.act_linear_beta))
 
     @property
     def Kp(self) -> int:

@@ -37,7 +37,11 @@ int check_shape(const moe_mxfp4_shape* s) {
   if (s->block_n != 16 && s->block_n != 32 && s->block_n != 64 && s->block_n != 128 &&
       s->block_n != 256)
     return MOE_ERR_UNSUPPORTED;
-  if (s->activation != MOE_ACT_SWIGLU) return MOE_ERR_UNSUPPORTED;
+  if (s->activation != MOE_ACT_SWIGLU && s->activation != MOE_ACT_SITU) return MOE_ERR_UNSUPPORTED;
+  if (s->activation == MOE_ACT_SITU &&
+      !(std::isfinite(s->act_beta) && s->act_beta > 0.0f && std::isfinite(s->act_linear_beta) &&
+        s->act_linear_beta > 0.0f))
+    return MOE_ERR_INVALID;
   if (s->a_dtype != MOE_ADTYPE_BF16 && s->a_dtype != MOE_ADTYPE_MXFP8) return MOE_ERR_UNSUPPORTED;
   // the W4A8 split GEMM2 keeps a row's whole K in registers: I <= 512
   if (s->a_dtype == MOE_ADTYPE_MXFP8 && s->I > 512) return MOE_ERR_UNSUPPORTED;
@@ -243,7 +247,12 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
                               : L.max_dense_tiles;
   }
   ga.max_units16 = L.max_units16;
-  ga.limit = s.swiglu_limit;
+  ga.act_fn.kind = s.activation;
+  ga.act_fn.limit = s.swiglu_limit;
+  ga.act_fn.beta = s.act_beta;
+  ga.act_fn.inv_beta = s.activation == MOE_ACT_SITU ? 1.0f / s.act_beta : 0.0f;
+  ga.act_fn.lb = s.act_linear_beta;
+  ga.act_fn.inv_lb = s.activation == MOE_ACT_SITU ? 1.0f / s.act_linear_beta : 0.0f;
   ga.act = reinterpret_cast<uint16_t*>(at(L.act));
   ga.y = reinterpret_cast<uint16_t*>(at(L.y));
   ga.a8 = s.a_dtype == MOE_ADTYPE_MXFP8;

@@ -201,6 +201,27 @@ __device__ __forceinline__ f32x4_t mfma_f4xf8(const uint4& w, uint32_t sa, const
 // ---------------------------------------------------------------- activation
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
+// Activation of the GEMM1 epilogue on the gate half g and the up half u.
+//   kind MOE_ACT_SWIGLU: silu(g) * u, with the clamp when limit > 0 (the
+//     Shape-template page, section 4; the Marlin page's swiglu limit);
+//   kind MOE_ACT_SITU: beta tanh(g / beta) sigmoid(g) * lb tanh(u / lb), the
+//     SiTU activation of the same section (printed there for beta = 4,
+//     lb = 25 as 2 tanh(g/4)(1 + tanh(g/2)) * 25 tanh(u/25)).
+// The reciprocals come from the host.
+struct ActArgs {
+  int kind;
+  float limit;
+  float beta, inv_beta, lb, inv_lb;
+};
+__device__ __forceinline__ float swiglu(float g, float u, float limit);
+__device__ __forceinline__ float act_apply(float g, float u, const ActArgs& a) {
+  if (a.kind == MOE_ACT_SITU) {
+    const float sg = 1.0f / (1.0f + __expf(-g));
+    return (a.beta * tanhf(g * a.inv_beta) * sg) * (a.lb * tanhf(u * a.inv_lb));
+  }
+  return swiglu(g, u, a.limit);
+}
+
 __device__ __forceinline__ float swiglu(float g, float u, float limit) {
   if (limit > 0.0f) {
     g = fminf(g, limit);

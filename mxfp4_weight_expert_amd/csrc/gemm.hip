@@ -234,7 +234,7 @@ __device__ __forceinline__ void gemm1_decode_items(
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ sorted_slot, int T, int H,
-    int I, int Kp, float limit, uint16_t* __restrict__ act, uint8_t* lds_scales) {
+    int I, int Kp, ActArgs actf, uint16_t* __restrict__ act, uint8_t* lds_scales) {
   constexpr int NT = 2 * TP;
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
@@ -292,8 +292,8 @@ __device__ __forceinline__ void gemm1_decode_items(
         const f32x4_t& ag = acc[2 * p];
         const f32x4_t& au = acc[2 * p + 1];
         uint2 pk;
-        pk.x = pack_bf16x2(swiglu(ag[0], au[0], limit), swiglu(ag[1], au[1], limit));
-        pk.y = pack_bf16x2(swiglu(ag[2], au[2], limit), swiglu(ag[3], au[3], limit));
+        pk.x = pack_bf16x2(act_apply(ag[0], au[0], actf), act_apply(ag[1], au[1], actf));
+        pk.y = pack_bf16x2(act_apply(ag[2], au[2], actf), act_apply(ag[3], au[3], actf));
         bst8(ars, aoff + p * 32, pk);
       }
     };
@@ -348,15 +348,15 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
-    const int32_t* __restrict__ sorted_slot, int T, int H, int I, int Kp, float limit,
+    const int32_t* __restrict__ sorted_slot, int T, int H, int I, int Kp, ActArgs actf,
     uint16_t* __restrict__ act) {
   extern __shared__ uint8_t lds_scales[];
   if (counters[ctr] * (I / 32) < kNarrowItemsBelow)
     gemm1_decode_items<D, NSMAX, 1, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
-                                        I, Kp, limit, act, lds_scales);
+                                        I, Kp, actf, act, lds_scales);
   else
     gemm1_decode_items<D, NSMAX, 2, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
-                                        I, Kp, limit, act, lds_scales);
+                                        I, Kp, actf, act, lds_scales);
 }
 
 // GEMM2 split path, decode shape, long K. Item = (chunk of at most
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const int32_t* __restrict__ units, const int32_t* __restrict__ counters,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slot, int T, int H,
-    int I, int Kp, float limit, uint8_t* __restrict__ actq, uint8_t* __restrict__ acts) {
+    int I, int Kp, ActArgs actf, uint8_t* __restrict__ actq, uint8_t* __restrict__ acts) {
   extern __shared__ uint8_t lds_scales[];
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
@@ -765,7 +765,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) a[4 * h + v] = swiglu(acc[2 * h][v], acc[2 * h + 1][v], limit);
+      for (int v = 0; v < 4; ++v) a[4 * h + v] = act_apply(acc[2 * h][v], acc[2 * h + 1][v], actf);
     const __amdgpu_buffer_rsrc_t qrs =
         make_rsrc(actq + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I);
     const __amdgpu_buffer_rsrc_t ars =
@@ -904,7 +904,7 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
 #define MOE_G1D(DD, NS, TL)                                                                       \
   hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, TL>), dim3(grid), dim3(kGemmBlock), lds, st,      \
                      a.x, a.w13, a.s13, units, ctr, a.counters, a.counts, a.sorted_slot, a.T, a.H,   \
-                     a.I, a.Kp, a.limit, a.act)
+                     a.I, a.Kp, a.act_fn, a.act)
     if (c32) {
       if (tl) MOE_G1D(2, 2, true); else if (d == 2) MOE_G1D(2, 2, false); else MOE_G1D(1, 2, false);
     } else {
@@ -965,7 +965,7 @@ hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
   hipLaunchKernelGGL((gemm1_decode_a8_kernel<DD, TL>), dim3(grid), dim3(kGemmBlock), lds, st, a.xq, \
                      a.xs, a.w13, a.s13, a.units16, a.counters, a.counts, a.sorted_slot, a.T, a.H,  \
                      a.I, a.Kp,                                                                 \
-                     a.limit, actq, a.act_scales)
+                     a.act_fn, actq, a.act_scales)
   if (tl) {
     MOE_G1A(2, true);
   } else {

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     const uint16_t* __restrict__ src, uint32_t src_bytes, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ s, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ sorted_slot, int I, int H,
-    int Kp, int sub, float limit, uint16_t* __restrict__ dst) {
+    int Kp, int sub, ActArgs actf, uint16_t* __restrict__ dst) {
   constexpr int kWR = 128 * MB;               // weight rows per tile
   constexpr int kRingN = MB == 2 ? 4 : 2;     // stages of loads in flight = stages per scale group
   constexpr int kWSt = kWR * 64;              // packed weight bytes of one K stage
@@ -405,10 +405,10 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 #pragma unroll
           for (int b4 = 0; b4 < 2; ++b4) {
             uint2 pk;
-            pk.x = pack_bf16x2(swiglu(c[4 * b4 + 0], c[4 * b4 + 8], limit),
-                               swiglu(c[4 * b4 + 1], c[4 * b4 + 9], limit));
-            pk.y = pack_bf16x2(swiglu(c[4 * b4 + 2], c[4 * b4 + 10], limit),
-                               swiglu(c[4 * b4 + 3], c[4 * b4 + 11], limit));
+            pk.x = pack_bf16x2(act_apply(c[4 * b4 + 0], c[4 * b4 + 8], actf),
+                               act_apply(c[4 * b4 + 1], c[4 * b4 + 9], actf));
+            pk.y = pack_bf16x2(act_apply(c[4 * b4 + 2], c[4 * b4 + 10], actf),
+                               act_apply(c[4 * b4 + 3], c[4 * b4 + 11], actf));
             const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * I * 2 +
                                  (fbase + 8 * b4 + 4 * h) * 2;
             bst8(ors, off, pk);
@@ -667,13 +667,13 @@ hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st) {
     const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 192), 1);
     hipLaunchKernelGGL((gemm_tiled_kernel<true, 3>), dim3(grid), dim3(kTiledThreads), 0, st, a.x,
                        x_bytes, a.w13, a.s13, a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp,
-                       sub, a.limit, a.act);
+                       sub, a.act_fn, a.act);
     return hipGetLastError();
   }
   const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128), 1);
   hipLaunchKernelGGL((gemm_tiled_kernel<true, 2>), dim3(grid), dim3(kTiledThreads), 0, st, a.x,
                      x_bytes, a.w13, a.s13, a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp,
-                     sub, a.limit, a.act);
+                     sub, a.act_fn, a.act);
   return hipGetLastError();
 }
 
@@ -695,7 +695,7 @@ hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
   const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles) * (a.H / 256), 1);
   hipLaunchKernelGGL((gemm_tiled_kernel<false, 2>), dim3(grid), dim3(kTiledThreads), 0, st, a.act,
                      static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2), a.w2, a.s2,
-                     a.dense_tiles, a.counters, a.sorted_slot, a.I, a.H, a.Kp, 1, a.limit, a.y);
+                     a.dense_tiles, a.counters, a.sorted_slot, a.I, a.H, a.Kp, 1, a.act_fn, a.y);
   return hipGetLastError();
 }
 
@@ -717,7 +717,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
     const uint8_t* __restrict__ src, uint32_t src_bytes, const uint8_t* __restrict__ srcs,
     uint32_t srcs_bytes, const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ counters,
-    const int32_t* __restrict__ sorted_slot, int I, int H, int Kp, int sub, float limit,
+    const int32_t* __restrict__ sorted_slot, int I, int H, int Kp, int sub, ActArgs actf,
     uint8_t* __restrict__ dstq, uint8_t* __restrict__ dsts, uint16_t* __restrict__ dsty) {
   __shared__ __attribute__((aligned(16))) uint8_t tok_lds[2 * kTok8Stage];
   __shared__ __attribute__((aligned(16))) uint8_t tsc_lds[2 * kTokScStage];
@@ -913,7 +913,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) a[4 * h + v] = swiglu(acc[h][nt][v], acc[2 + h][nt][v], limit);
+          for (int v = 0; v < 4; ++v) a[4 * h + v] = act_apply(acc[h][nt][v], acc[2 + h][nt][v], actf);
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
@@ -952,7 +952,7 @@ hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
                      static_cast<size_t>(8) * a.H, st, a.xq,
                      static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H), a.xs,
                      static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H / 32), a.w13, a.s13,
-                     a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp, sub, a.limit,
+                     a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp, sub, a.act_fn,
                      reinterpret_cast<uint8_t*>(a.act), a.act_scales, nullptr);
   return hipGetLastError();
 }

@@ -50,7 +50,7 @@ struct GemmArgs {
   int T, H, I, Kp, B, kmax_v, max_dense_tiles, max_units16, rows_pad;
   int Ep;  // local experts including the shared ones
   int dense_grid_tiles;  // tiles the dense GEMM2 grid is sized for (the kernels loop past it)
-  float limit;
+  ActArgs act_fn;  // GEMM1 epilogue activation
   uint16_t* act;  // [rows_pad, I] bf16 (W4A16), or E4M3 codes (W4A8)
   uint16_t* y;    // [rows_pad, H] bf16
   // W4A8 only (a8 != 0): MXFP8 x and act scales

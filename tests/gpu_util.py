@@ -26,7 +26,9 @@ def say(*a):
 def lib_shape(s: LayerShape, force: str = "auto") -> moe.Shape:
     return moe.Shape(T=s.T, E=s.E, E_global=s.E_g, topk=s.topk, H=s.H, I=s.I, block_n=s.B, S=s.S,
                      expert_offset=s.expert_offset, swiglu_limit=s.swiglu_limit,
-                     shared_scale=s.shared_scale, a_dtype=s.a_dtype, force_gemm2_path=force)
+                     shared_scale=s.shared_scale, a_dtype=s.a_dtype, force_gemm2_path=force,
+                     activation=s.activation, act_beta=s.act_beta,
+                     act_linear_beta=s.act_linear_beta)
 
 
 def bf16_dev(bits: np.ndarray) -> torch.Tensor:

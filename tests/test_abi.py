@@ -66,11 +66,24 @@ def _shape(**kw):
     (dict(S=9), 2), (dict(E=2040, E_global=2040, S=9), 2), (dict(E_global=3000, E=2000), 2),
     (dict(expert_offset=1), 1), (dict(T=-1), 1), (dict(E=0), 1), (dict(topk=0), 1),
     (dict(force_gemm2_path="dense", T=1 << 20), 2), (dict(H=8192 + 512), 2), (dict(I=8192 + 128), 2),
+    (dict(activation="situ", act_beta=0.0), 1), (dict(activation="situ", act_linear_beta=-1.0), 1),
+    (dict(activation="situ", act_beta=float("inf")), 1),
+    (dict(activation="situ", act_linear_beta=float("nan")), 1),
 ])
 def test_query_rejects_bad_shapes(kw, code):
     with pytest.raises(moe.MoeError) as ei:
         moe.query(_shape(**kw))
     assert ei.value.code == code
+
+
+def test_query_activation_kinds():
+    assert moe.query(_shape(activation="situ")) == moe.query(_shape())
+    # the SiTU caps are not read for SwiGLU
+    assert moe.query(_shape(act_beta=0.0, act_linear_beta=float("nan"))) > 0
+    bad = _shape().to_c()
+    bad.activation = 2
+    n = ctypes.c_uint64()
+    assert moe.load_library().moe_mxfp4_query(ctypes.byref(bad), ctypes.byref(n)) == 2
 
 
 @pytest.mark.parametrize("name", CONFIG_ORDER)

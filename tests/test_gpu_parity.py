@@ -44,6 +44,13 @@ SMALL = [
     LayerShape("split_k_odd", T=40, E=16, E_g=16, topk=4, H=512, I=640, B=32),
     LayerShape("split_sparse", T=8, E=64, E_g=64, topk=4, H=512, I=1024, B=16),
     LayerShape("split_dense_b32", T=64, E=8, E_g=8, topk=2, H=1024, I=1024, B=32, swiglu_limit=5.0),
+    # SiTU epilogue (K3.1 constants beta 4, linear beta 25, and other caps) on
+    # the decode GEMM1 with and without LDS token tiles and on the tiled GEMM1
+    LayerShape("situ_decode", T=64, E=32, E_g=32, topk=8, H=512, I=256, B=32, activation="situ"),
+    LayerShape("situ_sparse_b16", T=20, E=64, E_g=64, topk=4, H=1024, I=128, B=16,
+               activation="situ", act_beta=2.0, act_linear_beta=8.0),
+    LayerShape("situ_prefill", T=1024, E=16, E_g=16, topk=4, H=512, I=128, B=128, S=1,
+               activation="situ"),
 ]
 
 
@@ -90,6 +97,21 @@ def test_config_parity(name):
     torch.cuda.empty_cache()
 
 
+def test_situ_kimi_decode_shape():
+    """The K3.1 TP8 decode shape with its own activation, SiTU(4, 25)."""
+    s = CONFIGS["decode"].replace(activation="situ", name="decode_situ")
+    say(f"[config] {s.name}")
+    inp = make_inputs(s, config_seed("decode"))
+    dev = to_device(s, inp)
+    ref = oracle.reference_forward(s, inp, compute_out=False)
+    toks = _sample_tokens(s.T, 8, 13)
+    out, ws = run(s, dev)
+    check_maps(s, maps_np(s, ws), ref)
+    check_out(out_np(out)[toks], oracle.sampled_forward(s, inp, toks), f"{s.name} sampled tokens")
+    del out, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.fixture(scope="module")
 def kimi_weights():
     s = CONFIGS["decode"]
@@ -130,6 +152,10 @@ SMALL_A8 = [
                a_dtype="mxfp8"),
     LayerShape("a8_prefill_b256", T=700, E=6, E_g=6, topk=2, H=1536, I=256, B=256, a_dtype="mxfp8"),
     LayerShape("a8_one_token", T=1, E=32, E_g=32, topk=8, H=512, I=128, B=16, a_dtype="mxfp8"),
+    LayerShape("a8_situ", T=64, E=16, E_g=16, topk=4, H=512, I=256, B=32, activation="situ",
+               a_dtype="mxfp8"),
+    LayerShape("a8_situ_prefill", T=700, E=6, E_g=6, topk=2, H=512, I=256, B=128,
+               activation="situ", act_beta=3.0, act_linear_beta=10.0, a_dtype="mxfp8"),
 ]
 
 
