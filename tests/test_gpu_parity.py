@@ -252,6 +252,30 @@ def test_large_sort_maps(s):
         check_out(out_np(out)[toks], oracle.sampled_forward(s, inp, toks), f"{s.name}/{force}")
 
 
+# The largest supported sizes: H = I = 8192 (the longest K loops and the
+# largest LDS scale blocks) on the decode, split, tiled and generic dense
+# GEMM paths, and E + S = 2048 local experts through both sort paths.
+@pytest.mark.parametrize("s", [
+    LayerShape("max_hi_decode", T=9, E=2, E_g=2, topk=2, H=8192, I=8192, B=16),
+    LayerShape("max_hi_prefill", T=160, E=2, E_g=2, topk=1, H=8192, I=8192, B=128),
+    LayerShape("max_experts_small_sort", T=200, E=2047, E_g=2047, topk=32, H=512, I=128, B=32, S=1),
+    LayerShape("max_experts_large_sort", T=300, E=2047, E_g=2047, topk=32, H=512, I=128, B=16, S=1),
+], ids=lambda s: s.name)
+def test_maximum_sizes(s):
+    say(f"[max] {s.name}: {s.T * s.Kp} slots, H={s.H} I={s.I} E'={s.Ep}")
+    inp = make_inputs(s, 4321)
+    dev = to_device(s, inp)
+    toks = _sample_tokens(s.T, 2, 9)
+    want = oracle.sampled_forward(s, inp, toks)  # the same under every GEMM2 path
+    for force in ("auto", "split", "dense"):
+        ref = oracle.reference_forward(s, inp, force_path=FORCES[force], compute_out=False)
+        out, ws = run(s, dev, force)
+        check_maps(s, maps_np(s, ws, force), ref)
+        check_out(out_np(out)[toks], want, f"{s.name}/{force}")
+        del out, ws
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("rows,row_bytes", [(16, 64), (48, 192), (256, 1792), (768, 1792)])
 def test_prepack_layout(rows, row_bytes):
