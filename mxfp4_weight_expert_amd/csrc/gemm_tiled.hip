@@ -233,6 +233,14 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
         for (int q = 0; q < kRingN; ++q) sb[q * kWR + srho[i]] = v[q];
       }
     };
+    // one 16-byte piece p of store_stage: token chunks p < 4, then weight chunks
+    auto store_piece = [&](int b, int sl, int p) {
+      if (p < 4) {
+        *reinterpret_cast<uint4*>(tok_lds + b * kTokStage + tok_off(p * 32 + lr, lc)) = tv[sl][p];
+      } else if (p - 4 < kWPer) {
+        *reinterpret_cast<uint4*>(w_lds + b * kWSt + c_off<kWR>((p - 4) * 128 + wr, wc)) = wv[sl][p - 4];
+      }
+    };
     auto store_stage = [&](int b, int sl) {
       uint8_t* tb = tok_lds + b * kTokStage;
 #pragma unroll
@@ -266,7 +274,10 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     // One K stage with register slot sl = kb % kRingN: multiply the stage in
     // LDS buffer kb & 1, move stage kb+1 (slot (sl+1) % kRingN, loaded
     // kRingN - 1 stages ago) into the other buffer (read last in stage kb-1,
-    // which every wave finished before the previous barrier), refill slot sl
+    // which every wave finished before the previous barrier) one 16-byte
+    // piece per sub-step group, so the writes overlap the MFMAs instead of
+    // bunching up before the barrier (2.71 -> 2.58 ms at 32k tokens on
+    // MI355X; 7 pieces per thread for 384-row tiles, 6 for 256), refill slot sl
     // with stage kb + kRingN (near the end the last stage again: loaded,
     // never used). Scales move in groups of kRingN stages: the first stage of
     // group g loads group g + 1, its last stage stores it to the other scale
@@ -343,8 +354,10 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
         __builtin_amdgcn_sched_barrier(0);
         read_tok(t8 + 1, bn);
         dec(t8 + 1, an);
+        store_piece(b ^ 1, (sl + 1) % kRingN, t8);  // next stage, one piece per group
         mfmas();
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+        if (t8 < 4 + kWPer) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
 #pragma unroll
         for (int k = 0; k < 2 * MB; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -354,7 +367,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
         rotate();
       }
       __builtin_amdgcn_sched_barrier(0);
-      store_stage(b ^ 1, (sl + 1) % kRingN);
+      if (4 + kWPer > 7) store_piece(b ^ 1, (sl + 1) % kRingN, 7);
       if (sl == kRingN - 1) store_group(kb / kRingN + 1);
       __builtin_amdgcn_sched_barrier(0);
       load_stage(min(kb + kRingN, last), sl);
