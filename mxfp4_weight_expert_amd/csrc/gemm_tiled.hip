@@ -830,6 +830,16 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * kPkBlock);
     };
+    // piece p of store_stage: token chunks 0, 1, the scale word 2, weight chunks 3, 4
+    auto store_piece = [&](int b, int p) {
+      if (p < 2) {
+        *reinterpret_cast<uint4*>(tok_lds + b * kTok8Stage + tok8_off(p * 64 + lr, lc)) = tv[p];
+      } else if (p == 2) {
+        *reinterpret_cast<uint32_t*>(tsc_lds + b * kTokScStage + sr * 4) = sv;
+      } else {
+        *reinterpret_cast<uint4*>(w_lds + b * kWStage + w_off((p - 3) * 128 + wr, wc)) = wv[p - 3];
+      }
+    };
     auto store_stage = [&](int b) {
       uint8_t* tb = tok_lds + b * kTok8Stage;
 #pragma unroll
@@ -890,10 +900,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
       for (int nt = 0; nt < 4; ++nt) {
         __builtin_amdgcn_sched_barrier(0);
         if (nt < 3) read_x(nt + 1, x0n, x1n, bsn);
+        store_piece(b ^ 1, nt);  // next stage, one piece per tile group (as in the bf16 kernel)
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[mt][nt] = mfma_f4xf8(af[mt], as[mt], x0c, x1c, bsc, acc[mt][nt]);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads first
+        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
         __builtin_amdgcn_sched_barrier(0);
         if (nt < 3) {
@@ -903,7 +915,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-      store_stage(b ^ 1);
+      store_piece(b ^ 1, 4);
       __builtin_amdgcn_sched_barrier(0);
       load_stage(min(kb + 2, last));
       __builtin_amdgcn_sched_barrier(0);
