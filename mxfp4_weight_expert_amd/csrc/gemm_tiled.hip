@@ -233,6 +233,11 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
         for (int q = 0; q < kRingN; ++q) sb[q * kWR + srho[i]] = v[q];
       }
     };
+    // one 16-byte load p of load_stage (same order as the stores below)
+    auto load_piece = [&](int kb, int sl, int p) {
+      if (p < 4) tv[sl][p] = bld16s(srs, toff[p], kb * 256);
+      else if (p - 4 < kWPer) wv[sl][p - 4] = bld16s(wrs, woff, kb * kPkBlock + (p - 4) * wstep);
+    };
     // one 16-byte piece p of store_stage: token chunks p < 4, then weight chunks
     auto store_piece = [&](int b, int sl, int p) {
       if (p < 4) {
@@ -277,9 +282,10 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
     // which every wave finished before the previous barrier) one 16-byte
     // piece per sub-step group, so the writes overlap the MFMAs instead of
     // bunching up before the barrier (2.71 -> 2.58 ms at 32k tokens on
-    // MI355X; 7 pieces per thread for 384-row tiles, 6 for 256), refill slot sl
-    // with stage kb + kRingN (near the end the last stage again: loaded,
-    // never used). Scales move in groups of kRingN stages: the first stage of
+    // MI355X; 7 pieces per thread for 384-row tiles, 6 for 256), and refill
+    // slot sl (free since its stage went to LDS) with stage kb + kRingN one
+    // piece per group too, a further 2.8% (near the end the last stage again:
+    // loaded, never used). Scales move in groups of kRingN stages: the first stage of
     // group g loads group g + 1, its last stage stores it to the other scale
     // buffer (last read in group g - 1). Loads retire in issue order; the
     // pinned order keeps each wait to what it needs.
@@ -355,9 +361,11 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
         read_tok(t8 + 1, bn);
         dec(t8 + 1, an);
         store_piece(b ^ 1, (sl + 1) % kRingN, t8);  // next stage, one piece per group
+        load_piece(min(kb + kRingN, last), sl, t8);  // slot sl is free: in LDS since stage kb-1
         mfmas();
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
         if (t8 < 4 + kWPer) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // LDS write
+        if (t8 < 4 + kWPer) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // global load
 #pragma unroll
         for (int k = 0; k < 2 * MB; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -370,7 +378,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
       if (4 + kWPer > 7) store_piece(b ^ 1, (sl + 1) % kRingN, 7);
       if (sl == kRingN - 1) store_group(kb / kRingN + 1);
       __builtin_amdgcn_sched_barrier(0);
-      load_stage(min(kb + kRingN, last), sl);
+      if (4 + kWPer > 7) load_piece(min(kb + kRingN, last), sl, 7);
       if (sl == 0) load_group(min(kb / kRingN + 1, lastg));
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
