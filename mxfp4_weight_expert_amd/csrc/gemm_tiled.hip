@@ -838,6 +838,12 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
 #pragma unroll
       for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * kPkBlock);
     };
+    // piece p of load_stage (same order as store_piece)
+    auto load_piece = [&](int kb, int p) {
+      if (p < 2) tv[p] = bld16(srs, toff[p] + kb * 128);
+      else if (p == 2) sv = bld4(ssc, soff + kb * 4);
+      else wv[p - 3] = ld16(wsrc[p - 3] + kb * kPkBlock);
+    };
     // piece p of store_stage: token chunks 0, 1, the scale word 2, weight chunks 3, 4
     auto store_piece = [&](int b, int p) {
       if (p < 2) {
@@ -909,11 +915,13 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
         __builtin_amdgcn_sched_barrier(0);
         if (nt < 3) read_x(nt + 1, x0n, x1n, bsn);
         store_piece(b ^ 1, nt);  // next stage, one piece per tile group (as in the bf16 kernel)
+        load_piece(min(kb + 2, last), nt);  // the piece's register is free once stored
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[mt][nt] = mfma_f4xf8(af[mt], as[mt], x0c, x1c, bsc, acc[mt][nt]);
         __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads first
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
         __builtin_amdgcn_sched_barrier(0);
         if (nt < 3) {
@@ -925,7 +933,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
       __builtin_amdgcn_sched_barrier(0);
       store_piece(b ^ 1, 4);
       __builtin_amdgcn_sched_barrier(0);
-      load_stage(min(kb + 2, last));
+      load_piece(min(kb + 2, last), 4);
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     }
