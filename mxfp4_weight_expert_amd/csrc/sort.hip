@@ -318,13 +318,19 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ r
   const int tid = threadIdx.x;
   // 1) per expert: exclusive scan over the ranges, in place; neighbouring
   // threads read neighbouring experts (coalesced), 32 ranges per round with
-  // the round's loads in flight together
+  // the round's loads in flight together. The next round's loads are issued
+  // before this round's stores (they never overlap; written in this order
+  // because the compiler keeps loads behind stores to the same array).
   for (int e = tid; e < Ep; e += 1024) {
     int run = 0;
-    for (int r0 = 0; r0 < n_ranges; r0 += 32) {
-      int c[32];
+    int c[32], n[32];
 #pragma unroll
-      for (int j = 0; j < 32; ++j) c[j] = range_counts[static_cast<size_t>(min(r0 + j, n_ranges - 1)) * Ep + e];
+    for (int j = 0; j < 32; ++j) c[j] = range_counts[static_cast<size_t>(min(j, n_ranges - 1)) * Ep + e];
+    for (int r0 = 0; r0 < n_ranges; r0 += 32) {
+      const int r1 = r0 + 32;
+#pragma unroll
+      for (int j = 0; j < 32; ++j)
+        n[j] = range_counts[static_cast<size_t>(min(r1 + j, n_ranges - 1)) * Ep + e];
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
         if (r0 + j < n_ranges) {
@@ -332,6 +338,8 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ r
           run += c[j];
         }
       }
+#pragma unroll
+      for (int j = 0; j < 32; ++j) c[j] = n[j];
     }
     s_cnt[e] = run;
   }
