@@ -302,11 +302,62 @@ __global__ __launch_bounds__(64) void sort_count_kernel(const int32_t* __restric
   for (int i = lane; i < Ep; i += kWave) range_counts[static_cast<size_t>(r) * Ep + i] = h[i];
 }
 
-// One block of 1024 threads. Turns range_counts ([n_ranges][Ep]) into
-// per-range bases, writes counts, offsets, the chunk table and the chunk
-// count, then runs the GEMM2 gate.
-__global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ range_counts,
-                                                         int n_ranges, int Ep, int B, int force_path,
+// Per expert, the exclusive scan of its per-range counts, in place
+// (range_counts [n_ranges][Ep] becomes each range's first row offset within
+// the expert), and the expert's total row count into counts[e]. A block
+// covers 64 experts (one per lane, so loads are coalesced across the lanes)
+// and its four waves cover four quarters of the ranges: each wave sums its
+// quarter, the quarters' totals are scanned in LDS, and each wave rewrites
+// its quarter starting from its prefix.
+__global__ __launch_bounds__(256) void sort_range_scan_kernel(int32_t* __restrict__ range_counts,
+                                                              int n_ranges, int Ep,
+                                                              int32_t* __restrict__ counts) {
+  __shared__ int32_t s_part[4][kWave];
+  const int lane = lane_id(), q = wave_index();
+  const int e = blockIdx.x * kWave + lane;
+  const bool live = e < Ep;
+  const int ec = live ? e : Ep - 1;
+  const int r_lo = n_ranges * q / 4, r_hi = n_ranges * (q + 1) / 4;
+  auto at = [&](int r) -> int32_t* { return range_counts + static_cast<size_t>(r) * Ep + ec; };
+  int sum = 0;
+  for (int r0 = r_lo; r0 < r_hi; r0 += 32) {
+    int c[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = *at(min(r0 + j, r_hi - 1));
+#pragma unroll
+    for (int j = 0; j < 32; ++j) sum += r0 + j < r_hi ? c[j] : 0;
+  }
+  s_part[q][lane] = sum;
+  __syncthreads();
+  int run = 0;
+  for (int k = 0; k < q; ++k) run += s_part[k][lane];
+  if (q == 3 && live) counts[e] = run + sum;
+  if (!live || r_lo >= r_hi) return;  // no barrier follows
+  // rewrite the quarter; the next round's loads go out before this round's
+  // stores (they never overlap)
+  int c[32], n[32];
+#pragma unroll
+  for (int j = 0; j < 32; ++j) c[j] = *at(min(r_lo + j, r_hi - 1));
+  for (int r0 = r_lo; r0 < r_hi; r0 += 32) {
+    const int r1 = r0 + 32;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) n[j] = *at(min(r1 + j, r_hi - 1));
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (r0 + j < r_hi) {
+        *at(r0 + j) = run;
+        run += c[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) c[j] = n[j];
+  }
+}
+
+// One block of 1024 threads. From the per-expert totals (counts, written by
+// sort_range_scan_kernel), writes counts, offsets, the chunk table and the
+// chunk count, then runs the GEMM2 gate.
+__global__ __launch_bounds__(1024) void sort_scan_kernel(int Ep, int B, int force_path,
                                                          int32_t* __restrict__ counts,
                                                          int32_t* __restrict__ offsets,
                                                          int32_t* __restrict__ vinfo,
@@ -316,33 +367,8 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int32_t* __restrict__ r
   __shared__ int32_t s_cnt[kMaxExperts];
   __shared__ int32_t s_off[kMaxExperts];
   const int tid = threadIdx.x;
-  // 1) per expert: exclusive scan over the ranges, in place; neighbouring
-  // threads read neighbouring experts (coalesced), 32 ranges per round with
-  // the round's loads in flight together. The next round's loads are issued
-  // before this round's stores (they never overlap; written in this order
-  // because the compiler keeps loads behind stores to the same array).
-  for (int e = tid; e < Ep; e += 1024) {
-    int run = 0;
-    int c[32], n[32];
-#pragma unroll
-    for (int j = 0; j < 32; ++j) c[j] = range_counts[static_cast<size_t>(min(j, n_ranges - 1)) * Ep + e];
-    for (int r0 = 0; r0 < n_ranges; r0 += 32) {
-      const int r1 = r0 + 32;
-#pragma unroll
-      for (int j = 0; j < 32; ++j)
-        n[j] = range_counts[static_cast<size_t>(min(r1 + j, n_ranges - 1)) * Ep + e];
-#pragma unroll
-      for (int j = 0; j < 32; ++j) {
-        if (r0 + j < n_ranges) {
-          range_counts[static_cast<size_t>(r0 + j) * Ep + e] = run;
-          run += c[j];
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < 32; ++j) c[j] = n[j];
-    }
-    s_cnt[e] = run;
-  }
+  // 1) the per-expert totals
+  for (int e = tid; e < Ep; e += 1024) s_cnt[e] = counts[e];
   __syncthreads();
   // 2) expert offsets and the chunk table, then the gate
   block_scan_experts(s_cnt, Ep, B, counts, offsets, vinfo, units16, counters, s_off);
@@ -392,9 +418,12 @@ hipError_t launch_sort_and_gate(const SortArgs& a, hipStream_t st) {
                      a.Ep, a.n_ranges, a.range_counts);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, st, a.range_counts, a.n_ranges,
-                     a.Ep, a.B, a.force_path, a.counts, a.offsets, a.vinfo, a.units16, a.counters,
-                     a.dense_tiles);
+  hipLaunchKernelGGL(sort_range_scan_kernel, dim3((a.Ep + kWave - 1) / kWave), dim3(256), 0, st,
+                     a.range_counts, a.n_ranges, a.Ep, a.counts);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(sort_scan_kernel, dim3(1), dim3(1024), 0, st, a.Ep, a.B, a.force_path,
+                     a.counts, a.offsets, a.vinfo, a.units16, a.counters, a.dense_tiles);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(sort_scatter_kernel, dim3(a.n_ranges), dim3(64), lds, st, a.slot_expert,
