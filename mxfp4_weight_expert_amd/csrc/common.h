@@ -19,10 +19,10 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxShared = 8;
 constexpr int kMaxExperts = 2048;  // E + S
 // Slots per sort range (one wave each) above kSmallSlots. Smaller ranges
-// give the count and scatter kernels more waves but the single-block scan
-// more per-range counts: at 524k slots 4096 / 2048 / 1024 took 106 / 95 /
-// 109 us on MI355X.
-constexpr int kRangeSlots = 2048;
+// give the count and scatter kernels more waves and the range scan more
+// per-range counts: at 524k slots, with the multi-block range scan, 2048 /
+// 1024 / 512 took 78 / 67 / 70 us for the whole sort on MI355X.
+constexpr int kRangeSlots = 1024;
 constexpr int kSmallSlots = 8192;  // up to this many slots the sort runs in one block
 constexpr int kGateTau = 64;       // dense GEMM2 when rows >= kGateTau * touched experts
 constexpr int kDenseMT = 128;      // dense-path row tile
