@@ -114,12 +114,13 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
 }
 
 // Token tile of one K step in LDS, shared by the four waves of a block
-// (they work on the same chunk): 16 * NS rows x 256 bytes
-// (tok_lds_step<NS>). 16-byte chunk c
-// of tile row rr sits at rr * 256 + 16 * (c ^ tswz(rr)): the 32 lanes that
-// read one fragment (rows r = 0..15, chunks 4g + j, g = 0..1) and the 32
-// lanes that write two rows fall on distinct 16-byte bank groups of a
-// 512-byte bank line.
+// (they work on the same chunk): 16 * NS rows x 256 bytes, tok_lds_step<NS>()
+// bytes per buffer. 16-byte chunk c of tile row rr sits at
+// rr * 256 + 16 * (c ^ tswz(rr)): the 32 lanes that read one fragment (rows
+// r = 0..15, chunks 4g + j, g = 0..1) and the 32 lanes that write two rows
+// fall on distinct 16-byte bank groups of a 512-byte bank line. The stream
+// needs an even step count (D = 2, no tail): H / 128 always is, and the
+// split GEMM2 takes this path only when I / 128 is.
 template <int NS>
 constexpr int tok_lds_step() {
   return 16 * NS * 256;
