@@ -235,6 +235,17 @@ __device__ __forceinline__ uint4 ld16(const void* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// N consecutive dwords (1 <= N <= 4) at a 4-byte aligned address: exactly 4N
+// bytes, e.g. one weight row's I/32 scale bytes. The array's last row ends
+// the caller's buffer, so a wider load there would read past its end.
+template <int N>
+__device__ __forceinline__ void ld_dwords(const void* p, uint32_t (&d)[N]) {
+  static_assert(N >= 1 && N <= 4, "1 to 4 dwords");
+  const uint32_t* q = static_cast<const uint32_t*>(p);
+#pragma unroll
+  for (int i = 0; i < N; ++i) d[i] = q[i];
+}
+
 // 16-byte weight load. NT = true marks it non-temporal: for weights that
 // this layer call reads exactly once (their expert's rows fit one work
 // unit), so the streamed bytes do not displace reusable lines in L2 and the

@@ -510,7 +510,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
     auto seg = [&](auto ntw) {
       constexpr bool NTW = decltype(ntw)::value;
       uint4 w[kStreamAhead][NKB];
-      uint4 sc[kStreamAhead];  // the lane row's scale bytes (I/32 <= 16)
+      uint32_t sc[kStreamAhead][NKB];  // the lane row's I/32 scale bytes
       // prologue in slot order (pinned): the loop head then sees the same
       // pending-load order on entry as on every later iteration
   #pragma unroll
@@ -518,7 +518,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
         const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
   #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-        sc[a] = ld16(sp + ti * sstride);
+        ld_dwords(sp + ti * sstride, sc[a]);
         __builtin_amdgcn_sched_barrier(0);
       }
       for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
@@ -527,10 +527,9 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
         for (int a = 0; a < kStreamAhead; ++a) {
           const int i = i0 + a;
           f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
   #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) {
-            const float s = e8m0_scale_operand((sw[kb] >> (8 * g)) & 0xffu);
+            const float s = e8m0_scale_operand((sc[a][kb] >> (8 * g)) & 0xffu);
             const uint32_t ww[4] = {w[a][kb].x, w[a][kb].y, w[a][kb].z, w[a][kb].w};
   #pragma unroll
             for (int j = 0; j < 4; ++j)
@@ -540,7 +539,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
           const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
   #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-          sc[a] = ld16(sp + ti * sstride);
+          ld_dwords(sp + ti * sstride, sc[a]);
           res[a].x = pack_bf16x2(acc[0], acc[1]);
           res[a].y = pack_bf16x2(acc[2], acc[3]);
           __builtin_amdgcn_sched_barrier(0);
@@ -829,13 +828,13 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
     auto seg = [&](auto ntw) {
       constexpr bool NTW = decltype(ntw)::value;
       uint4 w[kStreamAhead][NKB];
-      uint4 sc[kStreamAhead];
+      uint32_t sc[kStreamAhead][NKB];  // the lane row's I/32 scale bytes
   #pragma unroll
       for (int a = 0; a < kStreamAhead; ++a) {
         const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
   #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-        sc[a] = ld16(sp + ti * sstride);
+        ld_dwords(sp + ti * sstride, sc[a]);
         __builtin_amdgcn_sched_barrier(0);
       }
       for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
@@ -844,15 +843,14 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
         for (int a = 0; a < kStreamAhead; ++a) {
           const int i = i0 + a;
           f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          const uint32_t sw[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
   #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            acc = mfma_f4xf8(w[a][kb], (sw[kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb], acc);
+            acc = mfma_f4xf8(w[a][kb], (sc[a][kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb], acc);
           __builtin_amdgcn_sched_barrier(0);
           const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
   #pragma unroll
           for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-          sc[a] = ld16(sp + ti * sstride);
+          ld_dwords(sp + ti * sstride, sc[a]);
           res[a].x = pack_bf16x2(acc[0], acc[1]);
           res[a].y = pack_bf16x2(acc[2], acc[3]);
           __builtin_amdgcn_sched_barrier(0);
