@@ -203,6 +203,11 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_shape* shape, moe_mxfp4_ws_layout
  * the call overwrites it and its contents after the call are the maps
  * listed in moe_mxfp4_ws_layout.
  *
+ * Alignment: x_dev, out_dev, w13_dev, s13_dev, w2_dev and s2_dev 16 bytes;
+ * router_logits_dev, topk_ids_dev and topk_w_dev 4 bytes; shared_logits_dev
+ * 2 bytes (MOE_ERR_INVALID otherwise). Each input is read only within the
+ * sizes listed above.
+ *
  * Exactly one of router_logits_dev and (topk_ids_dev, topk_w_dev) must be
  * non-NULL. Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE
  * before any launch; MOE_ERR_HIP if a launch fails (earlier kernels of the

@@ -163,6 +163,17 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
       s2_dev == nullptr || out_dev == nullptr || workspace_dev == nullptr)
     return MOE_ERR_INVALID;
   if (s.S > 0 && shared_logits_dev == nullptr) return MOE_ERR_INVALID;
+  // x, out, the weights and their scales are accessed with 16-byte vector
+  // loads and stores at multiples of 16 bytes from these pointers; the
+  // routing inputs with 4-byte loads, the shared logits with 2-byte loads.
+  auto aligned = [](const void* p, uintptr_t a) {
+    return reinterpret_cast<uintptr_t>(p) % a == 0;  // NULL passes
+  };
+  if (!aligned(x_dev, 16) || !aligned(out_dev, 16) || !aligned(w13_dev, 16) ||
+      !aligned(s13_dev, 16) || !aligned(w2_dev, 16) || !aligned(s2_dev, 16) ||
+      !aligned(router_logits_dev, 4) || !aligned(topk_ids_dev, 4) || !aligned(topk_w_dev, 4) ||
+      !aligned(shared_logits_dev, 2))
+    return MOE_ERR_INVALID;
   moe_mxfp4_ws_layout L;
   carve(&s, &L);
   if (workspace_bytes < L.total_bytes || reinterpret_cast<uintptr_t>(workspace_dev) % kAlign != 0)

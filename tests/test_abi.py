@@ -107,18 +107,21 @@ def test_kimi_k31_virtual_expert_bound_from_layout():
     assert L["kmax_v"] == 1024
 
 
-def _fwd(shape, logits=1, ids=None, w=None, ws=256, wsb=1 << 40, shared=None):
+def _fwd(shape, logits=1024, ids=None, w=None, ws=256, wsb=1 << 40, shared=None, x=256, w13=256,
+         s13=256, w2=256, s2=256, out=256):
+    """moe_mxfp4_forward on fake device addresses: only calls that fail
+    validation before any launch may be made here."""
     lib = moe.load_library()
     P = ctypes.c_void_p
-    return lib.moe_mxfp4_forward(P(256), P(logits) if logits else None, P(ids) if ids else None,
-                                 P(w) if w else None, P(shared) if shared else None, P(256), P(256),
-                                 P(256), P(256), ctypes.byref(shape.to_c()), P(256),
+    return lib.moe_mxfp4_forward(P(x), P(logits) if logits else None, P(ids) if ids else None,
+                                 P(w) if w else None, P(shared) if shared else None, P(w13), P(s13),
+                                 P(w2), P(s2), ctypes.byref(shape.to_c()), P(out),
                                  P(ws) if ws else None, ctypes.c_uint64(wsb), None)
 
 
 def test_forward_rejects_before_launch():
     s = _shape()
-    assert _fwd(s, logits=1, ids=512, w=512) == 1       # both routing inputs
+    assert _fwd(s, logits=1024, ids=512, w=512) == 1    # both routing inputs
     assert _fwd(s, logits=None) == 1                     # neither
     assert _fwd(s, logits=None, ids=512) == 1            # ids without weights
     assert _fwd(s, wsb=1024) == 3                        # workspace too small
@@ -127,6 +130,16 @@ def test_forward_rejects_before_launch():
     assert _fwd(_shape(S=1), shared=None) == 1           # shared experts need logits
     assert _fwd(_shape(H=100)) == 2
     assert _fwd(_shape(T=0), ws=None) == 0               # empty call: nothing to do
+    # misaligned buffers (each valid otherwise: the workspace is too small,
+    # so an aligned call would stop at MOE_ERR_WORKSPACE before any launch)
+    assert _fwd(s, wsb=1024) == 3
+    for kw in ({"x": 264}, {"out": 264}, {"w13": 260}, {"s13": 264}, {"w2": 258}, {"s2": 260},
+               {"logits": 1026}):
+        assert _fwd(s, wsb=1024, **kw) == 1, kw
+    assert _fwd(s, wsb=1024, logits=None, ids=514, w=512) == 1
+    assert _fwd(s, wsb=1024, logits=None, ids=512, w=514) == 1
+    assert _fwd(_shape(S=1), wsb=1024, shared=513) == 1
+    assert _fwd(_shape(S=1), wsb=1024, shared=514) == 3  # 2-byte aligned is enough
 
 
 def test_prepack_rejects_before_launch():
