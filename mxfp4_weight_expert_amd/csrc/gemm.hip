@@ -24,7 +24,13 @@ namespace moe {
 
 namespace {
 constexpr int kGemmBlock = 256;  // 4 waves, one item each at a time
-constexpr int kMaxGrid = 256 * 8;
+// Grid cap of the item-strided decode kernels: one block per four items up
+// to 16 blocks per CU, more than can be resident, so blocks start as others
+// finish and waves end within about one item of each other. Against a cap
+// of 8 per CU (2 to 3 items per wave) it took the T512 E256 H7168 I2048
+// split GEMMs from 693 / 416 to 675 / 403 us on MI355X; the T64 and T256
+// decode shapes did not change.
+constexpr int kMaxGrid = 256 * 16;
 }  // namespace
 
 // ---------------------------------------------------------------------------
