@@ -13,8 +13,10 @@ namespace moe {
 
 // Total order on float logits, larger first: map the bits so that unsigned
 // comparison follows the float order. -0.0 is folded into +0.0 first so the
-// two compare equal (the tie then goes to the lower id).
+// two compare equal (the tie then goes to the lower id). Every NaN maps to
+// 0, below -inf (0x007FFFFF): a NaN logit ranks last, NaNs by lower id.
 __device__ __forceinline__ uint32_t order_bits(float f) {
+  if (__builtin_isnan(f)) return 0u;
   uint32_t u = __float_as_uint(f + 0.0f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
@@ -55,7 +57,8 @@ __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a <
 
 // One wave per token. The token's logits become 64-bit keys (ordered logit
 // << 32 | ~id), NPL per lane (E_global <= 64 * NPL); larger key = larger
-// logit, equal logits: lower id. Every lane keeps its four largest keys
+// logit, equal logits: lower id. A NaN's key is ~id alone: above the empty
+// key 0 and below every number's. Every lane keeps its four largest keys
 // below a ceiling, sorted. Each of topk rounds finds the wave's largest head
 // key (a 32-bit DPP maximum over the ordered logits, and over the ids only
 // when several lanes tie) and pops it from its lane; a lane whose list runs
@@ -123,8 +126,10 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
   const bool sel = lane < topk;
   const float lg = unorder_bits(static_cast<uint32_t>(mine >> 32));
   const int id = static_cast<int>(~static_cast<uint32_t>(mine));
+  // A selected NaN (only when fewer than topk logits are numbers) gets
+  // weight 0; infinities follow IEEE arithmetic.
   const float lmax_f = __shfl(lg, 0, kWave);
-  const float ex = sel ? expf(lg - lmax_f) : 0.0f;
+  const float ex = (sel && !__builtin_isnan(lg)) ? expf(lg - lmax_f) : 0.0f;
   const float sum = wave_sum_f(ex);
   const int Kp = topk + S;
   if (sel) {

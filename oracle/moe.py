@@ -46,13 +46,22 @@ def route_topk_softmax(logits: np.ndarray, topk: int):
     (the [T, top-k] ids the routing kernel reads, [SHAPE] section 5; the
     StandardTopKOutput of [SHARED]) without defining it; the configs ask for
     "softmax top-k renormalised".
+    Non-finite logits (the pages do not treat them; this is the reading):
+    a NaN logit ranks below every number, -inf included, NaNs among
+    themselves by lower id, so it is selected only when fewer than topk
+    logits are numbers; a selected NaN takes no part in the softmax
+    (weight 0). Infinities follow IEEE arithmetic: exp(l - l_max) with
+    l_max = +inf, or with every selected logit -inf, is NaN, and so are
+    then all of the token's weights.
     Returns ids int32 [T, topk] (global expert ids) and w float64 [T, topk].
     """
     lg = np.asarray(logits, dtype=np.float32).astype(np.float64)
+    # argsort places NaN after every number, in index order (stable)
     order = np.argsort(-lg, axis=1, kind="stable")[:, :topk]
     sel = np.take_along_axis(lg, order, axis=1)
-    ex = np.exp(sel - sel[:, :1])
-    return order.astype(np.int32), ex / ex.sum(axis=1, keepdims=True)
+    with np.errstate(invalid="ignore"):
+        ex = np.where(np.isnan(sel), 0.0, np.exp(sel - sel[:, :1]))
+        return order.astype(np.int32), ex / ex.sum(axis=1, keepdims=True)
 
 
 def local_map(ids: np.ndarray, E: int, expert_offset: int) -> np.ndarray:

@@ -52,16 +52,22 @@ def _unpack_nibbles(packed: np.ndarray) -> np.ndarray:
     return out
 
 
+# The value of each of the 16 E2M1 codes (index = code), from e2m1_decode.
+E2M1_VALUES = e2m1_decode(np.arange(16))
+
+
 def dequant_mxfp4(packed: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """MXFP4 rows -> float64.
 
     packed [..., K/2] uint8, scales [..., K/32] uint8 -> W [..., K] with
-    W[..., k] = E2M1(code k) * 2^(scales[..., k // 32] - 127).
+    W[..., k] = E2M1(code k) * 2^(scales[..., k // 32] - 127): each code's
+    value from the 16-entry table, times its block's scale.
     """
     codes = _unpack_nibbles(packed)
     k = codes.shape[-1]
     assert scales.shape[-1] * MX_BLOCK == k, (scales.shape, k)
-    return e2m1_decode(codes) * np.repeat(e8m0_decode(scales), MX_BLOCK, axis=-1)
+    vals = E2M1_VALUES[codes].reshape(codes.shape[:-1] + (k // MX_BLOCK, MX_BLOCK))
+    return (vals * e8m0_decode(scales)[..., None]).reshape(codes.shape)
 
 
 def e4m3_decode(codes) -> np.ndarray:

@@ -175,6 +175,26 @@ def test_topk_weights_are_softmax_of_selected():
     assert np.allclose(w.sum(1), 1.0, rtol=0, atol=1e-15)
 
 
+def test_topk_non_finite_logits():
+    """NaN ranks below -inf (ties by lower id) and a selected NaN has weight
+    0; infinities follow IEEE arithmetic in exp(l - l_max)."""
+    nan, inf = np.nan, np.inf
+    lg = np.array([[1.0, nan, 0.5, -inf, 2.0],
+                   [nan, nan, 1.0, nan, nan],
+                   [-inf, 0.0, nan, -inf, nan],
+                   [inf, 0.0, 1.0, nan, -1.0],
+                   [nan, nan, nan, nan, nan],
+                   [-inf, -inf, nan, 3.0, -inf]], np.float32)
+    ids, w = oracle.route_topk_softmax(lg, 3)
+    assert ids.tolist() == [[4, 0, 2], [2, 0, 1], [1, 0, 3], [0, 2, 1], [0, 1, 2], [3, 0, 1]]
+    e = np.exp([0.0, -1.0, -1.5])
+    assert np.allclose(w[0], e / e.sum(), rtol=1e-15, atol=0)
+    assert w[1].tolist() == [1.0, 0.0, 0.0]
+    assert w[2].tolist() == [1.0, 0.0, 0.0]
+    assert np.all(np.isnan(w[3])) and np.all(np.isnan(w[4]))
+    assert w[5].tolist() == [1.0, 0.0, 0.0]
+
+
 def test_local_map_offset_and_masked_ids():
     ids = np.array([[-1, 0, 447, 448, 449, 895, 896, 1000]])
     got = oracle.local_map(ids, 448, 448)
@@ -288,7 +308,7 @@ def _pack_rows(codes):
     return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
 
 
-def _onehot_layer():
+def _onehot_layer(H=64, I=32, E=3, S=1):
     """A layer whose weights are one-hot rows, so its output has a closed form.
 
     Expert e: gate row i reads x[pg_e(i)] times cg_e, up row i reads
@@ -296,7 +316,6 @@ def _onehot_layer():
     The other scale group of each row holds a different exponent, so a
     wrong group index changes the result.
     """
-    H, I, E, S = 64, 32, 3, 1
     Ep = E + S
     gcode, gscale = 3, 126   # 1.5 * 2^-1 = 0.75
     ucode, uscale = 6, 125   # 4.0 * 2^-2 = 1.0
@@ -489,6 +508,152 @@ def test_mxfp8_activation_path_quantises_x_per_token():
     q, sc = oracle.quant_mxfp8(oracle.bf16_bits_to_f64(inp["x"]))
     assert np.array_equal(res["xq"], q) and np.array_equal(res["xs"], sc)
     assert res["xq"].shape == (s.T, s.H) and res["xs"].shape == (s.T, s.H // 32)
+
+
+# ------------------------------------- W4A8: where MXFP8 enters the layer
+# The W4A8 layer quantises x to MXFP8 per 32 elements along H before GEMM1,
+# and the activation output act per 32 elements along I after the activation
+# and before GEMM2 (the Shape-template page, section 7, names MXFP8
+# activations for the decode MoE; the recipe is OCP MX). This pin computes
+# that composition by hand on a one-hot layer: block scales from math.frexp,
+# element rounding by torch's float8_e4m3fn cast, and the activation from
+# math.exp, sharing nothing with the oracle's quantiser.
+
+def _e4m3_midpoint(v32: np.ndarray) -> np.ndarray:
+    """True where a float32 value lies exactly halfway between two E4M3
+    values (where rounding float64 -> float32 -> E4M3 could differ from a
+    direct rounding)."""
+    a = np.abs(v32.astype(np.float64))
+    m, e = np.frexp(a)
+    normal = a >= 2.0 ** -6
+    mid_n = (np.floor(m * 32) == m * 32) & (np.floor(m * 16) != m * 16)
+    k = a * 2.0 ** 10
+    mid_s = (np.floor(k) == k) & (np.mod(k, 2) == 1)
+    return np.where(normal, mid_n, mid_s) & (a <= 448.0)
+
+
+def _mxfp8_by_hand(v: np.ndarray) -> np.ndarray:
+    """MXFP8 round trip along the last axis, blocks of 32: shared exponent
+    floor(log2 amax) - 8 (biased, clamped to [0, 254]), elements rounded to
+    E4M3 by torch with saturation at 448."""
+    v = np.asarray(v, np.float64)
+    out = np.zeros_like(v)
+    for idx in np.ndindex(v.shape[:-1]):
+        for b in range(v.shape[-1] // 32):
+            blk = v[idx][32 * b: 32 * b + 32]
+            amax = float(np.max(np.abs(blk)))
+            if amax == 0.0:
+                continue
+            _, e = math.frexp(amax)  # amax = m 2^e, m in [0.5, 1)
+            se = min(max(e - 1 - 8 + 127, 0), 254) - 127
+            scaled = np.clip(blk / 2.0 ** se, -448.0, 448.0)
+            s32 = scaled.astype(np.float32)
+            assert not np.any(_e4m3_midpoint(s32) & (s32.astype(np.float64) != scaled))
+            q = torch.from_numpy(s32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+            out[idx][32 * b: 32 * b + 32] = q * 2.0 ** se
+    return out
+
+
+def _w4a8_onehot_case():
+    """32 tokens, every one routed to both local experts plus one shared
+    expert, so each expert holds 32 rows (a wrong quantisation axis over
+    rows is computable and must fail). H = I = 64: two MX blocks along each."""
+    H, I, E, S = 64, 64, 2, 1
+    _, _, _, _, pg, pu, cgv, cu, c2, wts = _onehot_layer(H, I, E, S)
+    T = 32
+    rng = np.random.default_rng(47)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32) * np.float32(1.7))
+    xf = oracle.bf16_bits_to_f64(x)
+    # a saturating block: amax 480 scales to 480 > 448 and saturates
+    x[3, 0:32] = f32_to_bf16_bits(np.linspace(-2.0, 2.0, 32).astype(np.float32))
+    x[3, 7] = f32_to_bf16_bits(np.array([480.0], np.float32))[0]
+    # an underflowing block: elements far below amax / 2^8 round to zero
+    x[5, 32:64] = f32_to_bf16_bits((np.arange(32) % 7 - 3).astype(np.float32) * np.float32(2 ** -20))
+    x[5, 40] = f32_to_bf16_bits(np.array([3.0], np.float32))[0]
+    xf = oracle.bf16_bits_to_f64(x)
+    ids = np.tile(np.array([[0, 1]], np.int32), (T, 1))
+    w = (rng.random((T, 2)) + 0.1).astype(np.float32)
+    sh = f32_to_bf16_bits((rng.standard_normal((T, 1)) * 2).astype(np.float32))
+    shape = LayerShape("cf_a8", T=T, E=E, E_g=E, topk=2, H=H, I=I, B=16, S=S, shared_scale=1.0,
+                       a_dtype="mxfp8", mode="ids")
+    inp = dict(x=x, logits=np.zeros((T, E), np.float32), shared=sh, topk_ids=ids, topk_w=w, **wts)
+    # the closed form, by hand
+    xd = _mxfp8_by_hand(xf)
+    assert np.any(xd != xf)                          # x quantisation changes x
+    assert xd[3, 7] == 448.0                         # saturated
+    assert np.all(xd[5, 32:64][np.arange(32) != 8] == 0.0) and xd[5, 40] == 3.0  # underflowed
+    shared_w = scipy.special.expit(oracle.bf16_bits_to_f64(sh))[:, 0]
+    out = np.zeros((T, H))
+    for e, wt in ((0, w[:, 0].astype(np.float64)), (1, w[:, 1].astype(np.float64)), (2, shared_w)):
+        act = np.zeros((T, I))
+        for t in range(T):
+            for i in range(I):
+                g = cgv(e) * xd[t, pg(e, i)]
+                u = cu * xd[t, pu(e, i)]
+                act[t, i] = g / (1.0 + math.exp(-g)) * u
+        actq = _mxfp8_by_hand(act)
+        assert np.any(actq != act)
+        out += wt[:, None] * c2 * actq[:, np.arange(H) % I]
+    return shape, inp, out
+
+
+def test_w4a8_composition_closed_form():
+    shape, inp, want = _w4a8_onehot_case()
+    got = oracle.reference_forward(shape, inp)["out"]
+    assert np.max(np.abs(got - want)) <= 1e-12 * np.max(np.abs(want))
+
+
+def _w4a8_closed_form_error():
+    try:
+        test_w4a8_composition_closed_form()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_w4a8_planted_mistakes_are_caught(monkeypatch):
+    assert not _w4a8_closed_form_error()
+    orig_glu, orig_act = omoe.expert_glu, omoe._activations
+    sig = lambda v: 1.0 / (1.0 + np.exp(-v))
+    rt = lambda v: omx.dequant_mxfp8(*omx.quant_mxfp8(v))
+    # 1. act not quantised before GEMM2
+    monkeypatch.setattr(omoe, "expert_glu",
+                        lambda xr, W13, W2, limit=0.0, act_mxfp8=False, **kw:
+                        orig_glu(xr, W13, W2, limit, False, **kw))
+    assert _w4a8_closed_form_error()
+
+    # 2. the GEMM1 outputs g and u quantised before the activation instead of act
+    def glu_h_quant(xr, W13, W2, limit=0.0, act_mxfp8=False, **kw):
+        I = W13.shape[0] // 2
+        h = xr @ W13.T
+        g, u = rt(h[:, :I]), rt(h[:, I:])
+        return (g * sig(g) * u) @ W2.T
+    monkeypatch.setattr(omoe, "expert_glu", glu_h_quant)
+    assert _w4a8_closed_form_error()
+
+    # 3. act quantised along the rows (tokens) instead of along I
+    def glu_act_along_t(xr, W13, W2, limit=0.0, act_mxfp8=False, **kw):
+        I = W13.shape[0] // 2
+        h = xr @ W13.T
+        g, u = h[:, :I], h[:, I:]
+        return rt((g * sig(g) * u).T).T @ W2.T
+    monkeypatch.setattr(omoe, "expert_glu", glu_act_along_t)
+    assert _w4a8_closed_form_error()
+    monkeypatch.setattr(omoe, "expert_glu", orig_glu)
+
+    # 4. x quantised along T instead of along H
+    def act_x_along_t(shape, inp):
+        x = omoe.bf16_bits_to_f64(inp["x"])
+        return rt(x.T).T, None, None
+    monkeypatch.setattr(omoe, "_activations", act_x_along_t)
+    assert _w4a8_closed_form_error()
+
+    # 5. x not quantised
+    monkeypatch.setattr(omoe, "_activations",
+                        lambda shape, inp: (omoe.bf16_bits_to_f64(inp["x"]), None, None))
+    assert _w4a8_closed_form_error()
+    monkeypatch.setattr(omoe, "_activations", orig_act)
+    assert not _w4a8_closed_form_error()
 
 
 # ----------------------------------------------- planted mistakes are caught
