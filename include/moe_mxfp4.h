@@ -29,9 +29,14 @@
  *   - Shapes are passed by host pointer and read during the call only.
  *   - Every function returns MOE_OK (0) or one of the MOE_ERR_* codes below;
  *     validation errors are returned before anything is enqueued.
- *   - Matrices are row-major. Nibble-packed operands hold two E2M1 codes per
- *     byte, the low nibble being the element with the even K index. Scales
- *     are E8M0 bytes (value 2^(e-127)), one per 32 consecutive K elements.
+ *   - Nibble-packed operands hold two E2M1 codes per byte, the low nibble
+ *     being the element with the even K index. Scales are E8M0 bytes
+ *     (value 2^(e-127)), one per 32 consecutive K elements.
+ *   - Activations, router inputs, scales and outputs are row-major. The
+ *     weight codes w13 and w2 are read in the packed layout that
+ *     moe_mxfp4_prepack writes from the row-major one; the shape's
+ *     weight_layout field states it (MOE_WEIGHTS_PACKED), and a forward call
+ *     tagged otherwise is rejected before any launch.
  */
 #ifndef MOE_MXFP4_H
 #define MOE_MXFP4_H
@@ -60,6 +65,17 @@ extern "C" {
 #define MOE_ADTYPE_BF16 0  /* W4A16: bf16 activations, bf16 MFMA */
 #define MOE_ADTYPE_MXFP8 1 /* W4A8: activations quantised to MXFP8 (E4M3 elements,
                               one E8M0 per 32 K), scaled f8f6f4 MFMA */
+
+/* Layout of the weight codes w13_dev / w2_dev (moe_mxfp4_shape.weight_layout).
+ * MOE_WEIGHTS_ROW_MAJOR: [E', rows, K/2] row-major, as drawn or stored; the
+ * forward calls do not read it (MOE_ERR_UNSUPPORTED): pass it through
+ * moe_mxfp4_prepack once, when the weights are loaded.
+ * MOE_WEIGHTS_PACKED: the output of moe_mxfp4_prepack (1 KB blocks of 16 rows
+ * x 64 bytes), the only layout the forward calls read. The repack is the kind
+ * the Marlin MoE kernel page (section 2) applies to its MXFP4 weights so that
+ * its loads match the MMA fragments. */
+#define MOE_WEIGHTS_ROW_MAJOR 0
+#define MOE_WEIGHTS_PACKED 1
 
 /* GEMM2 path forcing (tests): -1 lets the device gate decide. */
 #define MOE_GEMM2_AUTO (-1)
@@ -97,6 +113,10 @@ extern "C" {
  *   act_beta        SiTU gate cap beta (> 0, finite; the K3.1 value is 4)
  *   act_linear_beta SiTU up cap (> 0, finite; the K3.1 value is 25). Both
  *                   are read only for MOE_ACT_SITU, which ignores swiglu_limit
+ *   weight_layout   MOE_WEIGHTS_PACKED (required by the forward calls) or
+ *                   MOE_WEIGHTS_ROW_MAJOR (accepted by query and
+ *                   workspace_layout, which do not read weights); other
+ *                   values are MOE_ERR_INVALID
  */
 typedef struct moe_mxfp4_shape {
   int32_t T;
@@ -115,6 +135,7 @@ typedef struct moe_mxfp4_shape {
   float shared_scale;
   float act_beta;
   float act_linear_beta;
+  int32_t weight_layout;
 } moe_mxfp4_shape;
 
 /*
@@ -175,7 +196,8 @@ typedef struct moe_mxfp4_ws_layout {
 /*
  * Check a shape and return the workspace size it needs.
  * Host only; touches no device. Returns MOE_OK, MOE_ERR_INVALID (null
- * pointer, negative sizes, offset range outside E_global) or
+ * pointer, negative sizes, offset range outside E_global, unknown
+ * weight_layout) or
  * MOE_ERR_UNSUPPORTED (H % 512, I % 128, H or I > 8192, block_n, topk, S, E + S > 2048,
  * T * K' > 2^23, unknown activation or a_dtype, MXFP8 with I > 512).
  */
@@ -194,7 +216,8 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_shape* shape, moe_mxfp4_ws_layout
  *   topk_w_dev         float [T, topk], or NULL (given together with ids)
  *   shared_logits_dev  bf16 [T, S] (needed when S > 0, else ignored)
  *   w13_dev            uint8 [E', 2I, H/2]: rows [0, I) gate, [I, 2I) up,
- *                      in the packed layout of moe_mxfp4_prepack
+ *                      in the packed layout of moe_mxfp4_prepack (the shape's
+ *                      weight_layout must say MOE_WEIGHTS_PACKED)
  *   s13_dev            uint8 [E', 2I, H/32] (row-major, not packed)
  *   w2_dev             uint8 [E', H, I/2], packed like w13_dev
  *   s2_dev             uint8 [E', H, I/32] (row-major, not packed)
@@ -209,8 +232,8 @@ int moe_mxfp4_workspace_layout(const moe_mxfp4_shape* shape, moe_mxfp4_ws_layout
  * sizes listed above.
  *
  * Exactly one of router_logits_dev and (topk_ids_dev, topk_w_dev) must be
- * non-NULL. Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE
- * before any launch; MOE_ERR_HIP if a launch fails (earlier kernels of the
+ * non-NULL. Errors: MOE_ERR_INVALID, MOE_ERR_UNSUPPORTED (also for
+ * weight_layout MOE_WEIGHTS_ROW_MAJOR), MOE_ERR_WORKSPACE before any launch; MOE_ERR_HIP if a launch fails (earlier kernels of the
  * chain may have run). Calls on different streams need different
  * workspaces. Duplicate routed ids within a token (possible only in ids
  * mode) each get their own row.

@@ -23,6 +23,7 @@ STAGE_NAMES = ("route", "sort_gate", "gemm1", "gemm2", "finalize")
 ADTYPE = {"bf16": 0, "mxfp8": 1}
 ACTIVATION = {"swiglu": 0, "situ": 1}
 GEMM2_PATH = {"auto": -1, "split": 0, "dense": 1}
+WEIGHT_LAYOUT = {"row_major": 0, "packed": 1}
 
 
 class MoeError(RuntimeError):
@@ -37,7 +38,8 @@ class _Shape(ctypes.Structure):
         "a_dtype", "force_gemm2_path")] + [("swiglu_limit", ctypes.c_float),
                                             ("shared_scale", ctypes.c_float),
                                             ("act_beta", ctypes.c_float),
-                                            ("act_linear_beta", ctypes.c_float)]
+                                            ("act_linear_beta", ctypes.c_float),
+                                            ("weight_layout", ctypes.c_int32)]
 
 
 _LAYOUT_U64 = ("total_bytes", "counters", "route_ids", "slot_expert", "slot_w", "range_counts",
@@ -100,13 +102,14 @@ class Shape:
     activation: str = "swiglu"  # or "situ"
     act_beta: float = 4.0  # SiTU caps (read only for "situ")
     act_linear_beta: float = 25.0
+    weight_layout: str = "packed"  # w13/w2 as prepack() returns them
 
     def to_c(self) -> _Shape:
         return _Shape(self.T, self.E, self.E_global, self.topk, self.S, self.H, self.I,
                       self.block_n, self.expert_offset, ACTIVATION[self.activation],
                       ADTYPE[self.a_dtype], GEMM2_PATH[self.force_gemm2_path],
                       float(self.swiglu_limit), float(self.shared_scale), float(self.act_beta),
-                      float(self.act_linear_beta))
+                      float(self.act_linear_beta), WEIGHT_LAYOUT[self.weight_layout])
 
     @property
     def Kp(self) -> int:

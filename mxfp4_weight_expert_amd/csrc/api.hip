@@ -29,6 +29,8 @@ int check_shape(const moe_mxfp4_shape* s) {
   if (static_cast<int64_t>(s->expert_offset) + s->E > s->E_global) return MOE_ERR_INVALID;
   if (!std::isfinite(s->swiglu_limit) || !std::isfinite(s->shared_scale)) return MOE_ERR_INVALID;
   if (s->force_gemm2_path < -1 || s->force_gemm2_path > 1) return MOE_ERR_INVALID;
+  if (s->weight_layout != MOE_WEIGHTS_ROW_MAJOR && s->weight_layout != MOE_WEIGHTS_PACKED)
+    return MOE_ERR_INVALID;
   if (s->topk > kMaxTopK || s->topk > s->E_global || s->S > kMaxShared) return MOE_ERR_UNSUPPORTED;
   if (s->E + s->S > kMaxExperts || s->E_global > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->H % 512 != 0 || s->I % 128 != 0) return MOE_ERR_UNSUPPORTED;
@@ -155,6 +157,8 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   const int rc = check_shape(shape);
   if (rc != MOE_OK) return rc;
   const moe_mxfp4_shape& s = *shape;
+  // the GEMMs read w13 and w2 only in the packed layout
+  if (s.weight_layout != MOE_WEIGHTS_PACKED) return MOE_ERR_UNSUPPORTED;
   const bool ids_mode = topk_ids_dev != nullptr || topk_w_dev != nullptr;
   if (ids_mode == (router_logits_dev != nullptr)) return MOE_ERR_INVALID;
   if (ids_mode && (topk_ids_dev == nullptr || topk_w_dev == nullptr)) return MOE_ERR_INVALID;

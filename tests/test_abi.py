@@ -107,6 +107,19 @@ def test_kimi_k31_virtual_expert_bound_from_layout():
     assert L["kmax_v"] == 1024
 
 
+def _no_device():
+    """True when no HIP device is visible. Counting devices does not
+    initialise the GPU. The rejection tests below pass fabricated device
+    addresses: they must never run where a kernel could be dispatched if a
+    validation check regressed."""
+    import torch
+    return torch.cuda.device_count() == 0
+
+
+fabricated_addresses = pytest.mark.skipif(
+    not _no_device(), reason="fabricated device addresses: run only where no GPU is visible")
+
+
 def _fwd(shape, logits=1024, ids=None, w=None, ws=256, wsb=1 << 40, shared=None, x=256, w13=256,
          s13=256, w2=256, s2=256, out=256):
     """moe_mxfp4_forward on fake device addresses: only calls that fail
@@ -119,6 +132,7 @@ def _fwd(shape, logits=1024, ids=None, w=None, ws=256, wsb=1 << 40, shared=None,
                                  P(ws) if ws else None, ctypes.c_uint64(wsb), None)
 
 
+@fabricated_addresses
 def test_forward_rejects_before_launch():
     s = _shape()
     assert _fwd(s, logits=1024, ids=512, w=512) == 1    # both routing inputs
@@ -142,6 +156,32 @@ def test_forward_rejects_before_launch():
     assert _fwd(_shape(S=1), wsb=1024, shared=514) == 3  # 2-byte aligned is enough
 
 
+@fabricated_addresses
+def test_forward_rejects_row_major_weights_before_launch():
+    # a valid call in every other respect (workspace large enough, aligned):
+    # the row-major tag alone stops it
+    assert _fwd(_shape(weight_layout="row_major")) == 2
+    assert _fwd(_shape(weight_layout="row_major"), ws=None) == 2  # before the pointer checks
+    assert _fwd(_shape(T=0, weight_layout="row_major"), ws=None) == 2
+    bad = _shape().to_c()
+    bad.weight_layout = 7
+    lib = moe.load_library()
+    P = ctypes.c_void_p
+    assert lib.moe_mxfp4_forward(P(256), P(1024), None, None, None, P(256), P(256), P(256), P(256),
+                                 ctypes.byref(bad), P(256), P(256), ctypes.c_uint64(1 << 40),
+                                 None) == 1
+
+
+def test_weight_layout_tag_in_query():
+    # query and workspace_layout read no weights: both tags give the same size
+    assert moe.query(_shape(weight_layout="row_major")) == moe.query(_shape())
+    bad = _shape().to_c()
+    bad.weight_layout = -1
+    n = ctypes.c_uint64()
+    assert moe.load_library().moe_mxfp4_query(ctypes.byref(bad), ctypes.byref(n)) == 1
+
+
+@fabricated_addresses
 def test_prepack_rejects_before_launch():
     lib = moe.load_library()
     P = ctypes.c_void_p
