@@ -1,18 +1,34 @@
 #!/usr/bin/env python3
 """Throughput of the fused MXFP4 MoE layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config decode] [--no-sweep]
 
 A step is one whole layer call (routing, shared append, sort, gate, GEMM1 +
 SwiGLU, GEMM2, finalize) on one batch of seeded synthetic inputs that are
-resident in HBM before timing starts. Steps are replayed from a captured
-graph and alternate between two copies of the weights, so no step finds the
-previous step's weights in L2 or the Infinity Cache. Prints one JSON line.
+resident in HBM before timing starts. Steps are replayed from captured
+graphs that cycle through enough copies of the weights that no step finds
+the weights it reads in L2 or the 256 MB Infinity Cache (cold weights, as
+the decode page measures). Each replay is bracketed by its own pair of HIP
+events; the K replays together by one more pair and a synchronisation on
+both sides. Prints one JSON line.
 
-The dominant kernel (GEMM1) is also timed live with HIP events recorded by
-the library between the stages of the chain; its algorithmic bytes (decode
-workloads) or FLOPs (prefill) per launch over that time give the roofline
-fraction. The CPU baseline is the fp64 oracle on a bounded token sample.
+The headline is the 64-token decode layer (T=64, E=896, top-16, H=3584,
+I=384, BlockN=32): `value` is its tokens/s over the K timed steps. The line
+also carries, under "configs", the same measurement for the EP decode, the
+shared-expert + clamp layer and the 32k-token prefill in bf16 and W4A8
+(skip with --no-sweep). For every workload:
+  * layer time: median, p10 and p90 of the per-replay times, and the mean;
+  * layer_roofline: the whole layer's algorithmic HBM bytes (decode shapes:
+    touched experts' weights and scales, x, out, router logits) or FLOPs
+    (prefill: 6 R H I) over the median replay time, against 8 TB/s HBM or
+    the dense MFMA peak of the compute type;
+  * kernels: GEMM1 and GEMM2 timed with HIP events recorded by the library
+    between the stages of the same chain on the stream the kernels run on,
+    their algorithmic bytes or FLOPs per launch over that time;
+  * roofline (headline) is the dominant kernel's (GEMM1), with its HBM
+    traffic from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary when
+    the kernel sources still hash to the profiled version;
+  * cpu_baseline: the fp64 oracle timed on a bounded token sample.
 """
 from __future__ import annotations
 
@@ -28,6 +44,11 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
 METRIC = "MoE layer tokens/s and µs/layer; achieved HBM GB/s (decode), MFMA % (prefill)"
+# The Infinity Cache holds 256 MB: cycle through enough weight copies that
+# the other copies' touched weights between two uses of one copy exceed
+# twice that.
+MALL_FLUSH_BYTES = 512 << 20
+SWEEP = [("decode_ep", "bf16"), ("shared_clamp", "bf16"), ("prefill", "bf16"), ("prefill", "mxfp8")]
 
 
 def parse():
@@ -36,17 +57,25 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--a-dtype", default="bf16", choices=["bf16", "mxfp8"],
-                   help="activation format: bf16 (W4A16) or mxfp8 (W4A8)")
+                   help="activation format of the headline workload: bf16 (W4A16) or mxfp8 (W4A8)")
     p.add_argument("--activation", default=None, choices=["swiglu", "situ"],
                    help="GEMM1 epilogue (default: the workload's; situ uses beta 4, linear beta 25)")
     p.add_argument("--config", default="decode",
-                   help="tiny | decode | decode_ep | shared_clamp | prefill")
+                   help="headline workload: tiny | decode | decode_ep | shared_clamp | prefill")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="measure only the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
-                   help="target CPU time of one oracle sample run")
+                   help="target CPU time of the headline's oracle sample run")
+    p.add_argument("--sweep-cpu-seconds", type=float, default=6.0,
+                   help="target CPU time of each sweep workload's oracle sample run")
     p.add_argument("--calib-copy-mib", type=int, default=0,
                    help="first run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
 def measured_traffic(config: str, kernel: str):
@@ -63,9 +92,11 @@ def measured_traffic(config: str, kernel: str):
                 if not line.startswith("traffic-json: "):
                     continue
                 rec = json.loads(line[len("traffic-json: "):])
-                if rec.get("workload") != config or not rec.get("kernel", "").startswith("moe::" + kernel.split("<")[0]):
+                rk = rec.get("kernel", "")
+                rk = rk[len("moe::"):] if rk.startswith("moe::") else rk
+                if rec.get("workload") != config or rk.split("<")[0] != kernel.split("<")[0]:
                     continue
-                if ("<true" in kernel) != ("<true" in rec["kernel"]):
+                if ("<true" in kernel) != ("<true" in rk):  # tiled GEMM1 vs tiled dense GEMM2
                     continue
                 h = hashlib.sha256()
                 for src in rec["src"]:
@@ -95,7 +126,6 @@ def workload_name(s) -> str:
 def cpu_baseline(s, inp, target_s: float) -> dict:
     """The oracle (as it stands) on a prefix of the tokens, doubling the prefix
     until one run takes at least half the target time."""
-    import numpy as np
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -121,29 +151,25 @@ def cpu_baseline(s, inp, target_s: float) -> dict:
                       f"NumPy, one run of {dt:.1f} s"}
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported: the layer "
-              "runs on one GPU, and splitting experts over GPUs (expert_offset) is the "
-              "caller's part", file=sys.stderr)
-        sys.exit(2)
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v), q))
+
+
+def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) -> dict:
+    """One workload: graph-replayed layer steps, stage kernels, roofline."""
     import numpy as np
     import torch
 
     import mxfp4_weight_expert_amd as moe
     from workloads import CONFIGS, config_seed, make_inputs
 
-    moe.load_library()  # fails loudly if the HIP library is not built
-    s = CONFIGS[args.config].replace(a_dtype=args.a_dtype)
-    if args.activation:
-        s = s.replace(activation=args.activation)
+    s = CONFIGS[name].replace(a_dtype=a_dtype)
+    if activation:
+        s = s.replace(activation=activation)
     a8 = s.a_dtype == "mxfp8"
-    dev_id = 0
-    torch.cuda.set_device(dev_id)
-    log = lambda *a: print(*a, file=sys.stderr, flush=True)
-    log(f"[bench] generating {args.config} inputs")
-    inp = make_inputs(s, config_seed(args.config))
+    log(f"[bench] {name}/{a_dtype}: generating inputs")
+    inp = make_inputs(s, config_seed(name))
     shp = moe.Shape(T=s.T, E=s.E, E_global=s.E_g, topk=s.topk, H=s.H, I=s.I, block_n=s.B, S=s.S,
                     expert_offset=s.expert_offset, swiglu_limit=s.swiglu_limit,
                     shared_scale=s.shared_scale, a_dtype=s.a_dtype, activation=s.activation,
@@ -155,33 +181,34 @@ def main():
     x = bf16(inp["x"])
     logits = torch.from_numpy(inp["logits"]).cuda()
     shared = bf16(inp["shared"]) if s.S else None
-    wbytes = sum(inp[k].nbytes for k in ("w13", "s13", "w2", "s2"))
-    nsets = 2 if wbytes >= (1 << 30) else max(2, int((1 << 30) // max(wbytes, 1)) + 1)
-    nsets = min(nsets, 64)
-    sets = []
-    for _ in range(nsets):  # weights prepacked once, outside the timed region (load-time step)
-        sets.append({k: (moe.prepack(torch.from_numpy(inp[k]).cuda()) if k in ("w13", "w2")
-                         else torch.from_numpy(inp[k]).cuda()) for k in ("w13", "s13", "w2", "s2")})
+
+    def upload():  # prepacked once, outside the timed region (a load-time step)
+        return {k: (moe.prepack(torch.from_numpy(inp[k]).cuda()) if k in ("w13", "w2")
+                    else torch.from_numpy(inp[k]).cuda()) for k in ("w13", "s13", "w2", "s2")}
+
+    sets = [upload()]
     ws = torch.empty(moe.query(shp), dtype=torch.uint8, device="cuda")
     out = torch.empty((s.T, s.H), dtype=torch.bfloat16, device="cuda")
-    del inp["w13"], inp["w2"]
 
     def step(i, stream=None):
-        w = sets[i % nsets]
+        w = sets[i % len(sets)]
         moe.forward(x, w["w13"], w["s13"], w["w2"], w["s2"], shp, router_logits=logits,
                     shared_logits=shared, out=out, workspace=ws, stream=stream)
 
-    if args.calib_copy_mib > 0:
-        n = args.calib_copy_mib << 20
-        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
-
-    # eager warm-up, then one graph per weight set
-    for i in range(nsets):
+    # one eager call gives the routing: touched experts decide how many
+    # weight copies keep every replay's weights cold
+    step(0)
+    torch.cuda.synchronize()
+    maps = moe.read_maps(ws, shp)
+    gate = [int(v) for v in maps["counters"][4:8].cpu().tolist()]
+    U, R = gate[1], gate[2]
+    w13_e = 2 * s.I * (s.H // 2 + s.H // 32)  # W13 codes + scales of one expert
+    w2_e = s.H * (s.I // 2 + s.I // 32)
+    touched = max(U * (w13_e + w2_e), 1)
+    nsets = min(64, max(2, -(-MALL_FLUSH_BYTES // touched) + 1))
+    while len(sets) < nsets:
+        sets.append(upload())
+    for i in range(1, nsets):
         step(i)
     torch.cuda.synchronize()
     graphs = []
@@ -192,103 +219,172 @@ def main():
             step(i)
         graphs.append(g)
     torch.cuda.synchronize()
-
     for i in range(args.warmup):
         graphs[i % nsets].replay()
     torch.cuda.synchronize()
 
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] {name}/{a_dtype}: timing {args.steps} steps ({nsets} weight sets)")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     e0.record()
     for i in range(args.steps):
+        ev[i][0].record()
         graphs[i % nsets].replay()
+        ev[i][1].record()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    log(f"[bench] {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us/step)")
+    rep_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    med = pct(rep_us, 50)
+    log(f"[bench] {name}/{a_dtype}: {ms_per_step * 1e3:.1f} us/step mean, median {med:.1f} us "
+        f"(wall {wall / args.steps * 1e6:.1f} us/step)")
 
-    # Per-stage timing of the chain (eager, same kernels), HIP events on the
-    # library's stream.
+    # Stage kernels: the same chain with the library's per-stage HIP events
+    # on its stream (eager calls, same weight rotation).
     nst = moe.NUM_STAGES
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
+    sev = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)] for _ in range(args.steps)]
     for i in range(min(args.warmup, 3)):
         step(i)
     torch.cuda.synchronize()
     for i in range(args.steps):
         w = sets[i % nsets]
-        moe.forward_timed(evs[i], x, w["w13"], w["s13"], w["w2"], w["s2"], shp,
+        moe.forward_timed(sev[i], x, w["w13"], w["s13"], w["w2"], w["s2"], shp,
                           router_logits=logits, shared_logits=shared, out=out, workspace=ws)
     torch.cuda.synchronize()
-    stage_ms = [sum(evs[i][k].elapsed_time(evs[i][k + 1]) for i in range(args.steps)) / args.steps
+    stage_ms = [sum(sev[i][k].elapsed_time(sev[i][k + 1]) for i in range(args.steps)) / args.steps
                 for k in range(nst)]
     stages = {n: round(v * 1e3, 2) for n, v in zip(moe.STAGE_NAMES, stage_ms)}
-    log(f"[bench] stage us: {stages}")
-
-    maps = moe.read_maps(ws, shp)
-    gate = maps["counters"][4:8].cpu().tolist()
+    log(f"[bench] {name}/{a_dtype}: stage us {stages}")
     counts = maps["counts"].cpu().numpy()
     U_routed = int(np.count_nonzero(counts[: s.E]))
-    U = int(gate[1])
-    R = int(gate[2])
-    gemm1_ms = stage_ms[2]
-    tok_per_s = s.T / (ms_per_step / 1e3)
-    # GEMM1 algorithmic work per launch: W13 + its scales of every touched
-    # expert, x once, act written once (and the row -> slot map).
-    w13_expert_bytes = 2 * s.I * (s.H // 2 + s.H // 32)
-    # activations: bf16, or E4M3 codes plus one scale byte per 32
+    dense = gate[0] == 1
+
+    # algorithmic work (bytes: read once or written once; FLOPs: 2 per MAC)
     x_bytes = s.T * (s.H + s.H // 32) if a8 else s.T * s.H * 2
     act_bytes = R * (s.I + s.I // 32) if a8 else R * s.I * 2
-    gemm1_bytes = U * w13_expert_bytes + x_bytes + act_bytes + R * 4
+    gemm1_bytes = U * w13_e + x_bytes + act_bytes + R * 4
+    gemm2_bytes = U * w2_e + act_bytes + R * s.H * 2
     gemm1_flops = 2.0 * R * s.H * 2 * s.I
-    layer_bytes = U * (w13_expert_bytes + s.H * (s.I // 2 + s.I // 32)) + s.T * s.H * 4 \
-        + s.T * s.E_g * 4
-    if R >= 64 * max(U, 1):  # prefill-like: the contraction dominates
-        roof = {"bound": "mfma", "achieved": round(gemm1_flops / (gemm1_ms / 1e3) / 1e12, 2),
-                "peak": MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"], "unit": "TFLOP/s"}
+    gemm2_flops = 2.0 * R * s.I * s.H
+    layer_bytes = U * (w13_e + w2_e) + s.T * s.H * 4 + s.T * s.E_g * 4
+    layer_flops = gemm1_flops + gemm2_flops
+    mfma_peak = MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"]
+    compute_bound = R >= 64 * max(U, 1)  # prefill-like: the contraction dominates
+
+    def roof(bytes_, flops, us, bound_mfma):
+        if bound_mfma:
+            a = flops / (us * 1e-6) / 1e12
+            return {"bound": "mfma", "achieved": round(a, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                    "frac": round(a / mfma_peak, 4), "algorithmic_flops": flops}
+        a = bytes_ / (us * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "algorithmic_bytes": int(bytes_)}
+
+    if s.B <= 32:
+        k1 = "gemm1_decode_a8_kernel" if a8 else "gemm1_decode_kernel"
     else:
-        roof = {"bound": "hbm", "achieved": round(gemm1_bytes / (gemm1_ms / 1e3) / 1e9, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    kernel = ("gemm1_decode_a8_kernel" if a8 else "gemm1_decode_kernel") if s.B <= 32 else \
-        ("gemm_tiled_a8_kernel<true>" if a8 else "gemm_tiled_kernel<true")
-    roof["traffic"] = measured_traffic(args.config, kernel)
-    roof["kernel"] = kernel
-    roof["kernel_us"] = round(gemm1_ms * 1e3, 2)
-    roof["algorithmic_bytes" if roof["bound"] == "hbm" else "algorithmic_flops"] = \
-        gemm1_bytes if roof["bound"] == "hbm" else gemm1_flops
+        k1 = "gemm_tiled_a8_kernel<true>" if a8 else "gemm_tiled_kernel<true>"
+    if dense:
+        k2 = "gemm2_resident_a8_kernel" if a8 else "gemm2_resident_kernel"
+    else:
+        k2 = "gemm2_stream_a8_kernel" if a8 else "gemm2_stream_kernel"
+    kernels = {}
+    for label, kname, us, b, f in (("gemm1", k1, stages["gemm1"], gemm1_bytes, gemm1_flops),
+                                   ("gemm2", k2, stages["gemm2"], gemm2_bytes, gemm2_flops)):
+        r = roof(b, f, us, compute_bound)
+        r.update(kernel=kname, kernel_us=us, traffic=measured_traffic(s.name, kname))
+        kernels[label] = r
+    layer = roof(layer_bytes, layer_flops, med, compute_bound)
+    layer["basis"] = "median replay time of the whole layer"
 
     res = {
+        "workload": workload_name(s),
+        "T": s.T, "E": s.E, "E_global": s.E_g, "topk": s.topk, "S": s.S, "H": s.H, "I": s.I,
+        "block_n": s.B, "a_dtype": s.a_dtype,
+        "touched_experts": U_routed, "rows": R, "gemm2_path": "dense" if dense else "split",
+        "tokens_per_s": round(s.T / (ms_per_step * 1e-3), 1),
+        "ms_per_step": round(ms_per_step, 4),
+        "layer_us": {"median": round(med, 2), "p10": round(pct(rep_us, 10), 2),
+                     "p90": round(pct(rep_us, 90), 2), "mean": round(ms_per_step * 1e3, 2)},
+        "stage_us": stages,
+        "weight_sets": nsets,
+        "layer_roofline": layer,
+        "kernels": kernels,
+    }
+    del graphs, sets, ws, out, x, logits, shared
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline and cpu_seconds:
+        log(f"[bench] {name}/{a_dtype}: CPU baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(s, inp, cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    del inp
+    return res
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures a single GPU; --gpus {args.gpus} is not supported: the layer "
+              "runs on one GPU, and splitting experts over GPUs (expert_offset) is the "
+              "caller's part", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mxfp4_weight_expert_amd as moe
+
+    moe.load_library()  # fails loudly if the HIP library is not built
+    torch.cuda.set_device(0)
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 20
+        a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    head = measure(args.config, args.a_dtype, args, args.activation, args.cpu_seconds)
+    k1 = head["kernels"]["gemm1"]
+    roofline = {key: k1[key] for key in ("bound", "achieved", "peak", "unit", "frac", "traffic",
+                                         "kernel", "kernel_us")}
+    roofline["algorithmic_bytes" if k1["bound"] == "hbm" else "algorithmic_flops"] = \
+        k1.get("algorithmic_bytes", k1.get("algorithmic_flops"))
+    config = {key: v for key, v in head.items() if key not in ("cpu_baseline", "kernels",
+                                                               "layer_roofline", "tokens_per_s",
+                                                               "ms_per_step")}
+    config["gemm2"] = head["kernels"]["gemm2"]
+    res = {
         "metric": METRIC,
-        "value": round(tok_per_s, 1),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 x e2m1 (fp32 acc)" if a8 else "bf16",
-        "data": "synthetic (seeded PCG64: N(0,1) bf16 x, N(0,1) router logits, uniform E2M1 "
-                "nibbles, E8M0 scales uniform in [118,127])",
-        "config": {"workload": workload_name(s), "T": s.T, "E": s.E, "E_global": s.E_g,
-                   "topk": s.topk, "S": s.S, "H": s.H, "I": s.I, "block_n": s.B,
-                   "a_dtype": s.a_dtype,
-                   "touched_experts": U_routed, "rows": R, "gemm2_path": "dense" if gate[0] else "split",
-                   "layer_us": round(ms_per_step * 1e3, 2),
-                   "layer_hbm_GBps": round(layer_bytes / (ms_per_step / 1e3) / 1e9, 1),
-                   "stage_us": stages, "weight_sets": nsets},
-        "roofline": roof,
+        "dtype": "e4m3 x e2m1 (fp32 acc)" if args.a_dtype == "mxfp8" else "bf16",
+        "data": "synthetic (seeded PCG64: N(0,1) bf16 x, N(0,1) router logits (Zipf-skewed for "
+                "the EP decode), uniform E2M1 nibbles, E8M0 scales uniform in [118,127])",
+        "config": config,
+        "roofline": roofline,
+        "layer_roofline": head["layer_roofline"],
+        "cpu_baseline": head["cpu_baseline"],
     }
-    if not args.no_cpu_baseline:
-        log("[bench] CPU baseline (oracle)")
-        inp2 = make_inputs(s, config_seed(args.config))
-        res["cpu_baseline"] = cpu_baseline(s, inp2, args.cpu_seconds)
-    else:
-        res["cpu_baseline"] = None
+    if not args.no_sweep:
+        res["configs"] = {}
+        for name, adt in SWEEP:
+            if name == args.config and adt == args.a_dtype:
+                continue
+            key = name if adt == "bf16" else f"{name}_w4a8"
+            res["configs"][key] = measure(name, adt, args, None, args.sweep_cpu_seconds)
     print(json.dumps(res), flush=True)
 
 

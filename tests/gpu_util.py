@@ -100,7 +100,8 @@ def check_maps(s: LayerShape, got: dict, ref: dict, force_path: int = -1):
     if s.mode == "logits":
         assert np.array_equal(got["route_ids"], ref["route_ids"]), "top-k ids differ"
     assert np.array_equal(got["slot_expert"], ref["slot_expert"]), "slot experts differ"
-    assert np.allclose(got["slot_w"], ref["slot_w"], rtol=WEIGHT_RTOL, atol=0), "slot weights differ"
+    assert np.allclose(got["slot_w"], ref["slot_w"], rtol=WEIGHT_RTOL, atol=0, equal_nan=True), \
+        "slot weights differ"
     assert np.array_equal(got["counts"], ref["counts"]), "counts differ"
     assert np.array_equal(got["offsets"], ref["offsets"]), "offsets differ"
     R = int(ref["counts"].sum())
@@ -117,3 +118,50 @@ def check_maps(s: LayerShape, got: dict, ref: dict, force_path: int = -1):
     nu = int(got["counters"][1])
     u16 = oracle.sort_align(ref["slot_expert"], s.Ep, 16)["vinfo"]
     assert nu == u16.shape[0] and np.array_equal(got["units16"][:nu], u16), "16-row units differ"
+
+
+def covering_tokens(ref: dict, Kp: int, B: int, tile: int) -> np.ndarray:
+    """Tokens whose rows cover, from the oracle's maps, (a) the last B-row
+    chunk (the ragged tail) of every expert with rows, and (b) every row
+    position 0..tile-1 within an expert's tile-row tiles (the last slot of a
+    tile included). Greedy: the token of each uncovered expert's last row,
+    then a token for each position still uncovered."""
+    offsets = ref["offsets"].astype(np.int64)
+    counts = ref["counts"].astype(np.int64)
+    sorted_slot = ref["sorted_slot"].astype(np.int64)
+    expanded = ref["expanded_idx"].astype(np.int64)
+    R = int(counts.sum())
+    rows_all = np.arange(R)
+    row_expert = np.searchsorted(offsets, rows_all, side="right") - 1
+    pos = rows_all - offsets[row_expert]
+    tail_start = offsets[:-1] + (np.maximum(counts, 1) - 1) // B * B
+    in_tail = rows_all >= tail_start[row_expert]
+    tail_done = counts == 0
+    pos_done = np.zeros(tile, bool)
+    chosen = []
+
+    def take(t):
+        chosen.append(t)
+        rows = expanded[t * Kp:(t + 1) * Kp]
+        rows = rows[rows >= 0]
+        tail_done[row_expert[rows[in_tail[rows]]]] = True
+        pos_done[pos[rows] % tile] = True
+
+    for e in np.nonzero(~tail_done)[0]:
+        if not tail_done[e]:
+            take(int(sorted_slot[offsets[e + 1] - 1]) // Kp)
+    for p in np.nonzero(~pos_done)[0]:
+        if not pos_done[p] and np.any(counts > p):
+            e = int(np.argmax(counts > p))
+            take(int(sorted_slot[offsets[e] + p]) // Kp)
+    assert np.all(tail_done)
+    return np.unique(chosen)
+
+
+def oracle_rows(s: LayerShape, inp: dict, tokens: np.ndarray) -> np.ndarray:
+    """The oracle's output rows for `tokens`: the whole layer on that
+    sub-batch (every step is per token, so the rows equal those of the full
+    batch), grouped by expert so each touched expert is decoded once."""
+    sub = {k: (np.asarray(v)[tokens] if k in ("x", "logits", "shared", "topk_ids", "topk_w") else v)
+           for k, v in inp.items()}
+    return oracle.reference_forward(s.replace(T=int(len(tokens))), sub)["out"]

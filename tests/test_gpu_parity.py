@@ -15,7 +15,8 @@ import oracle
 import mxfp4_weight_expert_amd as moe
 from workloads import CONFIGS, CONFIG_ORDER, LayerShape, config_seed, make_inputs
 
-from gpu_util import bf16_dev, check_maps, check_out, maps_np, out_np, run, say, to_device
+from gpu_util import (bf16_dev, check_maps, check_out, covering_tokens, maps_np, oracle_rows,
+                      out_np, run, say, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -51,6 +52,14 @@ SMALL = [
                activation="situ", act_beta=2.0, act_linear_beta=8.0),
     LayerShape("situ_prefill", T=1024, E=16, E_g=16, topk=4, H=512, I=128, B=128, S=1,
                activation="situ"),
+    # the long-prefill kernels at their own inter size: I = 384 (and 576) is a
+    # multiple of 192, so GEMM1 runs 384-row weight tiles, and the dense GEMM2
+    # keeps the act tile resident (I <= 384) or takes the generic tiled path;
+    # many 128- and 256-row tiles per expert with ragged tails
+    LayerShape("prefill_i384_b128", T=2048, E=16, E_g=16, topk=4, H=512, I=384, B=128),
+    LayerShape("prefill_i384_b256", T=2048, E=12, E_g=12, topk=4, H=1024, I=384, B=256, S=1,
+               swiglu_limit=6.0),
+    LayerShape("prefill_i576_b128", T=1536, E=10, E_g=10, topk=4, H=512, I=576, B=128),
 ]
 
 
@@ -82,8 +91,14 @@ def test_config_parity(name):
     inp = make_inputs(s, config_seed(name))
     dev = to_device(s, inp)
     ref = oracle.reference_forward(s, inp, compute_out=(name == "tiny"))
-    toks = _sample_tokens(s.T, 6 if name == "prefill" else 8, 7)
-    want = ref["out"][toks] if name == "tiny" else oracle.sampled_forward(s, inp, toks)
+    if name == "prefill":
+        # rows in every expert's ragged tail chunk and at every position of a
+        # 128-row tile, computed by the oracle grouped by expert
+        toks = covering_tokens(ref, s.Kp, s.B, 128)
+        want = oracle_rows(s, inp, toks)
+    else:
+        toks = _sample_tokens(s.T, 8, 7)
+        want = ref["out"][toks] if name == "tiny" else oracle.sampled_forward(s, inp, toks)
     auto_path = ref["gate"][0]
     for force in ("auto", "split" if auto_path == 1 else "dense"):
         say(f"  force={force}")
@@ -156,6 +171,12 @@ SMALL_A8 = [
                a_dtype="mxfp8"),
     LayerShape("a8_situ_prefill", T=700, E=6, E_g=6, topk=2, H=512, I=256, B=128,
                activation="situ", act_beta=3.0, act_linear_beta=10.0, a_dtype="mxfp8"),
+    # the W4A8 long-prefill kernels at I = 384: tiled GEMM1 and the resident
+    # dense GEMM2 over many 128- and 256-row tiles with ragged tails
+    LayerShape("a8_prefill_i384_b128", T=2048, E=16, E_g=16, topk=4, H=512, I=384, B=128,
+               a_dtype="mxfp8"),
+    LayerShape("a8_prefill_i384_b256", T=2048, E=12, E_g=12, topk=4, H=1024, I=384, B=256, S=1,
+               swiglu_limit=6.0, a_dtype="mxfp8"),
 ]
 
 
@@ -203,8 +224,12 @@ def test_w4a8_config_parity(name):
     inp = make_inputs(s, config_seed(name))
     dev = to_device(s, inp)
     ref = oracle.reference_forward(s, inp, compute_out=False)
-    toks = _sample_tokens(s.T, 6 if name == "prefill" else 8, 11)
-    want = oracle.sampled_forward(s, inp, toks)
+    if name == "prefill":
+        toks = covering_tokens(ref, s.Kp, s.B, 128)
+        want = oracle_rows(s, inp, toks)
+    else:
+        toks = _sample_tokens(s.T, 8, 11)
+        want = oracle.sampled_forward(s, inp, toks)
     out, ws = run(s, dev)
     got = maps_np(s, ws)
     check_maps(s, got, ref)
@@ -227,6 +252,32 @@ def test_routing_ties_and_signed_zeros(E_g, topk):
     lg[0::3] = 0.0
     lg[0::3, ::2] = -0.0                       # rows of signed zeros only
     lg[1::3, :topk // 2 + 1] = np.float32(7.5)  # a tie straddling the top-k boundary
+    inp["logits"] = lg
+    ref = oracle.reference_forward(s, inp, compute_out=False)
+    out, ws = run(s, to_device(s, inp))
+    check_maps(s, maps_np(s, ws), ref)
+
+
+@pytest.mark.parametrize("E_g,topk", [(130, 5), (896, 16)])
+def test_routing_non_finite_logits(E_g, topk):
+    """NaN logits rank below -inf (ties by lower id) and a selected NaN gets
+    weight 0; infinities follow IEEE arithmetic (a selected +inf, or an
+    all -inf selection, makes the token's weights NaN). Ids bit-exact,
+    weights equal including their NaN positions."""
+    s = LayerShape(f"nonfinite_{E_g}", T=64, E=16, E_g=E_g, topk=topk, H=512, I=128, B=16)
+    inp = make_inputs(s, 950 + E_g)
+    lg = inp["logits"].copy()
+    rng = np.random.default_rng(E_g + 1)
+    lg[0::4][rng.random(lg[0::4].shape) < 0.3] = np.nan   # scattered NaNs
+    lg[1] = np.nan                                          # all NaN
+    lg[2, :] = np.nan
+    lg[2, E_g - topk // 2:] = 1.0                           # fewer numbers than topk
+    lg[3, ::3] = -np.inf                                    # -inf among numbers
+    lg[5, :] = -np.inf                                      # all -inf
+    lg[6, 7] = np.inf                                       # one +inf
+    lg[7, 1::2] = np.inf                                    # many +inf, ties
+    lg[9, :topk + 3] = -np.inf
+    lg[9, topk + 3:] = np.nan                               # -inf before NaN
     inp["logits"] = lg
     ref = oracle.reference_forward(s, inp, compute_out=False)
     out, ws = run(s, to_device(s, inp))
@@ -286,3 +337,22 @@ def test_prepack_layout(rows, row_bytes):
     got = moe.prepack(torch.from_numpy(w).cuda()).cpu().numpy().reshape(-1)
     want = w.reshape(rows // 16, 16, row_bytes // 64, 64).transpose(0, 2, 1, 3).reshape(-1)
     assert np.array_equal(got, want)
+
+
+def test_row_major_weight_tag_rejected_before_launch():
+    """A forward call whose shape tags w13/w2 as row-major fails with
+    MOE_ERR_UNSUPPORTED and enqueues nothing: out and the workspace keep
+    their contents."""
+    s = CONFIGS["tiny"]
+    inp = make_inputs(s, 31)
+    dev = to_device(s, inp)
+    shp = moe.Shape(T=s.T, E=s.E, E_global=s.E_g, topk=s.topk, H=s.H, I=s.I, block_n=s.B,
+                    weight_layout="row_major")
+    ws = torch.full((moe.query(shp),), 0x5A, dtype=torch.uint8, device="cuda")
+    out = torch.full((s.T, s.H), 3.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(moe.MoeError) as ei:
+        moe.forward(dev["x"], dev["w13"], dev["s13"], dev["w2"], dev["s2"], shp,
+                    router_logits=dev["logits"], out=out, workspace=ws)
+    assert ei.value.code == 2
+    torch.cuda.synchronize()
+    assert bool(torch.all(out == 3.0)) and bool(torch.all(ws == 0x5A))
