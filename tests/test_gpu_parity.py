@@ -52,14 +52,14 @@ SMALL = [
                activation="situ", act_beta=2.0, act_linear_beta=8.0),
     LayerShape("situ_prefill", T=1024, E=16, E_g=16, topk=4, H=512, I=128, B=128, S=1,
                activation="situ"),
-    # the long-prefill kernels at their own inter size: I = 384 (and 576) is a
+    # the long-prefill kernels at their own inter size: I = 384 (and 768) is a
     # multiple of 192, so GEMM1 runs 384-row weight tiles, and the dense GEMM2
     # keeps the act tile resident (I <= 384) or takes the generic tiled path;
     # many 128- and 256-row tiles per expert with ragged tails
     LayerShape("prefill_i384_b128", T=2048, E=16, E_g=16, topk=4, H=512, I=384, B=128),
     LayerShape("prefill_i384_b256", T=2048, E=12, E_g=12, topk=4, H=1024, I=384, B=256, S=1,
                swiglu_limit=6.0),
-    LayerShape("prefill_i576_b128", T=1536, E=10, E_g=10, topk=4, H=512, I=576, B=128),
+    LayerShape("prefill_i768_b128", T=1536, E=10, E_g=10, topk=4, H=512, I=768, B=128),
 ]
 
 
