@@ -54,6 +54,7 @@ extern "C" {
 #define MOE_ERR_UNSUPPORTED 2 /* shape outside the supported range */
 #define MOE_ERR_WORKSPACE 3   /* workspace too small or not 256-byte aligned */
 #define MOE_ERR_HIP 4         /* a kernel launch failed */
+#define MOE_ERR_SCRATCH 5     /* workspace beyond what moe_mxfp4_forward_noalloc holds */
 
 /* Activation kinds. */
 #define MOE_ACT_SWIGLU 0 /* act = silu(g) * u on the gate half g, up half u */
@@ -287,6 +288,36 @@ int moe_mxfp4_forward_timed(const void* x_dev, const float* router_logits_dev,
  */
 int moe_mxfp4_prepack(const uint8_t* w_dev, uint8_t* w_packed_dev, int64_t rows,
                       int64_t row_bytes, void* stream);
+
+/*
+ * moe_mxfp4_forward without a workspace argument, for callers that cannot
+ * allocate device memory: code under graph capture, tight serving loops,
+ * harnesses that forbid allocation. The call allocates nothing and runs the
+ * same launch chain and kernels as moe_mxfp4_forward, with the workspace in
+ * a library-owned device array of MOE_NOALLOC_SCRATCH_BYTES (128 MiB): one
+ * copy per GPU the library runs on, held until the process ends. Arguments
+ * as for moe_mxfp4_forward; the stream must belong to the current device,
+ * whose copy is used.
+ *
+ * Limits and behaviour:
+ *   - shapes whose moe_mxfp4_query size exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *     fail with MOE_ERR_SCRATCH before any launch (the T = 64 and T = 256
+ *     decode shapes of the K3.1 layer and the T = 512, H = 7168 shared-expert
+ *     shape fit; a 32k-token prefill does not);
+ *   - every call on one GPU shares that GPU's array and leaves its maps in
+ *     it: calls that overlap on one GPU (other streams, other threads) race
+ *     and give undefined results; serialise them;
+ *   - the first call on a device looks the array's address up
+ *     (hipGetSymbolAddress, which may load the code object): make it outside
+ *     graph capture. MOE_ERR_HIP if that lookup fails.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (128ull << 20)
+int moe_mxfp4_forward_noalloc(const void* x_dev, const float* router_logits_dev,
+                              const int32_t* topk_ids_dev, const float* topk_w_dev,
+                              const void* shared_logits_dev, const uint8_t* w13_dev,
+                              const uint8_t* s13_dev, const uint8_t* w2_dev,
+                              const uint8_t* s2_dev, const moe_mxfp4_shape* shape,
+                              void* out_dev, void* stream);
 
 /* Static text for a return code. */
 const char* moe_mxfp4_strerror(int code);

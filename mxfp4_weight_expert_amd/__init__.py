@@ -11,8 +11,9 @@ import ctypes
 import os
 from dataclasses import dataclass
 
-__all__ = ["Shape", "query", "workspace_layout", "forward", "forward_timed", "strerror", "lib_path",
-           "MoeError", "read_maps", "ADTYPE", "GEMM2_PATH", "load_library", "prepack"]
+__all__ = ["Shape", "query", "workspace_layout", "forward", "forward_timed", "forward_noalloc",
+           "strerror", "lib_path", "MoeError", "read_maps", "ADTYPE", "GEMM2_PATH", "load_library",
+           "prepack"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_HERE, "libmoe_mxfp4.so")
@@ -76,6 +77,9 @@ def load_library():
     lib.moe_mxfp4_forward.restype = ctypes.c_int
     lib.moe_mxfp4_forward_timed.argtypes = lib.moe_mxfp4_forward.argtypes + [ctypes.c_void_p]
     lib.moe_mxfp4_forward_timed.restype = ctypes.c_int
+    lib.moe_mxfp4_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              ctypes.POINTER(_Shape), vp, vp]
+    lib.moe_mxfp4_forward_noalloc.restype = ctypes.c_int
     lib.moe_mxfp4_prepack.argtypes = [vp, vp, ctypes.c_int64, ctypes.c_int64, vp]
     lib.moe_mxfp4_prepack.restype = ctypes.c_int
     _lib = lib
@@ -204,6 +208,33 @@ def forward(x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=N
     """
     return _call(load_library().moe_mxfp4_forward, x, w13, s13, w2, s2, shape, router_logits,
                  topk_ids, topk_w, shared_logits, out, workspace, stream, ())
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def forward_noalloc(x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=None,
+                    topk_w=None, shared_logits=None, out=None, stream=None):
+    """forward through moe_mxfp4_forward_noalloc: no workspace argument, the
+    library's per-GPU scratch array instead (shapes up to
+    NOALLOC_SCRATCH_BYTES of workspace). `out` must be given by callers that
+    cannot allocate; it is allocated here when None."""
+    import torch
+
+    for t in (x, w13, s13, w2, s2, router_logits, topk_ids, topk_w, shared_logits, out):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("all tensors must be contiguous")
+    if out is None:
+        out = torch.empty((shape.T, shape.H), dtype=torch.bfloat16, device=x.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+    fn = load_library().moe_mxfp4_forward_noalloc
+    rc = fn(_ptr(x), _ptr(router_logits), _ptr(topk_ids), _ptr(topk_w), _ptr(shared_logits),
+            _ptr(w13), _ptr(s13), _ptr(w2), _ptr(s2), ctypes.byref(shape.to_c()), _ptr(out),
+            ctypes.c_void_p(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_mxfp4_forward_noalloc")
+    return out
 
 
 def forward_timed(events, x, w13, s13, w2, s2, shape: Shape, *, router_logits=None, topk_ids=None,

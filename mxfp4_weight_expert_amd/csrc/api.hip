@@ -8,6 +8,7 @@
 // H % 512 and I % 128, which are kept).
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -141,6 +142,8 @@ const char* moe_mxfp4_strerror(int code) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape";
     case MOE_ERR_WORKSPACE: return "workspace too small or misaligned";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH:
+      return "shape needs more scratch than the allocation-free entry point holds";
     default: return "unknown error";
   }
 }
@@ -320,6 +323,63 @@ int moe_mxfp4_forward_timed(const void* x_dev, const float* router_logits_dev,
   return forward_impl(x_dev, router_logits_dev, topk_ids_dev, topk_w_dev, shared_logits_dev,
                       w13_dev, s13_dev, w2_dev, s2_dev, shape, out_dev, workspace_dev,
                       workspace_bytes, stream, stage_events);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free entry point. The workspace lives in a file-scope device
+// array: one copy per GPU the library runs on, held until the process ends.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): its device address is looked up once per
+// device with hipGetSymbolAddress, with that device current, and that
+// pointer is what the launch chain receives. Every call on a GPU shares that
+// GPU's copy; the chain writes every map it later reads in the same call, so
+// nothing has to start at zero, and calls that overlap on one GPU race.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+int current_device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_mxfp4_forward_noalloc(const void* x_dev, const float* router_logits_dev,
+                              const int32_t* topk_ids_dev, const float* topk_w_dev,
+                              const void* shared_logits_dev, const uint8_t* w13_dev,
+                              const uint8_t* s13_dev, const uint8_t* w2_dev,
+                              const uint8_t* s2_dev, const moe_mxfp4_shape* shape,
+                              void* out_dev, void* stream) {
+  const int rc = check_shape(shape);
+  if (rc != MOE_OK) return rc;
+  moe_mxfp4_ws_layout L;
+  carve(shape, &L);
+  if (L.total_bytes > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_SCRATCH;
+  void* ws = nullptr;
+  const int rs = current_device_scratch(&ws);
+  if (rs != MOE_OK) return rs;
+  return forward_impl(x_dev, router_logits_dev, topk_ids_dev, topk_w_dev, shared_logits_dev,
+                      w13_dev, s13_dev, w2_dev, s2_dev, shape, out_dev, ws,
+                      MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 }  // extern "C"

@@ -25,8 +25,9 @@ def _declared_functions():
 def test_library_exports_every_declared_function():
     lib = moe.load_library()
     names = _declared_functions()
-    assert names == ["moe_mxfp4_forward", "moe_mxfp4_forward_timed", "moe_mxfp4_prepack",
-                     "moe_mxfp4_query", "moe_mxfp4_strerror", "moe_mxfp4_workspace_layout"]
+    assert names == ["moe_mxfp4_forward", "moe_mxfp4_forward_noalloc", "moe_mxfp4_forward_timed",
+                     "moe_mxfp4_prepack", "moe_mxfp4_query", "moe_mxfp4_strerror",
+                     "moe_mxfp4_workspace_layout"]
     for n in names:
         assert hasattr(lib, n), n
     nm = subprocess.run(["nm", "-D", "--defined-only", moe.lib_path], capture_output=True, text=True)
