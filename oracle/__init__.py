@@ -15,19 +15,22 @@ the source pages:
   * the sigmoid shared-expert append from "SGLang MoE shared expert:
     fusing three kernels into one" (the append kernel, after the change);
   * the device-side Dense/Split GEMM2 choice from "FlashInfer device-side
-    gating of the MoE GEMM2 path" (sections 1 and 2).
+    gating of the MoE GEMM2 path" (sections 1 and 2);
+  * FP4 (E2M1) activations for the W4A4 variant from "SGLang CUTLASS MoE"
+    (section 6), in the MX block format of the weights.
 
 Functions whose result has no pin other than the oracle itself say
 "parity unpinned" in their docstring.
 """
 from .mx import (E2M1_MAGNITUDES, e2m1_decode, e8m0_decode, dequant_mxfp4,
-                 quant_mxfp8, dequant_mxfp8, e4m3_decode)
+                 quant_mxfp8, dequant_mxfp8, e4m3_decode, quant_mxfp4, pack_nibbles)
 from .moe import (route_topk_softmax, shared_append, local_map, sort_align,
                   kmax_v, gate_word, dense_tiles, expert_glu, situ, reference_forward,
                   sampled_forward, GATE_TAU, DENSE_MT, bf16_bits_to_f64)
 
 __all__ = [
     "E2M1_MAGNITUDES", "e2m1_decode", "e8m0_decode", "dequant_mxfp4", "quant_mxfp8",
+    "quant_mxfp4", "pack_nibbles",
     "dequant_mxfp8", "e4m3_decode", "route_topk_softmax", "shared_append", "local_map",
     "sort_align", "kmax_v", "gate_word", "dense_tiles", "expert_glu", "situ", "reference_forward",
     "sampled_forward", "GATE_TAU", "DENSE_MT", "bf16_bits_to_f64",

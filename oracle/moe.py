@@ -15,7 +15,12 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mx import dequant_mxfp4, dequant_mxfp8, quant_mxfp8
+from .mx import dequant_mxfp4, dequant_mxfp8, quant_mxfp4, quant_mxfp8
+
+# Activation formats of the layer: the A operand of both GEMMs. "bf16" is
+# W4A16; "mxfp8" (W4A8) and "mxfp4" (W4A4) quantise x along H before GEMM1
+# and act along I before GEMM2.
+_ACT_QUANT = {"mxfp8": (quant_mxfp8, dequant_mxfp8), "mxfp4": (quant_mxfp4, dequant_mxfp4)}
 
 # Device GEMM2 gate: the dense path is taken when the routed rows average at
 # least GATE_TAU per touched expert ([GATE] names the Dense and Split paths
@@ -186,7 +191,7 @@ def situ(g: np.ndarray, u: np.ndarray, beta: float, linear_beta: float) -> np.nd
 
 
 def expert_glu(xr: np.ndarray, W13: np.ndarray, W2: np.ndarray, limit: float = 0.0,
-               act_mxfp8: bool = False, act: str = "swiglu", beta: float = 4.0,
+               act_quant: str = "bf16", act: str = "swiglu", beta: float = 4.0,
                linear_beta: float = 25.0) -> np.ndarray:
     """One expert's gated MLP on its rows, float64.
 
@@ -198,7 +203,9 @@ def expert_glu(xr: np.ndarray, W13: np.ndarray, W2: np.ndarray, limit: float = 0
     page's swiglu limit: g = min(g, limit), u = clip(u, -limit, limit).
     With act = "situ" the activation is situ(g, u, beta, linear_beta)
     instead (the limit does not apply).
-    With act_mxfp8 the activation is MXFP8-quantised along I before GEMM2.
+    With act_quant "mxfp8" or "mxfp4" the activation is quantised to that
+    MX format along I before GEMM2 ("bf16": not quantised; the oracle does
+    not round it).
     xr [n, H], W13 [2I, H], W2 [H, I] -> y [n, H].
     """
     I = W13.shape[0] // 2
@@ -211,9 +218,9 @@ def expert_glu(xr: np.ndarray, W13: np.ndarray, W2: np.ndarray, limit: float = 0
             g = np.minimum(g, limit)
             u = np.clip(u, -limit, limit)
         act = g * _sigmoid(g) * u
-    if act_mxfp8:
-        q, s = quant_mxfp8(act)
-        act = dequant_mxfp8(q, s)
+    if act_quant in _ACT_QUANT:
+        quant, dequant = _ACT_QUANT[act_quant]
+        act = dequant(*quant(act))
     return act @ W2.T
 
 
@@ -243,10 +250,13 @@ def _routing(shape, inp):
 
 
 def _activations(shape, inp):
+    """x as GEMM1 reads it: bf16 values, or their MX quantisation along H
+    (returned with its codes and scales)."""
     x = bf16_bits_to_f64(inp["x"])
-    if shape.a_dtype == "mxfp8":
-        xq, xs = quant_mxfp8(x)
-        return dequant_mxfp8(xq, xs), xq, xs
+    if shape.a_dtype in _ACT_QUANT:
+        quant, dequant = _ACT_QUANT[shape.a_dtype]
+        xq, xs = quant(x)
+        return dequant(xq, xs), xq, xs
     return x, None, None
 
 
@@ -281,8 +291,7 @@ def reference_forward(shape, inp: dict, force_path: int = -1, compute_out: bool 
         tok = rows // s.Kp
         W13 = dequant_mxfp4(inp["w13"][e], inp["s13"][e])
         W2 = dequant_mxfp4(inp["w2"][e], inp["s2"][e])
-        y = expert_glu(xa[tok], W13, W2, s.swiglu_limit, s.a_dtype == "mxfp8",
-                       **_act_kw(s))
+        y = expert_glu(xa[tok], W13, W2, s.swiglu_limit, s.a_dtype, **_act_kw(s))
         np.add.at(out, tok, wflat[rows][:, None] * y)
     res["out"] = out
     return res
@@ -313,7 +322,6 @@ def sampled_forward(shape, inp: dict, tokens) -> np.ndarray:
                 cache[e] = (dequant_mxfp4(inp["w13"][e], inp["s13"][e]),
                             dequant_mxfp4(inp["w2"][e], inp["s2"][e]))
             W13, W2 = cache[e]
-            y = expert_glu(xa[i: i + 1], W13, W2, s.swiglu_limit, s.a_dtype == "mxfp8",
-                           **_act_kw(s))
+            y = expert_glu(xa[i: i + 1], W13, W2, s.swiglu_limit, s.a_dtype, **_act_kw(s))
             out[i] += slot_w[i, k] * y[0]
     return out

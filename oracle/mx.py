@@ -17,6 +17,14 @@ Formats, as the sources use them:
     page) without its recipe; the recipe here is the OCP MX one: shared
     exponent floor(log2(amax)) - 8, elements rounded to nearest-even with
     saturation at +-448.
+  * MXFP4 (W4A4 activations): E2M1 elements with one E8M0 per 32 K
+    elements. "SGLang CUTLASS MoE" (section 6, FP4 support) quantises the
+    activations to FP4 (E2M1) too and corrects E2M1's small range (largest
+    6.0) with extra scales; with power-of-two E8M0 block scales the range
+    is covered by the shared exponent, as in the OCP MX recipe: shared
+    exponent floor(log2(amax)) - 2 (2 = the largest E2M1 exponent),
+    elements rounded to the nearest E2M1 value, ties to the even code,
+    saturating at +-6.
 """
 from __future__ import annotations
 
@@ -133,3 +141,50 @@ def quant_mxfp8(v: np.ndarray):
 def dequant_mxfp8(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     """MXFP8 codes + E8M0 scales -> float64."""
     return e4m3_decode(codes) * np.repeat(e8m0_decode(scales), MX_BLOCK, axis=-1)
+
+
+def _e2m1_encode(a: np.ndarray) -> np.ndarray:
+    """Round float64 values to E2M1 codes: the nearest of the eight
+    magnitudes, a tie to the even code (the one whose mantissa bit is 0),
+    magnitudes above 6 saturating to 6; the sign bit is the input's (so a
+    negative value that rounds to zero gives code 8, -0)."""
+    a = np.asarray(a, dtype=np.float64)
+    mag = np.minimum(np.abs(a), 6.0)
+    d = np.abs(mag[..., None] - E2M1_MAGNITUDES)  # distance to each of codes 0..7
+    dmin = d.min(axis=-1, keepdims=True)
+    # among the (one or two) nearest codes, take the even one if there are two
+    cand = d == dmin
+    even_pref = np.where(np.arange(8) % 2 == 0, 0, 1)  # even codes rank first
+    score = np.where(cand, even_pref, 2)
+    codes = np.argmin(score, axis=-1).astype(np.int64)
+    codes = np.where(np.signbit(a), codes | 8, codes)
+    return codes.astype(np.uint8)
+
+
+def pack_nibbles(codes: np.ndarray) -> np.ndarray:
+    """[..., K] codes (0..15) -> [..., K/2] bytes; even K index in the low nibble."""
+    c = np.asarray(codes, dtype=np.uint8)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def quant_mxfp4(v: np.ndarray):
+    """MXFP4 quantisation along the last axis (length a multiple of 32).
+
+    Per 32-element block: amax = max |v|; if amax == 0 the scale byte is 0 and
+    every element is zero (sign kept). Otherwise the shared exponent is
+    floor(log2(amax)) - 2, stored biased by 127 and clamped to [0, 254];
+    elements are v / 2^shared rounded to E2M1 (_e2m1_encode).
+    Returns (codes packed two per byte [..., K/2], scales uint8 [..., K/32]),
+    the layout dequant_mxfp4 reads.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    k = v.shape[-1]
+    assert k % MX_BLOCK == 0
+    blk = v.reshape(v.shape[:-1] + (k // MX_BLOCK, MX_BLOCK))
+    amax = np.max(np.abs(blk), axis=-1)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    biased = np.clip((ex - 1) - 2 + 127, 0, 254)
+    biased = np.where(amax > 0, biased, 0)
+    scaled = blk / np.ldexp(1.0, biased - 127)[..., None]
+    codes = _e2m1_encode(scaled).reshape(v.shape)
+    return pack_nibbles(codes), biased.astype(np.uint8)

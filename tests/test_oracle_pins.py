@@ -470,6 +470,8 @@ SMALL = [
     LayerShape("s5", T=7, E=4, E_g=4, topk=2, H=64, I=64, B=16, a_dtype="mxfp8", S=1,
                swiglu_limit=2.0),
     LayerShape("s6_situ", T=10, E=6, E_g=6, topk=3, H=64, I=32, B=2, S=1, activation="situ"),
+    LayerShape("s7_a4", T=9, E=5, E_g=5, topk=2, H=64, I=64, B=2, S=1, swiglu_limit=3.0,
+               a_dtype="mxfp4"),
 ]
 
 
@@ -618,12 +620,12 @@ def test_w4a8_planted_mistakes_are_caught(monkeypatch):
     rt = lambda v: omx.dequant_mxfp8(*omx.quant_mxfp8(v))
     # 1. act not quantised before GEMM2
     monkeypatch.setattr(omoe, "expert_glu",
-                        lambda xr, W13, W2, limit=0.0, act_mxfp8=False, **kw:
-                        orig_glu(xr, W13, W2, limit, False, **kw))
+                        lambda xr, W13, W2, limit=0.0, act_quant="bf16", **kw:
+                        orig_glu(xr, W13, W2, limit, "bf16", **kw))
     assert _w4a8_closed_form_error()
 
     # 2. the GEMM1 outputs g and u quantised before the activation instead of act
-    def glu_h_quant(xr, W13, W2, limit=0.0, act_mxfp8=False, **kw):
+    def glu_h_quant(xr, W13, W2, limit=0.0, act_quant="bf16", **kw):
         I = W13.shape[0] // 2
         h = xr @ W13.T
         g, u = rt(h[:, :I]), rt(h[:, I:])
@@ -632,7 +634,7 @@ def test_w4a8_planted_mistakes_are_caught(monkeypatch):
     assert _w4a8_closed_form_error()
 
     # 3. act quantised along the rows (tokens) instead of along I
-    def glu_act_along_t(xr, W13, W2, limit=0.0, act_mxfp8=False, **kw):
+    def glu_act_along_t(xr, W13, W2, limit=0.0, act_quant="bf16", **kw):
         I = W13.shape[0] // 2
         h = xr @ W13.T
         g, u = h[:, :I], h[:, I:]
@@ -654,6 +656,205 @@ def test_w4a8_planted_mistakes_are_caught(monkeypatch):
     assert _w4a8_closed_form_error()
     monkeypatch.setattr(omoe, "_activations", orig_act)
     assert not _w4a8_closed_form_error()
+
+
+# -------------------------------------------------- MXFP4 (W4A4) activations
+# "SGLang CUTLASS MoE", section 6: FP4 (E2M1) activations as well as
+# weights. Here in the weights' own MX block format: one E8M0 per 32, shared
+# exponent floor(log2 amax) - 2, nearest E2M1 value with ties to the even
+# code, saturation at 6.
+
+def _e2m1_nearest_by_hand(m: float) -> int:
+    """Brute force over the eight magnitudes of the golden table: the nearest,
+    a tie to the even code; m >= 0."""
+    table = _e2m1_table()[:8]
+    m = min(m, 6.0)
+    best = None
+    for code in range(8):
+        d = abs(m - table[code])
+        if best is None or d < best[0] or (d == best[0] and code % 2 == 0):
+            best = (d, code)
+    return best[1]
+
+
+def test_e2m1_encode_by_brute_force():
+    rng = np.random.default_rng(17)
+    table = _e2m1_table()[:8]
+    mids = (table[1:] + table[:-1]) / 2
+    v = np.concatenate([rng.uniform(-7.5, 7.5, 4000), rng.uniform(-0.6, 0.6, 1000), table, mids,
+                        [6.0, 6.5, 7.0, 100.0, 1e-30]])
+    v = np.concatenate([v, -v])
+    got = omx._e2m1_encode(v)
+    want = [_e2m1_nearest_by_hand(abs(x)) | (8 if x < 0 or (x == 0 and math.copysign(1, x) < 0) else 0)
+            for x in v]
+    assert list(got) == want
+    # ties between neighbours go to the even code: 0.25 -> 0, 0.75 -> 1.0,
+    # 1.25 -> 1.0, 1.75 -> 2.0, 2.5 -> 2.0, 3.5 -> 4.0, 5.0 -> 4.0
+    assert list(omx._e2m1_encode(mids)) == [0, 2, 2, 4, 4, 6, 6]
+
+
+def test_mxfp4_shared_exponent_worked_examples():
+    blk = np.zeros((5, 32))
+    blk[0, 5] = 1.0      # amax 1 -> exponent -2 -> byte 125; 1.0 / 0.25 = 4 -> code 6
+    blk[1, :] = 6.0      # amax 6 -> exponent 0 -> byte 127; 6 -> code 7
+    blk[2, 3] = -7.0     # amax 7 -> exponent 0; -7 saturates to -6 -> code 15
+    blk[2, 4] = 0.2      # 0.2 -> 0 (nearest)
+    blk[4, 0] = -0.001   # rounds to -0 under amax 3: code 8
+    blk[4, 1] = 3.0      # amax 3 -> exponent -1 -> byte 126; 3 / 0.5 = 6 -> code 7
+    q, s = oracle.quant_mxfp4(blk)        # row 3 all zero -> byte 0, codes 0
+    codes = np.stack([q & 15, q >> 4], axis=-1).reshape(5, 32)
+    assert list(s[:, 0]) == [125, 127, 127, 0, 126]
+    assert codes[0, 5] == 6 and np.count_nonzero(codes[0]) == 1
+    assert np.all(codes[1] == 7)
+    assert codes[2, 3] == 15 and codes[2, 4] == 0
+    assert np.all(codes[3] == 0)
+    assert codes[4, 0] == 8 and codes[4, 1] == 7
+    d = oracle.dequant_mxfp4(q, s)
+    assert d[0, 5] == 1.0 and d[2, 3] == -6.0 and d[4, 1] == 3.0
+
+
+def test_mxfp4_rounding_error_bound():
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal((64, 256)) * np.exp(rng.uniform(-6, 6, (64, 1)))
+    q, s = oracle.quant_mxfp4(v)
+    d = oracle.dequant_mxfp4(q, s)
+    scale = np.repeat(oracle.e8m0_decode(s), 32, axis=-1)
+    m = np.abs(v) / scale
+    # spacing of E2M1 values at magnitude m: 0.5 below 2, 1 below 4, 2 above
+    half = np.where(m < 2, 0.25, np.where(m < 4, 0.5, 1.0)) * scale
+    inside = m <= 6.0
+    assert np.all(np.abs(d - v)[inside] <= half[inside])
+    assert np.all(np.abs(d[~inside]) == 6.0 * scale[~inside])  # saturated
+    assert np.all(m < 8.0)  # the shared exponent keeps every block below 2^3
+
+
+def _mxfp4_by_hand(v: np.ndarray) -> np.ndarray:
+    """MXFP4 round trip along the last axis, blocks of 32, by plain loops."""
+    table = _e2m1_table()[:8]
+    v = np.asarray(v, np.float64)
+    out = np.zeros_like(v)
+    for idx in np.ndindex(v.shape[:-1]):
+        for b in range(v.shape[-1] // 32):
+            blk = v[idx][32 * b: 32 * b + 32]
+            amax = float(np.max(np.abs(blk)))
+            if amax == 0.0:
+                continue
+            _, e = math.frexp(amax)
+            se = min(max(e - 1 - 2 + 127, 0), 254) - 127
+            for j, x in enumerate(blk):
+                code = _e2m1_nearest_by_hand(abs(x) / 2.0 ** se)
+                out[idx][32 * b + j] = math.copysign(table[code] * 2.0 ** se, x)
+    return out
+
+
+def _w4a4_onehot_case():
+    """The W4A8 one-hot case with MXFP4 activations (x along H, act along I)."""
+    H, I, E, S = 64, 64, 2, 1
+    _, _, _, _, pg, pu, cgv, cu, c2, wts = _onehot_layer(H, I, E, S)
+    T = 32
+    rng = np.random.default_rng(53)
+    x = f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32) * np.float32(1.7))
+    x[3, 0:32] = f32_to_bf16_bits(np.linspace(-2.0, 2.0, 32).astype(np.float32))
+    x[3, 7] = f32_to_bf16_bits(np.array([14.0], np.float32))[0]   # 14 / 2 = 7 saturates to 6
+    x[5, 32:64] = f32_to_bf16_bits((np.arange(32) % 7 - 3).astype(np.float32) * np.float32(2 ** -6))
+    x[5, 40] = f32_to_bf16_bits(np.array([3.0], np.float32))[0]  # the others round to zero
+    # a block of exact E2M1 midpoints (amax 5 -> shared exponent 0): each a tie
+    x[7, 0:32] = f32_to_bf16_bits(np.resize(np.array(
+        [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5, -5.0],
+        np.float32), 32))
+    xf = oracle.bf16_bits_to_f64(x)
+    ids = np.tile(np.array([[0, 1]], np.int32), (T, 1))
+    w = (rng.random((T, 2)) + 0.1).astype(np.float32)
+    sh = f32_to_bf16_bits((rng.standard_normal((T, 1)) * 2).astype(np.float32))
+    shape = LayerShape("cf_a4", T=T, E=E, E_g=E, topk=2, H=H, I=I, B=16, S=S, shared_scale=1.0,
+                       a_dtype="mxfp4", mode="ids")
+    inp = dict(x=x, logits=np.zeros((T, E), np.float32), shared=sh, topk_ids=ids, topk_w=w, **wts)
+    xd = _mxfp4_by_hand(xf)
+    assert np.any(xd != xf)
+    assert xd[3, 7] == 12.0                           # saturated: 6 * 2^1
+    assert np.all(xd[5, 32:64][np.arange(32) != 8] == 0.0) and xd[5, 40] == 3.0
+    assert list(xd[7, 0:7]) == [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0]  # ties to the even code
+    shared_w = scipy.special.expit(oracle.bf16_bits_to_f64(sh))[:, 0]
+    out = np.zeros((T, H))
+    for e, wt in ((0, w[:, 0].astype(np.float64)), (1, w[:, 1].astype(np.float64)), (2, shared_w)):
+        act = np.zeros((T, I))
+        for t in range(T):
+            for i in range(I):
+                g = cgv(e) * xd[t, pg(e, i)]
+                u = cu * xd[t, pu(e, i)]
+                act[t, i] = g / (1.0 + math.exp(-g)) * u
+        actq = _mxfp4_by_hand(act)
+        assert np.any(actq != act)
+        out += wt[:, None] * c2 * actq[:, np.arange(H) % I]
+    return shape, inp, out
+
+
+def test_w4a4_composition_closed_form():
+    shape, inp, want = _w4a4_onehot_case()
+    res = oracle.reference_forward(shape, inp)
+    assert np.max(np.abs(res["out"] - want)) <= 1e-12 * np.max(np.abs(want))
+    assert res["xq"].shape == (shape.T, shape.H // 2) and res["xs"].shape == (shape.T, shape.H // 32)
+
+
+def _w4a4_closed_form_error():
+    try:
+        test_w4a4_composition_closed_form()
+    except AssertionError:
+        return True
+    return False
+
+
+def test_w4a4_planted_mistakes_are_caught(monkeypatch):
+    assert not _w4a4_closed_form_error()
+    orig_glu, orig_act = omoe.expert_glu, omoe._activations
+    sig = lambda v: 1.0 / (1.0 + np.exp(-v))
+    rt4 = lambda v: omx.dequant_mxfp4(*omx.quant_mxfp4(v))
+    rt8 = lambda v: omx.dequant_mxfp8(*omx.quant_mxfp8(v))
+    # 1. act not quantised; 2. act quantised to MXFP8 instead of MXFP4
+    for fmt in ("bf16", "mxfp8"):
+        monkeypatch.setattr(omoe, "expert_glu",
+                            lambda xr, W13, W2, limit=0.0, act_quant="bf16", fmt=fmt, **kw:
+                            orig_glu(xr, W13, W2, limit, fmt, **kw))
+        assert _w4a4_closed_form_error(), fmt
+
+    # 3. g and u quantised before the activation instead of act
+    def glu_h_quant(xr, W13, W2, limit=0.0, act_quant="bf16", **kw):
+        I = W13.shape[0] // 2
+        h = xr @ W13.T
+        g, u = rt4(h[:, :I]), rt4(h[:, I:])
+        return (g * sig(g) * u) @ W2.T
+    monkeypatch.setattr(omoe, "expert_glu", glu_h_quant)
+    assert _w4a4_closed_form_error()
+
+    # 4. act quantised along the rows
+    def glu_act_along_t(xr, W13, W2, limit=0.0, act_quant="bf16", **kw):
+        I = W13.shape[0] // 2
+        h = xr @ W13.T
+        g, u = h[:, :I], h[:, I:]
+        return rt4((g * sig(g) * u).T).T @ W2.T
+    monkeypatch.setattr(omoe, "expert_glu", glu_act_along_t)
+    assert _w4a4_closed_form_error()
+    monkeypatch.setattr(omoe, "expert_glu", orig_glu)
+
+    # 5. x quantised along T; 6. x not quantised; 7. x quantised to MXFP8
+    for fn in (lambda x: rt4(x.T).T, lambda x: x, rt8):
+        monkeypatch.setattr(omoe, "_activations",
+                            lambda shape, inp, fn=fn: (fn(omoe.bf16_bits_to_f64(inp["x"])),
+                                                       np.zeros((shape.T, shape.H // 2), np.uint8),
+                                                       np.zeros((shape.T, shape.H // 32), np.uint8)))
+        assert _w4a4_closed_form_error()
+    monkeypatch.setattr(omoe, "_activations", orig_act)
+
+    # 8. ties rounded away from zero instead of to the even code
+    orig_enc = omx._e2m1_encode
+
+    def enc_ties_away(a):
+        a = np.asarray(a, np.float64)
+        return orig_enc(np.where(a == 0, a, a * (1 + 1e-12)))
+    monkeypatch.setattr(omx, "_e2m1_encode", enc_ties_away)
+    assert _w4a4_closed_form_error()
+    monkeypatch.setattr(omx, "_e2m1_encode", orig_enc)
+    assert not _w4a4_closed_form_error()
 
 
 # ----------------------------------------------- planted mistakes are caught
@@ -688,9 +889,9 @@ def test_planted_mistakes_are_caught(monkeypatch):
     # 2. gate and up halves swapped
     orig_glu = omoe.expert_glu
 
-    def glu_swapped(xr, W13, W2, limit=0.0, act_mxfp8=False, **act):
+    def glu_swapped(xr, W13, W2, limit=0.0, act_quant="bf16", **act):
         I = W13.shape[0] // 2
-        return orig_glu(xr, np.concatenate([W13[I:], W13[:I]]), W2, limit, act_mxfp8, **act)
+        return orig_glu(xr, np.concatenate([W13[I:], W13[:I]]), W2, limit, act_quant, **act)
     monkeypatch.setattr(omoe, "expert_glu", glu_swapped)
     assert _closed_form_error()
     monkeypatch.setattr(omoe, "expert_glu", orig_glu)
@@ -706,7 +907,7 @@ def test_planted_mistakes_are_caught(monkeypatch):
     assert _closed_form_error()
     monkeypatch.setattr(omoe, "dequant_mxfp4", orig_deq)
     # 4. gate clamped from below as well as above
-    def glu_clamp_both(xr, W13, W2, limit=0.0, act_mxfp8=False, **act):
+    def glu_clamp_both(xr, W13, W2, limit=0.0, act_quant="bf16", **act):
         I = W13.shape[0] // 2
         h = xr @ W13.T
         g, u = h[:, :I], h[:, I:]
