@@ -42,13 +42,14 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "fp4": 10100.0}
 METRIC = "MoE layer tokens/s and µs/layer; achieved HBM GB/s (decode), MFMA % (prefill)"
 # The Infinity Cache holds 256 MB: cycle through enough weight copies that
 # the other copies' touched weights between two uses of one copy exceed
 # twice that.
 MALL_FLUSH_BYTES = 512 << 20
-SWEEP = [("decode_ep", "bf16"), ("shared_clamp", "bf16"), ("prefill", "bf16"), ("prefill", "mxfp8")]
+SWEEP = [("decode_ep", "bf16"), ("shared_clamp", "bf16"), ("prefill", "bf16"), ("prefill", "mxfp8"),
+         ("prefill", "mxfp4")]
 
 
 def parse():
@@ -56,8 +57,9 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--a-dtype", default="bf16", choices=["bf16", "mxfp8"],
-                   help="activation format of the headline workload: bf16 (W4A16) or mxfp8 (W4A8)")
+    p.add_argument("--a-dtype", default="bf16", choices=["bf16", "mxfp8", "mxfp4"],
+                   help="activation format of the headline workload: bf16 (W4A16), mxfp8 (W4A8) "
+                        "or mxfp4 (W4A4)")
     p.add_argument("--activation", default=None, choices=["swiglu", "situ"],
                    help="GEMM1 epilogue (default: the workload's; situ uses beta 4, linear beta 25)")
     p.add_argument("--config", default="decode",
@@ -119,7 +121,8 @@ def workload_name(s) -> str:
         parts.append(f"SiTU(beta={s.act_beta:g}, linear_beta={s.act_linear_beta:g})")
     if s.routing == "zipf":
         parts.append(f"zipf={s.zipf_s:g}")
-    act = "W4A8 MXFP8 (E4M3) activations" if s.a_dtype == "mxfp8" else "W4A16 bf16 activations"
+    act = {"mxfp8": "W4A8 MXFP8 (E4M3) activations", "mxfp4": "W4A4 MXFP4 (E2M1) activations"}.get(
+        s.a_dtype, "W4A16 bf16 activations")
     return f"MXFP4 MoE layer ({s.name}): " + " ".join(parts) + f", {act}"
 
 
@@ -167,7 +170,8 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
     s = CONFIGS[name].replace(a_dtype=a_dtype)
     if activation:
         s = s.replace(activation=activation)
-    a8 = s.a_dtype == "mxfp8"
+    a8 = s.a_dtype in ("mxfp8", "mxfp4")  # MX activations (W4A8 or W4A4)
+    a4 = s.a_dtype == "mxfp4"
     log(f"[bench] {name}/{a_dtype}: generating inputs")
     inp = make_inputs(s, config_seed(name))
     shp = moe.Shape(T=s.T, E=s.E, E_global=s.E_g, topk=s.topk, H=s.H, I=s.I, block_n=s.B, S=s.S,
@@ -264,15 +268,17 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
     dense = gate[0] == 1
 
     # algorithmic work (bytes: read once or written once; FLOPs: 2 per MAC)
-    x_bytes = s.T * (s.H + s.H // 32) if a8 else s.T * s.H * 2
-    act_bytes = R * (s.I + s.I // 32) if a8 else R * s.I * 2
+    # activations: bf16, or MX codes (1 byte E4M3, half a byte E2M1) plus one
+    # scale byte per 32
+    x_bytes = s.T * ((s.H // 2 if a4 else s.H) + s.H // 32) if a8 else s.T * s.H * 2
+    act_bytes = R * ((s.I // 2 if a4 else s.I) + s.I // 32) if a8 else R * s.I * 2
     gemm1_bytes = U * w13_e + x_bytes + act_bytes + R * 4
     gemm2_bytes = U * w2_e + act_bytes + R * s.H * 2
     gemm1_flops = 2.0 * R * s.H * 2 * s.I
     gemm2_flops = 2.0 * R * s.I * s.H
     layer_bytes = U * (w13_e + w2_e) + s.T * s.H * 4 + s.T * s.E_g * 4
     layer_flops = gemm1_flops + gemm2_flops
-    mfma_peak = MFMA_PEAK_TFLOPS["fp8" if a8 else "bf16"]
+    mfma_peak = MFMA_PEAK_TFLOPS["fp4" if a4 else ("fp8" if a8 else "bf16")]
     compute_bound = R >= 64 * max(U, 1)  # prefill-like: the contraction dominates
 
     def roof(bytes_, flops, us, bound_mfma):
@@ -370,7 +376,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 x e2m1 (fp32 acc)" if args.a_dtype == "mxfp8" else "bf16",
+        "dtype": {"mxfp8": "e4m3 x e2m1 (fp32 acc)", "mxfp4": "e2m1 x e2m1 (fp32 acc)"}.get(
+            args.a_dtype, "bf16"),
         "data": "synthetic (seeded PCG64: N(0,1) bf16 x, N(0,1) router logits (Zipf-skewed for "
                 "the EP decode), uniform E2M1 nibbles, E8M0 scales uniform in [118,127])",
         "config": config,
@@ -383,7 +390,7 @@ def main():
         for name, adt in SWEEP:
             if name == args.config and adt == args.a_dtype:
                 continue
-            key = name if adt == "bf16" else f"{name}_w4a8"
+            key = name if adt == "bf16" else f"{name}_{'w4a8' if adt == 'mxfp8' else 'w4a4'}"
             res["configs"][key] = measure(name, adt, args, None, args.sweep_cpu_seconds)
     print(json.dumps(res), flush=True)
 

@@ -66,6 +66,10 @@ extern "C" {
 #define MOE_ADTYPE_BF16 0  /* W4A16: bf16 activations, bf16 MFMA */
 #define MOE_ADTYPE_MXFP8 1 /* W4A8: activations quantised to MXFP8 (E4M3 elements,
                               one E8M0 per 32 K), scaled f8f6f4 MFMA */
+#define MOE_ADTYPE_MXFP4 2 /* W4A4: activations quantised to MXFP4 (E2M1 elements,
+                              one E8M0 per 32 K), scaled f8f6f4 MFMA with both
+                              operands E2M1 ("SGLang CUTLASS MoE", section 6: FP4
+                              activations; here in the weights' MX block format) */
 
 /* Layout of the weight codes w13_dev / w2_dev (moe_mxfp4_shape.weight_layout).
  * MOE_WEIGHTS_ROW_MAJOR: [E', rows, K/2] row-major, as drawn or stored; the
@@ -102,9 +106,12 @@ extern "C" {
  *                   the prefill GEMM1 (tokens on the M side)
  *   expert_offset   global id of local expert 0
  *   activation      MOE_ACT_SWIGLU or MOE_ACT_SITU
- *   a_dtype         MOE_ADTYPE_BF16 or MOE_ADTYPE_MXFP8 (W4A8; needs I <= 512).
- *                   W4A8 quantises x to MXFP8 and the SwiGLU output act to
- *                   MXFP8 (per 32 along I) before GEMM2; the GEMMs run on
+ *   a_dtype         MOE_ADTYPE_BF16, MOE_ADTYPE_MXFP8 (W4A8) or
+ *                   MOE_ADTYPE_MXFP4 (W4A4); the MX formats need I <= 512.
+ *                   They quantise x (per 32 along H) and the activation
+ *                   output act (per 32 along I, before GEMM2) to MXFP8 or
+ *                   MXFP4 (shared exponent floor(log2 amax) - 8 or - 2,
+ *                   round to nearest even, saturating); the GEMMs run on
  *                   scaled f8f6f4 MFMA with the E2M1 weights fed as they are
  *   force_gemm2_path  MOE_GEMM2_AUTO, _SPLIT or _DENSE
  *   swiglu_limit    > 0: gate = min(gate, L), up = clamp(up, -L, L)
@@ -163,10 +170,12 @@ typedef struct moe_mxfp4_shape {
  *   units16       int32[max_units16*4] the rows again in units of at most 16
  *                 (same fields; counters[1] holds their number): the work list
  *                 of the decode GEMMs
- *   act           [rows_pad, I]   bf16 (W4A16) or E4M3 bytes (W4A8)
- *   act_scales    uint8[rows_pad, I/32] E8M0 (W4A8 only)
+ *   act           [rows_pad, I]   bf16 (W4A16) or E4M3 bytes (W4A8), or
+ *                 uint8[rows_pad, I/2] E2M1 pairs (W4A4, low nibble first)
+ *   act_scales    uint8[rows_pad, I/32] E8M0 (W4A8, W4A4)
  *   y             bf16[rows_pad, H] GEMM2 output in row order
- *   xq, xs        uint8[T, H], uint8[T, H/32]: MXFP8 x (W4A8 only)
+ *   xq, xs        uint8[T, H] (W4A8) or [T, H/2] (W4A4), uint8[T, H/32]:
+ *                 MX-quantised x (W4A8, W4A4 only)
  */
 typedef struct moe_mxfp4_ws_layout {
   uint64_t total_bytes;
@@ -200,7 +209,7 @@ typedef struct moe_mxfp4_ws_layout {
  * pointer, negative sizes, offset range outside E_global, unknown
  * weight_layout) or
  * MOE_ERR_UNSUPPORTED (H % 512, I % 128, H or I > 8192, block_n, topk, S, E + S > 2048,
- * T * K' > 2^23, unknown activation or a_dtype, MXFP8 with I > 512).
+ * T * K' > 2^23, unknown activation or a_dtype, MXFP8 or MXFP4 with I > 512).
  */
 int moe_mxfp4_query(const moe_mxfp4_shape* shape, uint64_t* workspace_bytes);
 

@@ -21,7 +21,7 @@ lib_path = os.path.join(_HERE, "libmoe_mxfp4.so")
 MOE_OK = 0
 NUM_STAGES = 5  # route, sort + gate, GEMM1, GEMM2, finalize
 STAGE_NAMES = ("route", "sort_gate", "gemm1", "gemm2", "finalize")
-ADTYPE = {"bf16": 0, "mxfp8": 1}
+ADTYPE = {"bf16": 0, "mxfp8": 1, "mxfp4": 2}
 ACTIVATION = {"swiglu": 0, "situ": 1}
 GEMM2_PATH = {"auto": -1, "split": 0, "dense": 1}
 WEIGHT_LAYOUT = {"row_major": 0, "packed": 1}
@@ -276,13 +276,14 @@ def read_maps(workspace, shape: Shape) -> dict:
         "vinfo": view(L["vinfo"], L["kmax_v"] * 4, i32).view(-1, 4),
         "dense_tiles": view(L["dense_tiles"], L["max_dense_tiles"] * 4, i32).view(-1, 4),
         "units16": view(L["units16"], L["max_units16"] * 4, i32).view(-1, 4),
-        "act": view(L["act"], L["rows_pad"] * shape.I * (1 if shape.a_dtype == "mxfp8" else 2),
-                    torch.uint8),
+        "act": view(L["act"], L["rows_pad"] * shape.I * {"bf16": 4, "mxfp8": 2, "mxfp4": 1}[
+            shape.a_dtype] // 2, torch.uint8),
         "y": view(L["y"], L["rows_pad"] * shape.H, torch.bfloat16).view(L["rows_pad"], shape.H),
         "layout": L,
     }
-    if shape.a_dtype == "mxfp8":
-        maps["xq"] = view(L["xq"], T * shape.H, torch.uint8).view(T, shape.H)
+    if shape.a_dtype in ("mxfp8", "mxfp4"):
+        xb = shape.H if shape.a_dtype == "mxfp8" else shape.H // 2  # code bytes per row
+        maps["xq"] = view(L["xq"], T * xb, torch.uint8).view(T, xb)
         maps["xs"] = view(L["xs"], T * shape.H // 32, torch.uint8).view(T, shape.H // 32)
         maps["act_scales"] = view(L["act_scales"], L["rows_pad"] * shape.I // 32, torch.uint8)
     return maps

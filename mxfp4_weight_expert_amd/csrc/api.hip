@@ -45,9 +45,11 @@ int check_shape(const moe_mxfp4_shape* s) {
       !(std::isfinite(s->act_beta) && s->act_beta > 0.0f && std::isfinite(s->act_linear_beta) &&
         s->act_linear_beta > 0.0f))
     return MOE_ERR_INVALID;
-  if (s->a_dtype != MOE_ADTYPE_BF16 && s->a_dtype != MOE_ADTYPE_MXFP8) return MOE_ERR_UNSUPPORTED;
-  // the W4A8 split GEMM2 keeps a row's whole K in registers: I <= 512
-  if (s->a_dtype == MOE_ADTYPE_MXFP8 && s->I > 512) return MOE_ERR_UNSUPPORTED;
+  if (s->a_dtype != MOE_ADTYPE_BF16 && s->a_dtype != MOE_ADTYPE_MXFP8 &&
+      s->a_dtype != MOE_ADTYPE_MXFP4)
+    return MOE_ERR_UNSUPPORTED;
+  // the MX-activation split GEMM2 keeps a row's whole K in registers: I <= 512
+  if (s->a_dtype != MOE_ADTYPE_BF16 && s->I > 512) return MOE_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(s->T) * (s->topk + s->S) > kMaxSlots) return MOE_ERR_UNSUPPORTED;
   // the kernels address x and act with 32-bit buffer offsets
   const int64_t rows = static_cast<int64_t>(s->T) * (s->topk + s->S) + 256;
@@ -60,7 +62,9 @@ int check_shape(const moe_mxfp4_shape* s) {
 void carve(const moe_mxfp4_shape* s, moe_mxfp4_ws_layout* L) {
   const uint64_t T = s->T, Kp = s->topk + s->S, Ep = s->E + s->S, H = s->H, I = s->I;
   const uint64_t slots = T * Kp;
-  const bool a8 = s->a_dtype == MOE_ADTYPE_MXFP8;
+  const bool mx = s->a_dtype != MOE_ADTYPE_BF16;
+  // bytes per activation element times 2: bf16 4, E4M3 2, E2M1 1
+  const uint64_t el2 = s->a_dtype == MOE_ADTYPE_MXFP4 ? 1 : (mx ? 2 : 4);
   L->kmax_v = static_cast<int32_t>(Ep + slots / s->block_n);
   L->max_dense_tiles = static_cast<int32_t>(Ep + slots / kDenseMT);
   L->max_units16 = static_cast<int32_t>(Ep + slots / 16);
@@ -86,11 +90,11 @@ void carve(const moe_mxfp4_shape* s, moe_mxfp4_ws_layout* L) {
   L->vinfo = take(static_cast<uint64_t>(L->kmax_v) * 16);
   L->dense_tiles = take(static_cast<uint64_t>(L->max_dense_tiles) * 16);
   L->units16 = take(static_cast<uint64_t>(L->max_units16) * 16);
-  L->act = take(rp * I * (a8 ? 1 : 2));
-  L->act_scales = take(a8 ? rp * I / 32 : 0);
+  L->act = take(rp * I * el2 / 2);
+  L->act_scales = take(mx ? rp * I / 32 : 0);
   L->y = take(rp * H * 2);
-  L->xq = take(a8 ? T * H : 0);
-  L->xs = take(a8 ? T * H / 32 : 0);
+  L->xq = take(mx ? T * H * el2 / 2 : 0);
+  L->xs = take(mx ? T * H / 32 : 0);
   L->total_bytes = o;
 }
 
@@ -273,12 +277,13 @@ int forward_impl(const void* x_dev, const float* router_logits_dev, const int32_
   ga.act_fn.inv_lb = s.activation == MOE_ACT_SITU ? 1.0f / s.act_linear_beta : 0.0f;
   ga.act = reinterpret_cast<uint16_t*>(at(L.act));
   ga.y = reinterpret_cast<uint16_t*>(at(L.y));
-  ga.a8 = s.a_dtype == MOE_ADTYPE_MXFP8;
+  ga.a8 = s.a_dtype != MOE_ADTYPE_BF16;  // MX activations (W4A8 or W4A4)
+  ga.a4 = s.a_dtype == MOE_ADTYPE_MXFP4;
   ga.xq = at(L.xq);
   ga.xs = at(L.xs);
   ga.act_scales = at(L.act_scales);
   if (mark() != hipSuccess) return MOE_ERR_HIP;
-  if (ga.a8 && launch_quant_x(ga.x, s.T, s.H, at(L.xq), at(L.xs), st) != hipSuccess)
+  if (ga.a8 && launch_quant_x(ga.x, s.T, s.H, at(L.xq), at(L.xs), ga.a4 != 0, st) != hipSuccess)
     return MOE_ERR_HIP;
   if (launch_gemm1(ga, st) != hipSuccess) return MOE_ERR_HIP;
   if (mark() != hipSuccess || launch_gemm2(ga, st) != hipSuccess) return MOE_ERR_HIP;

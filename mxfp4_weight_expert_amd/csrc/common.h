@@ -198,6 +198,65 @@ __device__ __forceinline__ f32x4_t mfma_f4xf8(const uint4& w, uint32_t sa, const
                                                           static_cast<int>(sb));
 }
 
+// Scaled MFMA, 16x16 output, K = 128, both operands E2M1 (W4A4): A as in
+// mfma_f4xf8; B = 16 columns of E2M1 codes in the same layout as A (lane
+// group g holds K [32g, 32g + 32) of its column, 16 bytes, low nibble
+// first), with its E8M0 scale byte for K block g in sb.
+__device__ __forceinline__ f32x4_t mfma_f4xf4(const uint4& w, uint32_t sa, const uint4& x,
+                                              uint32_t sb, f32x4_t c) {
+  const i32x8_t a = {static_cast<int>(w.x), static_cast<int>(w.y), static_cast<int>(w.z),
+                     static_cast<int>(w.w), 0, 0, 0, 0};
+  const i32x8_t b = {static_cast<int>(x.x), static_cast<int>(x.y), static_cast<int>(x.z),
+                     static_cast<int>(x.w), 0, 0, 0, 0};
+  // format codes: 4 = E2M1 for both operands
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 4, 4, 0, static_cast<int>(sa), 0,
+                                                          static_cast<int>(sb));
+}
+
+// The scaled MFMA of the MX-activation paths: W4A8 (E4M3 tokens in x0, x1)
+// or, with A4, W4A4 (E2M1 tokens in x0; x1 unused).
+template <bool A4>
+__device__ __forceinline__ f32x4_t mfma_f4xa(const uint4& w, uint32_t sa, const uint4& x0,
+                                             const uint4& x1, uint32_t sb, f32x4_t c) {
+  if constexpr (A4)
+    return mfma_f4xf4(w, sa, x0, sb, c);
+  else
+    return mfma_f4xf8(w, sa, x0, x1, sb, c);
+}
+
+// ------------------------------------------------------------------ MXFP4
+// MXFP4 block scale of a 32-element block with maximum magnitude amax: the
+// shared exponent floor(log2(amax)) - 2 (2 = the largest E2M1 exponent,
+// 6 = 1.5 * 2^2), biased by 127 and clamped to [0, 254]: max(e - 2, 0) with
+// e the exponent field of amax (<= 252 for finite amax).
+__device__ __forceinline__ uint32_t mxfp4_scale_byte(float amax) {
+  const uint32_t e = (__float_as_uint(amax) >> 23) & 0xffu;
+  return e >= 2u ? e - 2u : 0u;
+}
+// E2M1 code of v (already divided by the block scale): the nearest of
+// {0, .5, 1, 1.5, 2, 3, 4, 6}, a tie to the even code, |v| > 6 saturating to
+// 6; the sign bit is v's, so a negative value rounding to zero gives 8 (-0).
+// Each comparison threshold is a midpoint between neighbours: strict where
+// the lower neighbour's code is even, non-strict where the upper one's is.
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+  const float m = fabsf(v);
+  const uint32_t c = static_cast<uint32_t>(m > 0.25f) + static_cast<uint32_t>(m >= 0.75f) +
+                     static_cast<uint32_t>(m > 1.25f) + static_cast<uint32_t>(m >= 1.75f) +
+                     static_cast<uint32_t>(m > 2.5f) + static_cast<uint32_t>(m >= 3.5f) +
+                     static_cast<uint32_t>(m > 5.0f);
+  return c | ((__float_as_uint(v) >> 28) & 8u);
+}
+// Four scaled values -> four E2M1 codes in 16 bits, value i in nibble i.
+__device__ __forceinline__ uint32_t pack_e2m1x4(float a, float b, float c, float d) {
+  return e2m1_code(a) | (e2m1_code(b) << 4) | (e2m1_code(c) << 8) | (e2m1_code(d) << 12);
+}
+// 2^(127 - b) for an MX scale byte b <= 253: a normal float, so v * factor is
+// exact wherever the result matters (an underflow there rounds to a zero code
+// either way).
+__device__ __forceinline__ float mx_inv_scale(uint32_t b) {
+  return __uint_as_float((254u - b) << 23);
+}
+
 // ---------------------------------------------------------------- activation
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
@@ -310,6 +369,9 @@ __device__ __forceinline__ void bst8(__amdgpu_buffer_rsrc_t r, uint32_t off, uin
 }
 __device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void bst2(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(v), r, off, 0, 0);
 }
 __device__ __forceinline__ void bst1(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(v), r, off, 0, 0);

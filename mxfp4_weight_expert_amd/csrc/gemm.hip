@@ -561,29 +561,39 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// W4A8 decode GEMMs (MXFP8 activations). The E2M1 weights go into the
-// scaled MFMA as they are, with their E8M0 scales; no decode. One 16x16x128
-// MFMA per weight tile and K step: lane (r, g) supplies weight row r's codes
-// K [32g, 32g + 32) (the same 16-byte load as the bf16 path) and that
-// group's scale byte, and token r's E4M3 codes K [16g, 16g + 16) and
-// [64 + 16g, 64 + 16g + 16) with its scale byte for block g.
+// MX-activation decode GEMMs: W4A8 (MXFP8 activations) and, with A4, W4A4
+// (MXFP4 activations). The E2M1 weights go into the scaled MFMA as they are,
+// with their E8M0 scales; no decode. One 16x16x128 MFMA per weight tile and
+// K step: lane (r, g) supplies weight row r's codes K [32g, 32g + 32) (the
+// same 16-byte load as the bf16 path) and that group's scale byte, and
+// token r's codes with its scale byte for block g: E4M3 codes K [16g,
+// 16g + 16) and [64 + 16g, 64 + 16g + 16) (a K step is 128 bytes of a token
+// row), or E2M1 codes K [32g, 32g + 32), the same 16 bytes as the weight's
+// (a K step is 64 bytes).
 // ---------------------------------------------------------------------------
 
+// Token code bytes of one 128-element K step.
+template <bool A4>
+constexpr uint32_t tok_step_bytes() {
+  return A4 ? 64u : 128u;
+}
+
 // acc[t] += W_tile_t * Xq^T over nkb steps. xrs/xoff: buffer and byte offset
-// of the lane's E4M3 row plus 16g (kNoRow past the unit's end); srs/soff:
-// the row's scale bytes plus g (kNoRow likewise).
-template <bool NTW, int D>
+// of the lane's token code row plus 16g (kNoRow past the unit's end);
+// srs/soff: the row's scale bytes plus g (kNoRow likewise).
+template <bool NTW, int D, bool A4>
 __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_t (&wofs)[4],
                                                 const uint8_t* ls, const uint32_t (&lofs)[4],
                                                 int nkb, __amdgpu_buffer_rsrc_t xrs, uint32_t xoff,
                                                 __amdgpu_buffer_rsrc_t srs, uint32_t soff,
                                                 f32x4_t (&acc)[4]) {
+  constexpr uint32_t XS = tok_step_bytes<A4>();
   uint4 w[D][4], xb[D][2];
   uint32_t xsb[D];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    xb[d][0] = bld16(xrs, xoff + d * 128);
-    xb[d][1] = bld16(xrs, xoff + d * 128 + 64);
+    xb[d][0] = bld16(xrs, xoff + d * XS);
+    if (!A4) xb[d][1] = bld16(xrs, xoff + d * XS + 64);
     xsb[d] = bld1(srs, soff + d * 4);
 #pragma unroll
     for (int t = 0; t < 4; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
@@ -593,11 +603,11 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
   auto step = [&](int kb, int d) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
-      acc[t] = mfma_f4xf8(w[d][t], ls[lofs[t] + kb * 4], xb[d][0], xb[d][1], xsb[d], acc[t]);
+      acc[t] = mfma_f4xa<A4>(w[d][t], ls[lofs[t] + kb * 4], xb[d][0], xb[d][1], xsb[d], acc[t]);
     __builtin_amdgcn_sched_barrier(0);
     const int nk = min(kb + D, last);
-    xb[d][0] = bld16(xrs, xoff + nk * 128);
-    xb[d][1] = bld16(xrs, xoff + nk * 128 + 64);
+    xb[d][0] = bld16(xrs, xoff + nk * XS);
+    if (!A4) xb[d][1] = bld16(xrs, xoff + nk * XS + 64);
     xsb[d] = bld1(srs, soff + nk * 4);
 #pragma unroll
     for (int t = 0; t < 4; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + nk * kPkBlock);
@@ -611,35 +621,55 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
   }
 }
 
-// Block-shared E4M3 token tile of one K step in LDS for the W4A8 stream:
-// 16 rows x 128 code bytes, then the rows' four scale bytes. Chunk c (0..7)
-// of row rr sits at rr * 128 + 16 * (c ^ (((rr >> 2) & 3) << 1)): the 32
-// lanes of a fragment read (rows r, chunk g or 4 + g, g = 0..1) and of a
-// four-row write fall on distinct 16-byte bank groups.
-constexpr int kTok8LdsStep = 16 * 128 + 16 * 4;
-__device__ __forceinline__ uint32_t t8lds_off(int rr, int c) {
-  return static_cast<uint32_t>(rr * 128) + ((static_cast<uint32_t>(c) ^ ((static_cast<uint32_t>(rr >> 2) & 3u) << 1)) << 4);
+// Block-shared token tile of one K step in LDS for the MX stream: 16 rows x
+// tok_step_bytes codes, then the rows' four scale bytes.
+// E4M3 (128-byte rows): chunk c (0..7) of row rr sits at rr * 128 +
+// 16 * (c ^ (((rr >> 2) & 3) << 1)). E2M1 (64-byte rows): chunk c (0..3) at
+// rr * 64 + 16 * (c ^ (((rr >> 3) & 1) << 1)). Either way the 32 lanes of a
+// fragment read (rows r, the lane group's chunks) and of a write fall on
+// distinct 16-byte bank groups.
+template <bool A4>
+constexpr int tok_mx_lds_step() {
+  return 16 * static_cast<int>(tok_step_bytes<A4>()) + 16 * 4;
+}
+template <bool A4>
+__device__ __forceinline__ uint32_t tmx_lds_off(int rr, int c) {
+  if constexpr (A4)
+    return static_cast<uint32_t>(rr * 64) + ((static_cast<uint32_t>(c) ^ ((static_cast<uint32_t>(rr >> 3) & 1u) << 1)) << 4);
+  else
+    return static_cast<uint32_t>(rr * 128) + ((static_cast<uint32_t>(c) ^ ((static_cast<uint32_t>(rr >> 2) & 3u) << 1)) << 4);
+}
+// Threads of a block that copy token codes (16 rows x chunks per row), and
+// the first thread of the 16 that copy the rows' scale dwords.
+template <bool A4>
+constexpr int tok_mx_code_threads() {
+  return A4 ? 64 : 128;
 }
 
 // stream_block_a8 with the token codes and scales read from a block-shared
-// LDS tile (two buffers of kTok8LdsStep at tl), as stream_block_lds does for
-// bf16 tokens: one barrier per K step, every wave of the block calls it with
-// the same nkb. Threads t < 128 load code chunk t % 8 of tile row t / 8
-// (xrs at toff, zero past the unit's end), threads 128..143 the scale dword
-// of tile row t - 128 (srs at tsoff); the rest load nothing (out-of-range
-// offsets) and store nothing.
-template <bool NTW>
+// LDS tile (two buffers of tok_mx_lds_step at tl), as stream_block_lds does
+// for bf16 tokens: one barrier per K step, every wave of the block calls it
+// with the same nkb. Threads t < NC = tok_mx_code_threads load one 16-byte
+// code chunk of a tile row (xrs at toff, zero past the unit's end: chunk
+// t % 8 of row t / 8 for E4M3, t % 4 of row t / 4 for E2M1), threads
+// NC..NC+15 the scale dword of tile row t - NC (srs at tsoff); the rest load
+// nothing (out-of-range offsets) and store nothing.
+template <bool NTW, bool A4>
 __device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uint32_t (&wofs)[4],
                                                     const uint8_t* ls, const uint32_t (&lofs)[4],
                                                     int nkb, __amdgpu_buffer_rsrc_t xrs, uint32_t toff,
                                                     __amdgpu_buffer_rsrc_t srs, uint32_t tsoff,
                                                     uint8_t* tl, f32x4_t (&acc)[4]) {
   constexpr int D = 2;
+  constexpr uint32_t XS = tok_step_bytes<A4>();
+  constexpr int NC = tok_mx_code_threads<A4>();
+  constexpr int STEP = tok_mx_lds_step<A4>();
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int t = static_cast<int>(threadIdx.x);
-  const bool code_role = t < 128, scale_role = t >= 128 && t < 144;
-  const uint32_t st_off = code_role ? t8lds_off(t >> 3, t & 7) : 16 * 128 + (t - 128) * 4;
+  const bool code_role = t < NC, scale_role = t >= NC && t < NC + 16;
+  const uint32_t st_off = code_role ? (A4 ? tmx_lds_off<A4>(t >> 2, t & 3) : tmx_lds_off<A4>(t >> 3, t & 7))
+                                    : 16 * XS + (t - NC) * 4;
   uint4 w[D][4], tv[D];
   uint32_t ts[D];
   auto put = [&](uint8_t* buf, int d) {
@@ -648,7 +678,7 @@ __device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uin
   };
 #pragma unroll
   for (int d = 0; d < D; ++d) {
-    tv[d] = bld16(xrs, toff + d * 128);
+    tv[d] = bld16(xrs, toff + d * XS);
     ts[d] = bld4(srs, tsoff + d * 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) w[d][q] = ldw16<NTW>(wp + wofs[q] + d * kPkBlock);
@@ -658,16 +688,17 @@ __device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uin
   __syncthreads();
   const int last = nkb - 1;
   auto step = [&](int kb, int d) {
-    const uint8_t* tb = tl + (kb & 1) * kTok8LdsStep;
-    const uint4 x0 = *reinterpret_cast<const uint4*>(tb + t8lds_off(r, g));
-    const uint4 x1 = *reinterpret_cast<const uint4*>(tb + t8lds_off(r, 4 + g));
-    const uint32_t xsb = tb[16 * 128 + r * 4 + g];
+    const uint8_t* tb = tl + (kb & 1) * STEP;
+    uint4 x0, x1;
+    x0 = *reinterpret_cast<const uint4*>(tb + tmx_lds_off<A4>(r, g));
+    if (!A4) x1 = *reinterpret_cast<const uint4*>(tb + tmx_lds_off<A4>(r, 4 + g));
+    const uint32_t xsb = tb[16 * XS + r * 4 + g];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) acc[q] = mfma_f4xf8(w[d][q], ls[lofs[q] + kb * 4], x0, x1, xsb, acc[q]);
+    for (int q = 0; q < 4; ++q) acc[q] = mfma_f4xa<A4>(w[d][q], ls[lofs[q] + kb * 4], x0, x1, xsb, acc[q]);
     __builtin_amdgcn_sched_barrier(0);
-    put(tl + ((kb + 1) & 1) * kTok8LdsStep, (d + 1) % D);
+    put(tl + ((kb + 1) & 1) * STEP, (d + 1) % D);
     const int nk = min(kb + D, last);
-    tv[d] = bld16(xrs, toff + nk * 128);
+    tv[d] = bld16(xrs, toff + nk * XS);
     ts[d] = bld4(srs, tsoff + nk * 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) w[d][q] = ldw16<NTW>(wp + wofs[q] + nk * kPkBlock);
@@ -683,10 +714,12 @@ __device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uin
 }
 
 // The 32 act values of one token row and one 32-feature group, spread as 8
-// values over the four lanes r, r + 16, r + 32, r + 48: MXFP8-quantise them
-// (block amax over the four lanes) and store the lane's two 4-byte runs at
-// byte offsets o0 and o1 of `qrs`, and the block's scale byte at `soff` of
-// `srs` (lanes with g != 0 pass an out-of-range offset).
+// values over the four lanes r, r + 16, r + 32, r + 48 (features 4g + v and
+// 16 + 4g + v): MX-quantise them (block amax over the four lanes) and store
+// the lane's two runs of four codes at byte offsets o0 and o1 of `qrs` (4
+// E4M3 bytes each, or with A4 2 bytes of E2M1 pairs), and the block's scale
+// byte at `soff` of `srs` (lanes with g != 0 pass an out-of-range offset).
+template <bool A4>
 __device__ __forceinline__ void quant_store_act(const float (&a)[8], __amdgpu_buffer_rsrc_t qrs,
                                                 uint32_t o0, uint32_t o1,
                                                 __amdgpu_buffer_rsrc_t srs, uint32_t soff) {
@@ -695,18 +728,26 @@ __device__ __forceinline__ void quant_store_act(const float (&a)[8], __amdgpu_bu
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
   amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
   amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-  const uint32_t b = mxfp8_scale_byte(amax);
-  const float inv = mxfp8_inv_scale(b);
-  bst4(qrs, o0, pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
-  bst4(qrs, o1, pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
-  bst1(srs, soff, b);
+  if constexpr (A4) {
+    const uint32_t b = mxfp4_scale_byte(amax);
+    const float inv = mx_inv_scale(b);
+    bst2(qrs, o0, pack_e2m1x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
+    bst2(qrs, o1, pack_e2m1x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
+    bst1(srs, soff, b);
+  } else {
+    const uint32_t b = mxfp8_scale_byte(amax);
+    const float inv = mxfp8_inv_scale(b);
+    bst4(qrs, o0, pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
+    bst4(qrs, o1, pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
+    bst1(srs, soff, b);
+  }
 }
 
-// GEMM1 + SwiGLU + act quantisation, W4A8, decode shape. Items and LDS as
-// in gemm1_decode_kernel; the 32-feature group of an item is exactly one
-// MXFP8 block of act. TL: token tiles through LDS (stream_block_a8_lds,
-// D = 2), after the scale blocks in the dynamic LDS.
-template <int D, bool TL>
+// GEMM1 + SwiGLU + act quantisation, W4A8 (or W4A4 with A4), decode shape.
+// Items and LDS as in gemm1_decode_kernel; the 32-feature group of an item
+// is exactly one MX block of act. TL: token tiles through LDS
+// (stream_block_a8_lds, D = 2), after the scale blocks in the dynamic LDS.
+template <int D, bool TL, bool A4>
 __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
@@ -722,7 +763,8 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
   const int nkb = H >> 7;
   const int blk = 32 * static_cast<int>(srow);
   uint8_t* my = lds_scales + wave_index() * 2 * blk;
-  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xq, static_cast<uint32_t>(static_cast<size_t>(T) * H));
+  const uint32_t HB = A4 ? static_cast<uint32_t>(H) / 2 : static_cast<uint32_t>(H);  // x row bytes
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xq, static_cast<uint32_t>(static_cast<size_t>(T) * HB));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(xs, static_cast<uint32_t>(static_cast<size_t>(T) * srow));
   const uint32_t wofs[4] = {0u, static_cast<uint32_t>(I * wrow), static_cast<uint32_t>(16 * wrow),
                             static_cast<uint32_t>((I + 16) * wrow)};
@@ -743,25 +785,27 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     const uint8_t* wp = w13 + row0 * wrow + r * 64 + g * 16;  // packed layout
     const bool valid = r < nrows;
     const uint32_t tok = static_cast<uint32_t>(sorted_slot[r0 + min(r, nrows - 1)] / Kp);
-    const uint32_t xoff = valid ? tok * static_cast<uint32_t>(H) + g * 16 : kNoRow;
+    const uint32_t xoff = valid ? tok * HB + g * 16 : kNoRow;
     const uint32_t soff = valid ? tok * static_cast<uint32_t>(srow) + g : kNoRow;
     f32x4_t acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     auto run = [&](auto ntw) {
       if constexpr (TL) {
-        // this thread's row of the block's token tile: codes (t < 128) or scales
-        const int rr = tt < 128 ? tt >> 3 : tt - 128;
+        // this thread's row of the block's token tile: codes (t < NC) or scales
+        constexpr int NC = tok_mx_code_threads<A4>();
+        const int rr = tt < NC ? (A4 ? tt >> 2 : tt >> 3) : tt - NC;
         const uint32_t ttok = static_cast<uint32_t>(sorted_slot[r0 + min(rr, nrows - 1)] / Kp);
         const bool tv_ok = rr < nrows;
-        const uint32_t toff = tt < 128 && tv_ok ? ttok * static_cast<uint32_t>(H) + (tt & 7) * 16 : kNoRow;
+        const uint32_t toff =
+            tt < NC && tv_ok ? ttok * HB + (A4 ? (tt & 3) : (tt & 7)) * 16 : kNoRow;
         const uint32_t tsoff =
-            tt >= 128 && tt < 144 && tv_ok ? ttok * static_cast<uint32_t>(srow) : kNoRow;
-        stream_block_a8_lds<decltype(ntw)::value>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, toff, srs,
-                                                  tsoff, tl, acc);
+            tt >= NC && tt < NC + 16 && tv_ok ? ttok * static_cast<uint32_t>(srow) : kNoRow;
+        stream_block_a8_lds<decltype(ntw)::value, A4>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, toff,
+                                                      srs, tsoff, tl, acc);
       } else {
-        stream_block_a8<decltype(ntw)::value, D>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff, srs,
-                                                 soff, acc);
+        stream_block_a8<decltype(ntw)::value, D, A4>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff,
+                                                     srs, soff, acc);
       }
     };
     // weights read once in this call (the expert's only unit): non-temporal
@@ -772,20 +816,23 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int v = 0; v < 4; ++v) a[4 * h + v] = act_apply(acc[2 * h][v], acc[2 * h + 1][v], actf);
+    // act codes: I bytes per row (E4M3) or I / 2 (E2M1 pairs)
+    const uint32_t IB = A4 ? static_cast<uint32_t>(I) / 2 : static_cast<uint32_t>(I);
     const __amdgpu_buffer_rsrc_t qrs =
-        make_rsrc(actq + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I);
+        make_rsrc(actq + static_cast<size_t>(r0) * IB, static_cast<uint32_t>(nrows) * IB);
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(acts + static_cast<size_t>(r0) * srow_a, static_cast<uint32_t>(nrows) * srow_a);
-    const uint32_t o0 = static_cast<uint32_t>(r) * I + f0 + 4 * g;
-    quant_store_act(a, qrs, o0, o0 + 16, ars,
-                    g == 0 ? static_cast<uint32_t>(r) * srow_a + (f0 >> 5) : kNoRow);
+    const uint32_t e0 = static_cast<uint32_t>(r) * I + f0 + 4 * g;  // element index of a[0]
+    const uint32_t o0 = A4 ? e0 / 2 : e0;
+    quant_store_act<A4>(a, qrs, o0, o0 + (A4 ? 8 : 16), ars,
+                        g == 0 ? static_cast<uint32_t>(r) * srow_a + (f0 >> 5) : kNoRow);
   }
 }
 
-// GEMM2 split path, W4A8, short K (NKB = I/128 <= 4): the balanced stream of
-// gemm2_stream_kernel with E4M3 act fragments (and their scale bytes) in
-// registers and one scaled MFMA per tile and K step.
-template <int NKB>
+// GEMM2 split path, W4A8 (or W4A4 with A4), short K (NKB = I/128 <= 4):
+// the balanced stream of gemm2_stream_kernel with the MX act fragments (and
+// their scale bytes) in registers and one scaled MFMA per tile and K step.
+template <int NKB, bool A4>
 __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
     const uint8_t* __restrict__ actq, const uint8_t* __restrict__ acts,
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
@@ -812,21 +859,23 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
     const size_t row0 = static_cast<size_t>(e) * H + h0 * 16 + r;
     const uint8_t* wp = w2 + (row0 - r) * wrow + r * 64 + g * 16;  // packed layout
     const uint8_t* sp = s2 + row0 * srow;
+    constexpr uint32_t XS = tok_step_bytes<A4>();
+    const uint32_t IB = A4 ? static_cast<uint32_t>(I) / 2 : static_cast<uint32_t>(I);
     const __amdgpu_buffer_rsrc_t qrs =
-        make_rsrc(actq + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I);
+        make_rsrc(actq + static_cast<size_t>(r0) * IB, static_cast<uint32_t>(nrows) * IB);
     const __amdgpu_buffer_rsrc_t ars =
         make_rsrc(acts + static_cast<size_t>(r0) * srow, static_cast<uint32_t>(nrows * srow));
     const __amdgpu_buffer_rsrc_t yrs =
         make_rsrc(y + static_cast<size_t>(r0) * H, static_cast<uint32_t>(nrows) * H * 2);
-    const uint32_t qoff = static_cast<uint32_t>(r) * I + g * 16;
+    const uint32_t qoff = static_cast<uint32_t>(r) * IB + g * 16;
     const uint32_t aoff = static_cast<uint32_t>(r * srow) + g;
     const uint32_t yrow = static_cast<uint32_t>(r) * H * 2 + (h0 * 16 + g * 4) * 2;
     uint4 xa[NKB][2];
     uint32_t xsa[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      xa[kb][0] = bld16(qrs, qoff + kb * 128);
-      xa[kb][1] = bld16(qrs, qoff + kb * 128 + 64);
+      xa[kb][0] = bld16(qrs, qoff + kb * XS);
+      if (!A4) xa[kb][1] = bld16(qrs, qoff + kb * XS + 64);
       xsa[kb] = bld1(ars, aoff + kb * 4);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -851,7 +900,8 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
           f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   #pragma unroll
           for (int kb = 0; kb < NKB; ++kb)
-            acc = mfma_f4xf8(w[a][kb], (sc[a][kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb], acc);
+            acc = mfma_f4xa<A4>(w[a][kb], (sc[a][kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb],
+                                acc);
           __builtin_amdgcn_sched_barrier(0);
           const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
   #pragma unroll
@@ -960,17 +1010,17 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
   return launch_gemm2_dense_tiled(a, st);
 }
 
-hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
+template <bool A4>
+static hipError_t launch_gemm1_mx(const GemmArgs& a, hipStream_t st) {
   const int grid = grid_for(static_cast<long>(a.max_units16) * (a.I / 32));
   const int ring = ring_depth(a.H / 128) >= 2 ? 2 : 1;
   const bool tl = token_tiles_in_lds(a, ring);
-  const size_t lds = static_cast<size_t>(4) * 2 * a.H + (tl ? 2 * kTok8LdsStep : 0);
+  const size_t lds = static_cast<size_t>(4) * 2 * a.H + (tl ? 2 * tok_mx_lds_step<A4>() : 0);
   uint8_t* actq = reinterpret_cast<uint8_t*>(a.act);
 #define MOE_G1A(DD, TL)                                                                          \
-  hipLaunchKernelGGL((gemm1_decode_a8_kernel<DD, TL>), dim3(grid), dim3(kGemmBlock), lds, st, a.xq, \
-                     a.xs, a.w13, a.s13, a.units16, a.counters, a.counts, a.sorted_slot, a.T, a.H,  \
-                     a.I, a.Kp,                                                                 \
-                     a.act_fn, actq, a.act_scales)
+  hipLaunchKernelGGL((gemm1_decode_a8_kernel<DD, TL, A4>), dim3(grid), dim3(kGemmBlock), lds, st, \
+                     a.xq, a.xs, a.w13, a.s13, a.units16, a.counters, a.counts, a.sorted_slot, a.T,  \
+                     a.H, a.I, a.Kp, a.act_fn, actq, a.act_scales)
   if (tl) {
     MOE_G1A(2, true);
   } else {
@@ -985,11 +1035,16 @@ hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
+  return a.a4 ? launch_gemm1_mx<true>(a, st) : launch_gemm1_mx<false>(a, st);
+}
+
+template <bool A4>
+static hipError_t launch_gemm2_stream_mx(const GemmArgs& a, hipStream_t st) {
   const uint8_t* actq = reinterpret_cast<const uint8_t*>(a.act);
   const int gstream = MOE_STREAM_GRID;
-#define MOE_G2SA(NK)                                                                       \
-  hipLaunchKernelGGL(gemm2_stream_a8_kernel<NK>, dim3(gstream), dim3(kGemmBlock), 0, st,  \
+#define MOE_G2SA(NK)                                                                          \
+  hipLaunchKernelGGL((gemm2_stream_a8_kernel<NK, A4>), dim3(gstream), dim3(kGemmBlock), 0, st, \
                      actq, a.act_scales, a.w2, a.s2, a.units16, a.counters, a.counts, a.H, a.I, a.y)
   switch (a.I / 128) {
     case 1: MOE_G2SA(1); break;
@@ -998,7 +1053,12 @@ hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st) {
     default: MOE_G2SA(4); break;
   }
 #undef MOE_G2SA
-  hipError_t err = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st) {
+  const hipError_t err =
+      a.a4 ? launch_gemm2_stream_mx<true>(a, st) : launch_gemm2_stream_mx<false>(a, st);
   if (err != hipSuccess) return err;
   return launch_gemm2_dense_tiled_a8(a, st);
 }

@@ -69,6 +69,21 @@ __device__ __forceinline__ uint32_t tok_off(int r, int c) {
 __device__ __forceinline__ uint32_t tok8_off(int r, int c) {
   return static_cast<uint32_t>(r * 128 + ((c ^ ((r >> 1) & 7)) << 4));
 }
+// Byte offset of 16-byte chunk c (0..3) of E2M1 token row r (64-byte rows):
+// the 32 lanes reading rows r0..r0+15 at chunks g, g' (g, g' < 2, or >= 2)
+// hit 32 distinct 16-byte bank groups of a 512-byte bank line, since rows
+// r and r + 8 (the same 64-byte unit of the line) swap chunk halves.
+__device__ __forceinline__ uint32_t tok4_off(int r, int c) {
+  return static_cast<uint32_t>(r * 64 + ((c ^ (((r >> 3) & 1) << 1)) << 4));
+}
+// MX token row layout of one K stage: E4M3 (128 bytes) or E2M1 (64 bytes).
+template <bool A4>
+__device__ __forceinline__ uint32_t tokmx_off(int r, int c) {
+  if constexpr (A4)
+    return tok4_off(r, c);
+  else
+    return tok8_off(r, c);
+}
 // Byte offset of 16-byte chunk c (0..3) of weight row rho in a stage of
 // ROWS rows (a multiple of 32): chunk-major, so the 32 rows of one MFMA
 // fragment are a permutation of 32 consecutive 16-byte slots (conflict-free
@@ -721,30 +736,36 @@ hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
 }
 
 // ---------------------------------------------------------------------------
-// W4A8 tiled GEMMs: MXFP8 tokens, E2M1 weights fed to the scaled 16x16x128
-// MFMA as they are (no decode). Same block tile, waves and pipeline as
-// above; a token stage is 128 rows x 128 E4M3 bytes (16 KB) plus the rows'
-// four scale bytes. Wave (wm, wn) computes four 16-row weight tiles (GEMM1:
-// gate features +0 / +16, then the up rows of the same features) x four
-// 16-token tiles: 16 MFMAs per K stage.
+// MX-activation tiled GEMMs: W4A8 (MXFP8 tokens) or, with A4, W4A4 (MXFP4
+// tokens), E2M1 weights fed to the scaled 16x16x128 MFMA as they are (no
+// decode). Same block tile, waves and pipeline as above; a token stage is
+// 128 rows x 128 E4M3 bytes (16 KB) or 128 rows x 64 bytes of E2M1 pairs
+// (8 KB), plus the rows' four scale bytes. Wave (wm, wn) computes four
+// 16-row weight tiles (GEMM1: gate features +0 / +16, then the up rows of
+// the same features) x four 16-token tiles: 16 MFMAs per K stage.
 // ---------------------------------------------------------------------------
 namespace {
 constexpr int kTokScStage = kTileRows * 4;    // token scale bytes of one K stage
+constexpr int kTok4Stage = kTileRows * 64;    // E2M1 token bytes of one K stage (8 KB)
 
 }  // namespace
 
-template <bool G1>
+template <bool G1, bool A4>
 __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
     const uint8_t* __restrict__ src, uint32_t src_bytes, const uint8_t* __restrict__ srcs,
     uint32_t srcs_bytes, const uint8_t* __restrict__ w, const uint8_t* __restrict__ s,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ counters,
     const int32_t* __restrict__ sorted_slot, int I, int H, int Kp, int sub, ActArgs actf,
     uint8_t* __restrict__ dstq, uint8_t* __restrict__ dsts, uint16_t* __restrict__ dsty) {
-  __shared__ __attribute__((aligned(16))) uint8_t tok_lds[2 * kTok8Stage];
+  constexpr int kTokSt = A4 ? kTok4Stage : kTok8Stage;
+  constexpr uint32_t XS = A4 ? 64u : 128u;  // token code bytes of a row per K stage
+  constexpr int NTP = A4 ? 1 : 2;           // 16-byte token pieces per thread and stage
+  __shared__ __attribute__((aligned(16))) uint8_t tok_lds[2 * kTokSt];
   __shared__ __attribute__((aligned(16))) uint8_t tsc_lds[2 * kTokScStage];
   __shared__ __attribute__((aligned(16))) uint8_t w_lds[2 * kWStage];
   extern __shared__ __attribute__((aligned(16))) uint8_t s_lds[];
   const int K = G1 ? H : I;
+  const uint32_t KB = A4 ? static_cast<uint32_t>(K) / 2 : static_cast<uint32_t>(K);  // token row bytes
   int ntiles;
   if (G1) {
     ntiles = counters[kCtrNumV];
@@ -793,13 +814,14 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
       }
     }
 
-    // ---- token rows: thread t moves chunk t%8 of rows 64i + t/8, and the
-    // 4 scale bytes of row t%128 (four threads per row store the same word).
-    const int lc = t & 7, lr = t >> 3, sr = t & 127;
+    // ---- token rows: thread t moves chunk t%8 of rows 64i + t/8 (E4M3) or
+    // chunk t%4 of row t/4 (E2M1), and the 4 scale bytes of row t%128 (four
+    // threads per row store the same word).
+    const int lc = A4 ? (t & 3) : (t & 7), lr = A4 ? (t >> 2) : (t >> 3), sr = t & 127;
     uint32_t toff[2], soff;
     {
       uint32_t base[3];
-      const int rr[3] = {lr, 64 + lr, sr};
+      const int rr[3] = {lr, A4 ? lr : 64 + lr, sr};
       if (G1) {
         const __amdgpu_buffer_rsrc_t ssr =
             make_rsrc(sorted_slot + row0, static_cast<uint32_t>(nrows) * 4u);
@@ -814,7 +836,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        toff[i] = base[i] * static_cast<uint32_t>(K) + lc * 16 + (rr[i] < nrows ? 0u : kNoRow);
+        toff[i] = base[i] * KB + lc * 16 + (rr[i] < nrows ? 0u : kNoRow);
       soff = base[2] * static_cast<uint32_t>(srow) + (sr < nrows ? 0u : kNoRow);
     }
     const __amdgpu_buffer_rsrc_t srs = make_rsrc(src, src_bytes);
@@ -833,32 +855,32 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
     uint32_t sv;
     auto load_stage = [&](int kb) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) tv[i] = bld16(srs, toff[i] + kb * 128);
+      for (int i = 0; i < NTP; ++i) tv[i] = bld16(srs, toff[i] + kb * XS);
       sv = bld4(ssc, soff + kb * 4);
 #pragma unroll
       for (int i = 0; i < 2; ++i) wv[i] = ld16(wsrc[i] + kb * kPkBlock);
     };
-    // piece p of load_stage (same order as store_piece)
+    // piece p of load_stage (same order as store_piece; E2M1 tokens have no piece 1)
     auto load_piece = [&](int kb, int p) {
-      if (p < 2) tv[p] = bld16(srs, toff[p] + kb * 128);
+      if (p < NTP) tv[p] = bld16(srs, toff[p] + kb * XS);
       else if (p == 2) sv = bld4(ssc, soff + kb * 4);
-      else wv[p - 3] = ld16(wsrc[p - 3] + kb * kPkBlock);
+      else if (p > 2) wv[p - 3] = ld16(wsrc[p - 3] + kb * kPkBlock);
     };
     // piece p of store_stage: token chunks 0, 1, the scale word 2, weight chunks 3, 4
     auto store_piece = [&](int b, int p) {
-      if (p < 2) {
-        *reinterpret_cast<uint4*>(tok_lds + b * kTok8Stage + tok8_off(p * 64 + lr, lc)) = tv[p];
+      if (p < NTP) {
+        *reinterpret_cast<uint4*>(tok_lds + b * kTokSt + tokmx_off<A4>(p * 64 + lr, lc)) = tv[p];
       } else if (p == 2) {
         *reinterpret_cast<uint32_t*>(tsc_lds + b * kTokScStage + sr * 4) = sv;
-      } else {
+      } else if (p > 2) {
         *reinterpret_cast<uint4*>(w_lds + b * kWStage + w_off((p - 3) * 128 + wr, wc)) = wv[p - 3];
       }
     };
     auto store_stage = [&](int b) {
-      uint8_t* tb = tok_lds + b * kTok8Stage;
+      uint8_t* tb = tok_lds + b * kTokSt;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        *reinterpret_cast<uint4*>(tb + tok8_off(i * 64 + lr, lc)) = tv[i];
+      for (int i = 0; i < NTP; ++i)
+        *reinterpret_cast<uint4*>(tb + tokmx_off<A4>(i * 64 + lr, lc)) = tv[i];
       *reinterpret_cast<uint32_t*>(tsc_lds + b * kTokScStage + sr * 4) = sv;
       uint8_t* wb = w_lds + b * kWStage;
 #pragma unroll
@@ -889,7 +911,7 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
 
     for (int kb = 0; kb < nkb; ++kb) {
       const int b = kb & 1;
-      const uint8_t* tb = tok_lds + b * kTok8Stage;
+      const uint8_t* tb = tok_lds + b * kTokSt;
       const uint8_t* tsb = tsc_lds + b * kTokScStage;
       const uint8_t* wb = w_lds + b * kWStage;
       uint4 af[4];
@@ -899,8 +921,8 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
       uint32_t bsc, bsn;
       auto read_x = [&](int nt, uint4& x0, uint4& x1, uint32_t& bs) {
         const int tr = wm * 64 + nt * 16 + c;
-        x0 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, g));
-        x1 = *reinterpret_cast<const uint4*>(tb + tok8_off(tr, 4 + g));
+        x0 = *reinterpret_cast<const uint4*>(tb + tokmx_off<A4>(tr, g));
+        if (!A4) x1 = *reinterpret_cast<const uint4*>(tb + tokmx_off<A4>(tr, 4 + g));
         bs = tsb[tr * 4 + g];
       };
       __builtin_amdgcn_sched_barrier(0);
@@ -918,15 +940,15 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
         load_piece(min(kb + 2, last), nt);  // the piece's register is free once stored
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          acc[mt][nt] = mfma_f4xf8(af[mt], as[mt], x0c, x1c, bsc, acc[mt][nt]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads first
+          acc[mt][nt] = mfma_f4xa<A4>(af[mt], as[mt], x0c, x1c, bsc, acc[mt][nt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, A4 ? 2 : 3, 0);  // LDS reads first
         __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // one LDS write
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one global load
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
         __builtin_amdgcn_sched_barrier(0);
         if (nt < 3) {
           x0c = x0n;
-          x1c = x1n;
+          if (!A4) x1c = x1n;
           bsc = bsn;
         }
       }
@@ -943,8 +965,9 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
     if (G1) {
       const int fbase = f0 + wn * 32;
       const uint32_t srow_a = static_cast<uint32_t>(I) >> 5;
+      const uint32_t IB = A4 ? static_cast<uint32_t>(I) / 2 : static_cast<uint32_t>(I);
       const __amdgpu_buffer_rsrc_t qrs =
-          make_rsrc(dstq + static_cast<size_t>(row0) * I, static_cast<uint32_t>(nrows) * I);
+          make_rsrc(dstq + static_cast<size_t>(row0) * IB, static_cast<uint32_t>(nrows) * IB);
       const __amdgpu_buffer_rsrc_t ars =
           make_rsrc(dsts + static_cast<size_t>(row0) * srow_a, static_cast<uint32_t>(nrows) * srow_a);
 #pragma unroll
@@ -960,12 +983,20 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(a[i]));
         amax = fmaxf(amax, __shfl_xor(amax, 16, kWave));
         amax = fmaxf(amax, __shfl_xor(amax, 32, kWave));
-        const uint32_t sb = mxfp8_scale_byte(amax);
-        const float inv = mxfp8_inv_scale(sb);
-        const uint32_t o0 = tr * I + fbase + 4 * g;
-        bst4(qrs, o0, pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
-        bst4(qrs, o0 + 16, pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
-        bst1(ars, g == 0 ? tr * srow_a + (fbase >> 5) : kNoRow, sb);
+        const uint32_t e0 = tr * I + fbase + 4 * g;  // element index of a[0]
+        if constexpr (A4) {
+          const uint32_t sb = mxfp4_scale_byte(amax);
+          const float inv = mx_inv_scale(sb);
+          bst2(qrs, e0 / 2, pack_e2m1x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
+          bst2(qrs, e0 / 2 + 8, pack_e2m1x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
+          bst1(ars, g == 0 ? tr * srow_a + (fbase >> 5) : kNoRow, sb);
+        } else {
+          const uint32_t sb = mxfp8_scale_byte(amax);
+          const float inv = mxfp8_inv_scale(sb);
+          bst4(qrs, e0, pack_e4m3x4(a[0] * inv, a[1] * inv, a[2] * inv, a[3] * inv));
+          bst4(qrs, e0 + 16, pack_e4m3x4(a[4] * inv, a[5] * inv, a[6] * inv, a[7] * inv));
+          bst1(ars, g == 0 ? tr * srow_a + (fbase >> 5) : kNoRow, sb);
+        }
       }
     } else {
       const int fbase = f0 + wn * 64;
@@ -989,12 +1020,15 @@ __global__ __launch_bounds__(kTiledThreads, 1) void gemm_tiled_a8_kernel(
 hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
   const int sub = a.B > kTileRows ? a.B / kTileRows : 1;
   const int grid = tiled_grid(static_cast<long>(a.kmax_v) * sub * (a.I / 128), 1);
-  hipLaunchKernelGGL(gemm_tiled_a8_kernel<true>, dim3(grid), dim3(kTiledThreads),
-                     static_cast<size_t>(8) * a.H, st, a.xq,
-                     static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H), a.xs,
-                     static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H / 32), a.w13, a.s13,
-                     a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp, sub, a.act_fn,
-                     reinterpret_cast<uint8_t*>(a.act), a.act_scales, nullptr);
+  const size_t xbytes = static_cast<size_t>(a.T) * a.H / (a.a4 ? 2 : 1);
+#define MOE_GT1A(A4)                                                                          \
+  hipLaunchKernelGGL((gemm_tiled_a8_kernel<true, A4>), dim3(grid), dim3(kTiledThreads),      \
+                     static_cast<size_t>(8) * a.H, st, a.xq, static_cast<uint32_t>(xbytes),  \
+                     a.xs, static_cast<uint32_t>(static_cast<size_t>(a.T) * a.H / 32), a.w13, \
+                     a.s13, a.vinfo, a.counters, a.sorted_slot, a.I, a.H, a.Kp, sub, a.act_fn, \
+                     reinterpret_cast<uint8_t*>(a.act), a.act_scales, nullptr)
+  if (a.a4) MOE_GT1A(true); else MOE_GT1A(false);
+#undef MOE_GT1A
   return hipGetLastError();
 }
 
@@ -1010,14 +1044,15 @@ hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
 // group ahead; outputs go through the wave's LDS staging rows like the bf16
 // kernel's. LDS: 128 * I * 33 / 32 + 64 KB.
 // ---------------------------------------------------------------------------
-template <int NKB>
+template <int NKB, bool A4>
 __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
     const uint8_t* __restrict__ actq, uint32_t actq_bytes, const uint8_t* __restrict__ acts,
     uint32_t acts_bytes, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ counters, int H,
     uint16_t* __restrict__ y) {
   constexpr int I = NKB * 128;
-  constexpr int kRowB = I;  // E4M3 act bytes per row
+  constexpr int kRowB = A4 ? I / 2 : I;  // act code bytes per row: E2M1 pairs or E4M3
+  constexpr int XS = A4 ? 64 : 128;      // of which one K step
   __shared__ __attribute__((aligned(16))) uint8_t a_lds[kTileRows * kRowB];
   // act scales, [kb][row][4]: the four 32-K scale bytes of K step kb
   __shared__ __attribute__((aligned(16))) uint8_t as_lds[NKB * kTileRows * 4];
@@ -1032,16 +1067,21 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
   const int c = lane & 15, g = lane >> 4;
   const int nspan = H >> 8;
   constexpr uint32_t wrow = I / 2, srow = I / 32;
-  // act chunk q (16 bytes; 8 per K step) of tile row rr: within each K
-  // step's 8 chunks the index is XORed with (rr >> 1) & 7, which puts the 16
-  // rows of one MFMA fragment on 16 distinct 16-byte bank groups
-  auto a_off = [](int rr, int q) -> uint32_t {
-    return static_cast<uint32_t>(rr * kRowB + (((q & ~7) | ((q ^ (rr >> 1)) & 7)) << 4));
+  // act chunk q (16 bytes; 8 per K step for E4M3) of tile row rr: within
+  // each K step's 8 chunks the index is XORed with (rr >> 1) & 7, which puts
+  // the 16 rows of one MFMA fragment on 16 distinct 16-byte bank groups.
+  // E2M1: 4 chunks per K step, XORed with ((rr >> 3) & 1) << 1 (rows r and
+  // r + 8 swap chunk halves).
+  auto swz = [](int rr) -> int { return A4 ? (((rr >> 3) & 1) << 1) : ((rr >> 1) & 7); };
+  auto a_off = [&](int rr, int q) -> uint32_t {
+    constexpr int m = A4 ? 3 : 7;
+    return static_cast<uint32_t>(rr * kRowB + (((q & ~m) | ((q ^ swz(rr)) & m)) << 4));
   };
   // lane's fragment bases (token c of a 16-token tile, chunks g and 4 + g of
-  // a K step); tile nt and step kb add nt * 16 * kRowB + kb * 128
-  const uint8_t* xb0 = a_lds + c * kRowB + (((g ^ (c >> 1)) & 7) << 4);
-  const uint8_t* xb1 = a_lds + c * kRowB + ((((4 + g) ^ (c >> 1)) & 7) << 4);
+  // a K step, or chunk g for E2M1); tile nt and step kb add
+  // nt * 16 * kRowB + kb * XS (nt * 16 leaves the swizzle unchanged)
+  const uint8_t* xb0 = a_lds + c * kRowB + (((g ^ swz(c)) & (A4 ? 3 : 7)) << 4);
+  const uint8_t* xb1 = a_lds + c * kRowB + ((((4 + g) ^ swz(c)) & 7) << 4);
   const uint8_t* sbase = as_lds + c * 4 + g;  // + (kb * 128 + nt * 16) * 4
   const uint32_t wv_off = static_cast<uint32_t>(c) * 64 + g * 16;  // packed layout
   const uint32_t sv_off = static_cast<uint32_t>(c) * srow + g;
@@ -1107,8 +1147,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
       uint32_t bsc, bsn;
       auto read_x = [&](int st, uint4& x0, uint4& x1, uint32_t& bs) {
         const int kb = st >> 3, nt = st & 7;
-        x0 = *reinterpret_cast<const uint4*>(xb0 + nt * 16 * kRowB + kb * 128);
-        x1 = *reinterpret_cast<const uint4*>(xb1 + nt * 16 * kRowB + kb * 128);
+        x0 = *reinterpret_cast<const uint4*>(xb0 + nt * 16 * kRowB + kb * XS);
+        if (!A4) x1 = *reinterpret_cast<const uint4*>(xb1 + nt * 16 * kRowB + kb * XS);
         bs = sbase[(kb * kTileRows + nt * 16) * 4];
       };
       __builtin_amdgcn_sched_barrier(0);
@@ -1120,8 +1160,8 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
         if (st + 1 < 8 * NKB) read_x(st + 1, x0n, x1n, bsn);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
-          acc[mt][nt] = mfma_f4xf8(wf[kb][mt], ws[kb][mt], x0c, x1c, bsc, acc[mt][nt]);
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads first
+          acc[mt][nt] = mfma_f4xa<A4>(wf[kb][mt], ws[kb][mt], x0c, x1c, bsc, acc[mt][nt]);
+        __builtin_amdgcn_sched_group_barrier(0x100, A4 ? 2 : 3, 0);  // LDS reads first
         __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // then the MFMAs
         __builtin_amdgcn_sched_barrier(0);
         if (nt == 7) {  // step kb done: refill it with the next span
@@ -1129,7 +1169,7 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
           __builtin_amdgcn_sched_barrier(0);
         }
         x0c = x0n;
-        x1c = x1n;
+        if (!A4) x1c = x1n;
         bsc = bsn;
       }
       // ---- this span's 64 x 128 outputs through the wave's LDS staging rows
@@ -1164,14 +1204,15 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
   }
 }
 
-hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
-  // the W4A8 path admits I <= 512 only, so the act tile always fits in LDS
+template <bool A4>
+static hipError_t launch_gemm2_resident_mx(const GemmArgs& a, hipStream_t st) {
+  // the MX paths admit I <= 512 only, so the act tile always fits in LDS
   const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles), 1);
   const uint8_t* actq = reinterpret_cast<const uint8_t*>(a.act);
-  const uint32_t qb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I);
+  const uint32_t qb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / (A4 ? 2 : 1));
   const uint32_t sb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / 32);
-#define MOE_G2RA(NK)                                                                          \
-  hipLaunchKernelGGL(gemm2_resident_a8_kernel<NK>, dim3(grid), dim3(256), 0, st, actq, qb,   \
+#define MOE_G2RA(NK)                                                                           \
+  hipLaunchKernelGGL((gemm2_resident_a8_kernel<NK, A4>), dim3(grid), dim3(256), 0, st, actq, qb, \
                      a.act_scales, sb, a.w2, a.s2, a.dense_tiles, a.counters, a.H, a.y)
   switch (a.I / 128) {
     case 1: MOE_G2RA(1); break;
@@ -1181,6 +1222,10 @@ hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
   }
 #undef MOE_G2RA
   return hipGetLastError();
+}
+
+hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
+  return a.a4 ? launch_gemm2_resident_mx<true>(a, st) : launch_gemm2_resident_mx<false>(a, st);
 }
 
 }  // namespace moe

@@ -51,11 +51,13 @@ struct GemmArgs {
   int Ep;  // local experts including the shared ones
   int dense_grid_tiles;  // tiles the dense GEMM2 grid is sized for (the kernels loop past it)
   ActArgs act_fn;  // GEMM1 epilogue activation
-  uint16_t* act;  // [rows_pad, I] bf16 (W4A16), or E4M3 codes (W4A8)
+  uint16_t* act;  // [rows_pad, I] bf16 (W4A16), E4M3 codes (W4A8) or E2M1 code pairs [rows_pad, I/2] (W4A4)
   uint16_t* y;    // [rows_pad, H] bf16
-  // W4A8 only (a8 != 0): MXFP8 x and act scales
+  // MX activations (a8 != 0: W4A8 MXFP8, or W4A4 MXFP4 when a4 is also set):
+  // quantised x and act scales
   int a8;
-  const uint8_t* xq;    // [T, H] E4M3
+  int a4;
+  const uint8_t* xq;    // [T, H] E4M3 (W4A8) or [T, H/2] E2M1 pairs (W4A4)
   const uint8_t* xs;    // [T, H/32] E8M0
   uint8_t* act_scales;  // [rows_pad, I/32] E8M0
 };
@@ -66,10 +68,12 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st);  // split + dense, g
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st);
 
-// x -> MXFP8 (W4A8 path): xq [T, H] E4M3 codes, xs [T, H/32] E8M0 scales.
-hipError_t launch_quant_x(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs,
+// x -> MXFP8 (W4A8 path: xq [T, H] E4M3 codes) or MXFP4 (a4, W4A4 path:
+// xq [T, H/2] E2M1 code pairs), xs [T, H/32] E8M0 scales.
+hipError_t launch_quant_x(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, bool a4,
                           hipStream_t st);
-// W4A8 kernels (the launchers above dispatch to them when a8 is set).
+// MX-activation kernels, W4A8 or W4A4 by a4 (the launchers above dispatch to
+// them when a8 is set).
 hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st);

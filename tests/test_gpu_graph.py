@@ -19,7 +19,7 @@ from gpu_util import check_maps, check_out, lib_shape, maps_np, out_np, say, to_
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("a_dtype", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("a_dtype", ["bf16", "mxfp8", "mxfp4"])
 def test_graph_replay_follows_inputs_across_the_gate(a_dtype):
     s = LayerShape("graph_gate", T=256, E=64, E_g=64, topk=4, H=512, I=128, B=32, a_dtype=a_dtype)
     inp = make_inputs(s, 777)

@@ -10,8 +10,8 @@ bit for bit.
 - Power-of-two scales: adding 1 to every E8M0 byte of W2 doubles W2 exactly,
   hence Y and the output. Without a clamp, SwiGLU is linear in the up half,
   so adding 1 to the up rows' W13 scale bytes doubles the output too. This
-  holds on the W4A8 path as well: the MXFP8 scale of a doubled block moves
-  up by one and its codes stay the same.
+  holds on the W4A8 and W4A4 paths as well: the MX scale of a doubled block
+  moves up by one and its codes stay the same.
 - Tokens with no local expert (every id outside the local range, or masked
   with -1) give exact zeros; a masked slot gives the same output bits as the
   same slot routed to a local expert with weight 0.
@@ -41,6 +41,8 @@ INV = [
     LayerShape("inv_split_long_k", T=40, E=16, E_g=16, topk=4, H=512, I=640, B=32),
     LayerShape("inv_decode_w4a8", T=64, E=64, E_g=64, topk=8, H=512, I=256, B=32, a_dtype="mxfp8"),
     LayerShape("inv_prefill_w4a8", T=512, E=8, E_g=8, topk=2, H=512, I=128, B=128, a_dtype="mxfp8"),
+    LayerShape("inv_decode_w4a4", T=64, E=64, E_g=64, topk=8, H=512, I=256, B=32, a_dtype="mxfp4"),
+    LayerShape("inv_prefill_w4a4", T=512, E=8, E_g=8, topk=2, H=512, I=384, B=128, a_dtype="mxfp4"),
 ]
 FORCES = ["auto", "split", "dense"]
 SEED = 4242
@@ -125,7 +127,7 @@ def test_off_range_tokens_are_exact_zeros(B):
 
 
 @pytest.mark.parametrize("force", ["split", "dense"])
-@pytest.mark.parametrize("a_dtype", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("a_dtype", ["bf16", "mxfp8", "mxfp4"])
 def test_masked_ids_contribute_nothing(force, a_dtype):
     s = LayerShape("masked_ids", T=29, E=16, E_g=40, topk=5, H=512, I=128, B=16,
                    expert_offset=10, mode="ids", a_dtype=a_dtype)

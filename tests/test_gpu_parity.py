@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import mxfp4_weight_expert_amd as moe
-from workloads import CONFIGS, CONFIG_ORDER, LayerShape, config_seed, make_inputs
+from workloads import CONFIGS, CONFIG_ORDER, LayerShape, config_seed, f32_to_bf16_bits, make_inputs
 
 from gpu_util import (bf16_dev, check_maps, check_out, covering_tokens, maps_np, oracle_rows,
                       out_np, run, say, to_device)
@@ -215,6 +215,73 @@ def test_w4a8_quant_special_values():
     ref = oracle.reference_forward(s, inp)
     out, ws = run(s, to_device(s, inp))
     _check_xq(maps_np(s, ws), ref)
+
+
+# ------------------------------------------------------------------ W4A4
+# MXFP4 activations (the FP4 path of "SGLang CUTLASS MoE", section 6, in the
+# weights' MX block format): x's codes and scales bit-exact; outputs to the
+# same tolerances against the quantisation-aware oracle (an act code at an
+# E2M1 rounding boundary may land one step apart, since act is quantised
+# from fp32 here and from fp64 there).
+SMALL_A4 = [s.replace(name=s.name.replace("a8_", "a4_"), a_dtype="mxfp4") for s in SMALL_A8]
+
+
+@pytest.mark.parametrize("force", list(FORCES))
+@pytest.mark.parametrize("s", SMALL_A4, ids=lambda s: s.name)
+def test_w4a4_small_full_parity(s, force):
+    say(f"[w4a4] {s.name} force={force}")
+    inp = make_inputs(s, 800 + SMALL_A4.index(s))
+    ref = oracle.reference_forward(s, inp, force_path=FORCES[force])
+    dev = to_device(s, inp)
+    out, ws = run(s, dev, force)
+    got = maps_np(s, ws, force)
+    check_maps(s, got, ref)
+    _check_xq(got, ref)
+    check_out(out_np(out), ref["out"], f"{s.name}/{force}")
+
+
+def test_w4a4_quant_special_values():
+    """Zero, signed-zero, subnormal, saturating and exact-tie blocks of x."""
+    s = LayerShape("a4_special", T=6, E=4, E_g=4, topk=2, H=512, I=128, B=16, a_dtype="mxfp4")
+    inp = make_inputs(s, 78)
+    x = inp["x"].copy()
+    x[0, :32] = 0                      # all-zero block -> scale 0, codes 0
+    x[0, 32:64] = 0x8000               # negative zeros -> codes 8
+    x[1, :32] = 0x0001                 # bf16 subnormals: scale byte clamps to 0
+    x[1, 32:64] = 0x7F00               # 2^127: scale byte 252, code 6 (4.0)
+    x[2, :32] = np.arange(32, dtype=np.uint16) + 0x3F80  # 1.0 .. just above
+    x[3, :32] = 0xC0C0                 # -6 exactly
+    x[3, 32:64] = 0x40E0               # 7: saturates to 6 after scaling
+    # ties between E2M1 neighbours (amax 5 -> scale 1): 0.25 .. 5.0, both signs
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    x[4, :32] = f32_to_bf16_bits(np.resize(np.concatenate([ties, -ties]), 32))
+    x[5, :32] = f32_to_bf16_bits(np.resize(np.concatenate([ties, -ties]) * np.float32(2 ** -20), 32))
+    inp["x"] = x
+    ref = oracle.reference_forward(s, inp)
+    out, ws = run(s, to_device(s, inp))
+    _check_xq(maps_np(s, ws), ref)
+
+
+@pytest.mark.parametrize("name", ["decode", "decode_ep", "prefill"])
+def test_w4a4_config_parity(name):
+    s = CONFIGS[name].replace(a_dtype="mxfp4", name=name + "_w4a4")
+    say(f"[w4a4 config] {s.name}")
+    inp = make_inputs(s, config_seed(name))
+    dev = to_device(s, inp)
+    ref = oracle.reference_forward(s, inp, compute_out=False)
+    if name == "prefill":
+        toks = covering_tokens(ref, s.Kp, s.B, 128)
+        want = oracle_rows(s, inp, toks)
+    else:
+        toks = _sample_tokens(s.T, 8, 12)
+        want = oracle.sampled_forward(s, inp, toks)
+    out, ws = run(s, dev)
+    got = maps_np(s, ws)
+    check_maps(s, got, ref)
+    _check_xq(got, ref)
+    check_out(out_np(out)[toks], want, f"{s.name} sampled tokens {len(toks)}")
+    del out, ws
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["decode", "decode_ep", "prefill"])
