@@ -31,6 +31,35 @@ constexpr int kGemmBlock = 256;  // 4 waves, one item each at a time
 // split GEMMs from 693 / 416 to 675 / 403 us on MI355X; the T64 and T256
 // decode shapes did not change.
 constexpr int kMaxGrid = 256 * 16;
+
+// XCD-aware item ranges. The hardware deals consecutive block ids round-robin
+// over the 8 XCDs, each with its own L2. The item list (unit-major: all
+// feature groups of a unit, then the next unit) is cut into 8 contiguous
+// ranges, one per XCD, and the blocks of an XCD walk their range. The units
+// of one expert are consecutive items, so an expert whose rows span several
+// units is read by waves of one XCD at about the same time and its weights
+// are re-read from that L2 instead of crossing XCDs. The range length is a
+// multiple of 4, so the four waves of a block always take four consecutive
+// items of one unit (the grid is a multiple of 8).
+struct XcdItems {
+  int first, step, end;  // this wave's first item, its stride, the range end
+};
+__device__ __forceinline__ XcdItems xcd_items(int nitems) {
+  const int xcd = static_cast<int>(blockIdx.x) & 7;
+  const int per = (((nitems + 7) >> 3) + 3) & ~3;
+  const int lo = xcd * per;
+  XcdItems r;
+  r.first = lo + (static_cast<int>(blockIdx.x) >> 3) * 4 + wave_index();
+  r.step = (static_cast<int>(gridDim.x) >> 3) * 4;
+  r.end = min(lo + per, nitems);
+  return r;
+}
+// The same split for wave-owned contiguous ranges: consecutive wave ids on
+// one XCD.
+__device__ __forceinline__ int64_t xcd_wave_id() {
+  const int64_t lb = static_cast<int64_t>(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+  return lb * 4 + wave_index();
+}
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -262,7 +291,8 @@ __device__ __forceinline__ void gemm1_decode_items(
     lofs[2 * p] = static_cast<uint32_t>(16 * p * srow);
     lofs[2 * p + 1] = static_cast<uint32_t>(blk + 16 * p * srow);
   }
-  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
+  const XcdItems xi = xcd_items(nitems);
+  for (int item = xi.first; item < xi.end; item += xi.step) {
     const int u = item / groups;
     const int f0 = (item - u * groups) * 16 * TP;
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
@@ -392,7 +422,8 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
                             static_cast<uint32_t>(48 * wrow)};
   const uint32_t lofs[4] = {0u, static_cast<uint32_t>(16 * srow), static_cast<uint32_t>(32 * srow),
                             static_cast<uint32_t>(48 * srow)};
-  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
+  const XcdItems xi = xcd_items(nitems);
+  for (int item = xi.first; item < xi.end; item += xi.step) {
     const int u = item / quads;
     const int h0 = (item - u * quads) * 64;
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
@@ -485,7 +516,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
   const int tpu = H >> 4;  // tiles per unit
   const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave_index();
+  const int64_t wid = xcd_wave_id();
   int64_t t = total * wid / nwaves;
   const int64_t t_end = total * (wid + 1) / nwaves;
   const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
@@ -773,7 +804,8 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
   const uint32_t srow_a = static_cast<uint32_t>(I) >> 5;
   uint8_t* tl = lds_scales + 4 * 2 * blk;
   const int tt = static_cast<int>(threadIdx.x);
-  for (int item = blockIdx.x * 4 + wave_index(); item < nitems; item += gridDim.x * 4) {
+  const XcdItems xi = xcd_items(nitems);
+  for (int item = xi.first; item < xi.end; item += xi.step) {
     const int u = item / groups;
     const int f0 = (item - u * groups) * 32;
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
@@ -844,7 +876,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
   const int tpu = H >> 4;
   const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
-  const int64_t wid = static_cast<int64_t>(blockIdx.x) * 4 + wave_index();
+  const int64_t wid = xcd_wave_id();
   int64_t t = total * wid / nwaves;
   const int64_t t_end = total * (wid + 1) / nwaves;
   const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
@@ -936,10 +968,12 @@ static bool token_tiles_in_lds(const GemmArgs& a, int ring) {
   return ring == 2 && static_cast<long>(a.T) * a.Kp >= 2L * a.Ep;
 }
 
+// One block per four items, at most kMaxGrid, a multiple of 8 (xcd_items).
 static int grid_for(long items) {
   long blocks = (items + 3) / 4;
-  if (blocks < 1) blocks = 1;
-  return static_cast<int>(blocks < kMaxGrid ? blocks : kMaxGrid);
+  if (blocks < 8) blocks = 8;
+  if (blocks > kMaxGrid) blocks = kMaxGrid;
+  return static_cast<int>((blocks + 7) / 8 * 8);
 }
 
 hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
