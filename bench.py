@@ -105,7 +105,7 @@ def measured_traffic(config: str, kernel: str):
                     with open(os.path.join(csrc, src), "rb") as g:
                         h.update(g.read())
                 if h.hexdigest()[:16] == rec["src_sha256_16"]:
-                    return rec["traffic_bytes"]
+                    return rec.get("traffic_bytes")
     return None
 
 
