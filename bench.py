@@ -302,7 +302,9 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
     for label, kname, us, b, f in (("gemm1", k1, stages["gemm1"], gemm1_bytes, gemm1_flops),
                                    ("gemm2", k2, stages["gemm2"], gemm2_bytes, gemm2_flops)):
         r = roof(b, f, us, compute_bound)
-        r.update(kernel=kname, kernel_us=us, traffic=measured_traffic(s.name, kname))
+        r.update(kernel=kname, kernel_us=us,
+                 traffic=measured_traffic(s.name if s.a_dtype == "bf16" else f"{s.name}/{s.a_dtype}",
+                                          kname))
         kernels[label] = r
     layer = roof(layer_bytes, layer_flops, med, compute_bound)
     layer["basis"] = "median replay time of the whole layer"
