@@ -953,9 +953,17 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
   }
 }
 
-// Persistent grid of the streaming GEMM2 kernels: waves split the tile list evenly.
+// Persistent grid of the streaming GEMM2 kernels: waves split the tile list
+// evenly. One block per CU (one wave per SIMD): on MI355X, 768 blocks (three
+// per CU, the register limit) kept more loads in flight but streamed slower
+// (T64 decode 83.8 -> 80.5 us, Zipf-routed T256 EP decode 31.2 -> 27.6 us
+// with one block per CU). Timestamps taken per wave showed why: of the three
+// blocks sharing a CU the first-dispatched one finished in about 35 us, the
+// second in 57 and the third in 72 (the oldest wave issues first), while
+// the chip's read rate rose from about 6 to 7.3-7.9 TB/s as the number of
+// waves streaming at once fell. 128 or 192 blocks, or a ring of 2, lose.
 #ifndef MOE_STREAM_GRID
-#define MOE_STREAM_GRID (256 * 3)
+#define MOE_STREAM_GRID 256
 #endif
 
 // Token tiles through LDS (stream_block_lds) pay off once chunks carry
