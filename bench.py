@@ -303,10 +303,16 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
         k1 = "gemm1_decode_a8_kernel" if a8 else "gemm1_decode_kernel"
     else:
         k1 = "gemm_tiled_a8_kernel<true>" if a8 else "gemm_tiled_kernel<true>"
-    if dense:
-        k2 = "gemm2_resident_a8_kernel" if a8 else "gemm2_resident_kernel"
+    # GEMM2: one gated launch runs either path (MX act, or bf16 act with
+    # I <= 384); beyond that the split kernel and the generic tiled dense one
+    if a8:
+        k2 = "gemm2_gated_mx_kernel"
+    elif s.I <= 384:
+        k2 = "gemm2_gated_kernel"
+    elif dense:
+        k2 = "gemm_tiled_kernel<false>"
     else:
-        k2 = "gemm2_stream_a8_kernel" if a8 else "gemm2_stream_kernel"
+        k2 = "gemm2_stream_kernel" if s.I == 512 else "gemm2_split_kernel"
     kernels = {}
     for label, kname, us, b, f in (("gemm1", k1, stages["gemm1"], gemm1_bytes, gemm1_flops),
                                    ("gemm2", k2, stages["gemm2"], gemm2_bytes, gemm2_flops)):

@@ -26,6 +26,7 @@ constexpr int kRangeSlots = 1024;
 constexpr int kSmallSlots = 8192;  // up to this many slots the sort runs in one block
 constexpr int kGateTau = 64;       // dense GEMM2 when rows >= kGateTau * touched experts
 constexpr int kDenseMT = 128;      // dense-path row tile
+constexpr int kResidentMaxI = 384;  // largest I whose bf16 dense-path act tile stays in LDS
 constexpr int kMaxTiledK = 8192;   // largest H and I (LDS budget of the tiled GEMMs)
 constexpr int kCounterWords = 64;
 constexpr int kCtrNumV = 0;

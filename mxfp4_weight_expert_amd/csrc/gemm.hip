@@ -19,6 +19,7 @@
 // and keeps every weight load a contiguous 16 bytes.
 #include "common.h"
 #include "kernels.h"
+#include "gemm2_stream.h"
 
 namespace moe {
 
@@ -53,12 +54,6 @@ __device__ __forceinline__ XcdItems xcd_items(int nitems) {
   r.step = (static_cast<int>(gridDim.x) >> 3) * 4;
   r.end = min(lo + per, nitems);
   return r;
-}
-// The same split for wave-owned contiguous ranges: consecutive wave ids on
-// one XCD.
-__device__ __forceinline__ int64_t xcd_wave_id() {
-  const int64_t lb = static_cast<int64_t>(blockIdx.x & 7) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-  return lb * 4 + wave_index();
 }
 }  // namespace
 
@@ -489,21 +484,10 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
   }
 }
 
-// GEMM2 split path for short K (NKB = I/128 <= 4 steps), balanced stream.
-// The work unit is a 16-row tile of one 16-row unit's output over the full
-// K. Waves own equal contiguous ranges of the unit-major tile list, so the
-// last wave ends at most one tile after the first. Within the part of its
-// range that falls in one unit, a wave keeps the unit's activation fragments
-// in registers and streams tiles through a ring kStreamAhead tiles deep;
-// each tile's scales come in with one 16-byte load per lane (the row's I/32
-// bytes). The ring is unrolled by kStreamAhead; iterations past the range
-// recompute the last tile and their stores fall outside the unit's output
-// buffer, so the hardware drops them (no branches in the stream).
-#ifndef MOE_STREAM_AHEAD
-#define MOE_STREAM_AHEAD 4
-#endif
-constexpr int kStreamAhead = MOE_STREAM_AHEAD;
-
+// GEMM2 split path for short K with bf16 act where no resident dense kernel
+// exists (384 < I <= 512): the stream of gemm2_stream.h in a launch of its
+// own, next to the generic tiled dense kernel. For I <= 384 both paths run
+// in one gated launch (gemm_tiled.hip).
 template <int NKB>
 __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2,
@@ -511,84 +495,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
     const int32_t* __restrict__ counters, const int32_t* __restrict__ counts, int H, int I,
     uint16_t* __restrict__ y) {
   if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
-  const int lane = lane_id();
-  const int r = lane & 15, g = lane >> 4;
-  const int tpu = H >> 4;  // tiles per unit
-  const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
-  const int64_t wid = xcd_wave_id();
-  int64_t t = total * wid / nwaves;
-  const int64_t t_end = total * (wid + 1) / nwaves;
-  const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
-  const uint32_t tstride = static_cast<uint32_t>(16 * wrow);
-  const uint32_t sstride = static_cast<uint32_t>(16 * srow);
-  while (t < t_end) {
-    const int u = static_cast<int>(t / tpu);
-    const int h0 = static_cast<int>(t - static_cast<int64_t>(u) * tpu);  // first tile
-    const int nt = static_cast<int>(min(t_end, static_cast<int64_t>(u + 1) * tpu) - t);
-    const int4 ui = reinterpret_cast<const int4*>(units)[u];
-    const int e = ui.x, r0 = ui.y, nrows = ui.z;
-    const size_t row0 = static_cast<size_t>(e) * H + h0 * 16 + r;
-    const uint8_t* wp = w2 + (row0 - r) * wrow + r * 64 + g * 16;  // packed layout
-    const uint8_t* sp = s2 + row0 * srow;
-    const __amdgpu_buffer_rsrc_t ars =
-        make_rsrc(act + static_cast<size_t>(r0) * I, static_cast<uint32_t>(nrows) * I * 2);
-    const __amdgpu_buffer_rsrc_t yrs =
-        make_rsrc(y + static_cast<size_t>(r0) * H, static_cast<uint32_t>(nrows) * H * 2);
-    const uint32_t boff = static_cast<uint32_t>(r) * I * 2 + g * 64;
-    const uint32_t yrow = static_cast<uint32_t>(r) * H * 2 + (h0 * 16 + g * 4) * 2;
-    uint4 xa[NKB][4];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) xa[kb][j] = bld16(ars, boff + kb * 256 + j * 16);
-    __builtin_amdgcn_sched_barrier(0);
-    // weights read once in this call (the expert's only unit): non-temporal
-    auto seg = [&](auto ntw) {
-      constexpr bool NTW = decltype(ntw)::value;
-      uint4 w[kStreamAhead][NKB];
-      uint32_t sc[kStreamAhead][NKB];  // the lane row's I/32 scale bytes
-      // prologue in slot order (pinned): the loop head then sees the same
-      // pending-load order on entry as on every later iteration
-  #pragma unroll
-      for (int a = 0; a < kStreamAhead; ++a) {
-        const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
-  #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-        ld_dwords(sp + ti * sstride, sc[a]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
-        uint2 res[kStreamAhead];
-  #pragma unroll
-        for (int a = 0; a < kStreamAhead; ++a) {
-          const int i = i0 + a;
-          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) {
-            const float s = e8m0_scale_operand((sc[a][kb] >> (8 * g)) & 0xffu);
-            const uint32_t ww[4] = {w[a][kb].x, w[a][kb].y, w[a][kb].z, w[a][kb].w};
-  #pragma unroll
-            for (int j = 0; j < 4; ++j)
-              acc = mfma16x16x32(decode_fp4x8(ww[j], s), as_bf16x8(xa[kb][j]), acc);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
-  #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-          ld_dwords(sp + ti * sstride, sc[a]);
-          res[a].x = pack_bf16x2(acc[0], acc[1]);
-          res[a].y = pack_bf16x2(acc[2], acc[3]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-  #pragma unroll
-        for (int a = 0; a < kStreamAhead; ++a)
-          bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
-      }
-    };
-    if (counts[e] <= 16) seg(BoolC<true>{}); else seg(BoolC<false>{});
-    t += nt;
-  }
+  gemm2_stream_body<NKB>(act, w2, s2, units, counters, counts, H, I, y);
 }
 
 // ---------------------------------------------------------------------------
@@ -603,11 +510,6 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_stream_kernel(
 // (a K step is 64 bytes).
 // ---------------------------------------------------------------------------
 
-// Token code bytes of one 128-element K step.
-template <bool A4>
-constexpr uint32_t tok_step_bytes() {
-  return A4 ? 64u : 128u;
-}
 
 // acc[t] += W_tile_t * Xq^T over nkb steps. xrs/xoff: buffer and byte offset
 // of the lane's token code row plus 16g (kNoRow past the unit's end);
@@ -861,111 +763,6 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
   }
 }
 
-// GEMM2 split path, W4A8 (or W4A4 with A4), short K (NKB = I/128 <= 4):
-// the balanced stream of gemm2_stream_kernel with the MX act fragments (and
-// their scale bytes) in registers and one scaled MFMA per tile and K step.
-template <int NKB, bool A4>
-__global__ __launch_bounds__(kGemmBlock) void gemm2_stream_a8_kernel(
-    const uint8_t* __restrict__ actq, const uint8_t* __restrict__ acts,
-    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
-    const int32_t* __restrict__ units, const int32_t* __restrict__ counters,
-    const int32_t* __restrict__ counts, int H, int I, uint16_t* __restrict__ y) {
-  if (counters[kCtrGate] != 0) return;  // dense path chosen: zero items here
-  const int lane = lane_id();
-  const int r = lane & 15, g = lane >> 4;
-  const int tpu = H >> 4;
-  const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
-  const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
-  const int64_t wid = xcd_wave_id();
-  int64_t t = total * wid / nwaves;
-  const int64_t t_end = total * (wid + 1) / nwaves;
-  const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
-  const uint32_t tstride = static_cast<uint32_t>(16 * wrow);
-  const uint32_t sstride = static_cast<uint32_t>(16 * srow);
-  while (t < t_end) {
-    const int u = static_cast<int>(t / tpu);
-    const int h0 = static_cast<int>(t - static_cast<int64_t>(u) * tpu);
-    const int nt = static_cast<int>(min(t_end, static_cast<int64_t>(u + 1) * tpu) - t);
-    const int4 ui = reinterpret_cast<const int4*>(units)[u];
-    const int e = ui.x, r0 = ui.y, nrows = ui.z;
-    const size_t row0 = static_cast<size_t>(e) * H + h0 * 16 + r;
-    const uint8_t* wp = w2 + (row0 - r) * wrow + r * 64 + g * 16;  // packed layout
-    const uint8_t* sp = s2 + row0 * srow;
-    constexpr uint32_t XS = tok_step_bytes<A4>();
-    const uint32_t IB = A4 ? static_cast<uint32_t>(I) / 2 : static_cast<uint32_t>(I);
-    const __amdgpu_buffer_rsrc_t qrs =
-        make_rsrc(actq + static_cast<size_t>(r0) * IB, static_cast<uint32_t>(nrows) * IB);
-    const __amdgpu_buffer_rsrc_t ars =
-        make_rsrc(acts + static_cast<size_t>(r0) * srow, static_cast<uint32_t>(nrows * srow));
-    const __amdgpu_buffer_rsrc_t yrs =
-        make_rsrc(y + static_cast<size_t>(r0) * H, static_cast<uint32_t>(nrows) * H * 2);
-    const uint32_t qoff = static_cast<uint32_t>(r) * IB + g * 16;
-    const uint32_t aoff = static_cast<uint32_t>(r * srow) + g;
-    const uint32_t yrow = static_cast<uint32_t>(r) * H * 2 + (h0 * 16 + g * 4) * 2;
-    uint4 xa[NKB][2];
-    uint32_t xsa[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      xa[kb][0] = bld16(qrs, qoff + kb * XS);
-      if (!A4) xa[kb][1] = bld16(qrs, qoff + kb * XS + 64);
-      xsa[kb] = bld1(ars, aoff + kb * 4);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    // weights read once in this call (the expert's only unit): non-temporal
-    auto seg = [&](auto ntw) {
-      constexpr bool NTW = decltype(ntw)::value;
-      uint4 w[kStreamAhead][NKB];
-      uint32_t sc[kStreamAhead][NKB];  // the lane row's I/32 scale bytes
-  #pragma unroll
-      for (int a = 0; a < kStreamAhead; ++a) {
-        const uint32_t ti = static_cast<uint32_t>(min(a, nt - 1));
-  #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-        ld_dwords(sp + ti * sstride, sc[a]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      for (int i0 = 0; i0 < nt; i0 += kStreamAhead) {
-        uint2 res[kStreamAhead];
-  #pragma unroll
-        for (int a = 0; a < kStreamAhead; ++a) {
-          const int i = i0 + a;
-          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb)
-            acc = mfma_f4xa<A4>(w[a][kb], (sc[a][kb] >> (8 * g)) & 0xffu, xa[kb][0], xa[kb][1], xsa[kb],
-                                acc);
-          __builtin_amdgcn_sched_barrier(0);
-          const uint32_t ti = static_cast<uint32_t>(min(i + kStreamAhead, nt - 1));
-  #pragma unroll
-          for (int kb = 0; kb < NKB; ++kb) w[a][kb] = ldw16<NTW>(wp + ti * tstride + kb * kPkBlock);
-          ld_dwords(sp + ti * sstride, sc[a]);
-          res[a].x = pack_bf16x2(acc[0], acc[1]);
-          res[a].y = pack_bf16x2(acc[2], acc[3]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-  #pragma unroll
-        for (int a = 0; a < kStreamAhead; ++a)
-          bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
-      }
-    };
-    if (counts[e] <= 16) seg(BoolC<true>{}); else seg(BoolC<false>{});
-    t += nt;
-  }
-}
-
-// Persistent grid of the streaming GEMM2 kernels: waves split the tile list
-// evenly. One block per CU (one wave per SIMD): on MI355X, 768 blocks (three
-// per CU, the register limit) kept more loads in flight but streamed slower
-// (T64 decode 83.8 -> 80.5 us, Zipf-routed T256 EP decode 31.2 -> 27.6 us
-// with one block per CU). Timestamps taken per wave showed why: of the three
-// blocks sharing a CU the first-dispatched one finished in about 35 us, the
-// second in 57 and the third in 72 (the oldest wave issues first), while
-// the chip's read rate rose from about 6 to 7.3-7.9 TB/s as the number of
-// waves streaming at once fell. 128 or 192 blocks, or a ring of 2, lose.
-#ifndef MOE_STREAM_GRID
-#define MOE_STREAM_GRID 256
-#endif
-
 // Token tiles through LDS (stream_block_lds) pay off once chunks carry
 // several rows: on MI355X they took the T512 E256 H7168 GEMMs from 925 / 518
 // to 692 / 414 us and the Zipf-routed T256 EP decode GEMM1 from 68 to 50 us,
@@ -1014,20 +811,12 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
-  if (a.a8) return launch_gemm2_a8(a, st);
+  if (a.a8) return launch_gemm2_gated_mx(a, st);
+  if (a.I <= kResidentMaxI) return launch_gemm2_gated(a, st);
   const int nkb2 = a.I / 128;
-  if (nkb2 <= 4) {
-    const int gstream = MOE_STREAM_GRID;
-#define MOE_G2S(NK)                                                                      \
-  hipLaunchKernelGGL(gemm2_stream_kernel<NK>, dim3(gstream), dim3(kGemmBlock), 0, st,   \
-                     a.act, a.w2, a.s2, a.units16, a.counters, a.counts, a.H, a.I, a.y)
-    switch (nkb2) {
-      case 1: MOE_G2S(1); break;
-      case 2: MOE_G2S(2); break;
-      case 3: MOE_G2S(3); break;
-      default: MOE_G2S(4); break;
-    }
-#undef MOE_G2S
+  if (nkb2 == 4) {  // I = 512: the stream, then the generic tiled dense kernel
+    hipLaunchKernelGGL(gemm2_stream_kernel<4>, dim3(kStreamGrid), dim3(kGemmBlock), 0, st, a.act,
+                       a.w2, a.s2, a.units16, a.counters, a.counts, a.H, a.I, a.y);
   } else {
     const bool c32 = a.B == 32;
     const int32_t* units = c32 ? a.vinfo : a.units16;
@@ -1079,30 +868,6 @@ static hipError_t launch_gemm1_mx(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st) {
   return a.a4 ? launch_gemm1_mx<true>(a, st) : launch_gemm1_mx<false>(a, st);
-}
-
-template <bool A4>
-static hipError_t launch_gemm2_stream_mx(const GemmArgs& a, hipStream_t st) {
-  const uint8_t* actq = reinterpret_cast<const uint8_t*>(a.act);
-  const int gstream = MOE_STREAM_GRID;
-#define MOE_G2SA(NK)                                                                          \
-  hipLaunchKernelGGL((gemm2_stream_a8_kernel<NK, A4>), dim3(gstream), dim3(kGemmBlock), 0, st, \
-                     actq, a.act_scales, a.w2, a.s2, a.units16, a.counters, a.counts, a.H, a.I, a.y)
-  switch (a.I / 128) {
-    case 1: MOE_G2SA(1); break;
-    case 2: MOE_G2SA(2); break;
-    case 3: MOE_G2SA(3); break;
-    default: MOE_G2SA(4); break;
-  }
-#undef MOE_G2SA
-  return hipGetLastError();
-}
-
-hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st) {
-  const hipError_t err =
-      a.a4 ? launch_gemm2_stream_mx<true>(a, st) : launch_gemm2_stream_mx<false>(a, st);
-  if (err != hipSuccess) return err;
-  return launch_gemm2_dense_tiled_a8(a, st);
 }
 
 }  // namespace moe

@@ -30,6 +30,7 @@
 // expert's weights run together on one XCD and meet in its L2.
 #include "common.h"
 #include "kernels.h"
+#include "gemm2_stream.h"
 
 namespace moe {
 
@@ -491,7 +492,7 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 constexpr int kResThreads = 256;
 
 template <int NKB>
-__global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
+__device__ __forceinline__ void gemm2_resident_body(
     const uint16_t* __restrict__ act, uint32_t act_bytes, const uint8_t* __restrict__ w2,
     const uint8_t* __restrict__ s2, const int32_t* __restrict__ tiles,
     const int32_t* __restrict__ counters, int H, uint16_t* __restrict__ y) {
@@ -686,8 +687,40 @@ __global__ __launch_bounds__(kResThreads, 1) void gemm2_resident_kernel(
   }
 }
 
-// Persistent grid: `per_cu` blocks per CU (LDS and registers allow two for
-// the bf16 kernel, one for the W4A8 kernel), at most one block per item; a
+// GEMM2 of either path in one launch, for I <= 384 ("Device-side gating of
+// the MoE GEMM2 path": the gate word picks Dense or Split on the device and
+// the launch chain stays fixed). The stream kernel and the resident dense
+// kernel both run one 4-wave block per CU (the stream by choice, the dense
+// kernel by its LDS and registers), so one persistent grid of kStreamGrid
+// blocks serves either body, and the path not taken costs no launch of its
+// own (about 4 us per layer at decode shapes on MI355X).
+template <int NKB>
+__global__ __launch_bounds__(kResThreads, 1) void gemm2_gated_kernel(
+    const uint16_t* __restrict__ act, uint32_t act_bytes, const uint8_t* __restrict__ w2,
+    const uint8_t* __restrict__ s2, const int32_t* __restrict__ units,
+    const int32_t* __restrict__ dense_tiles, const int32_t* __restrict__ counters,
+    const int32_t* __restrict__ counts, int H, uint16_t* __restrict__ y) {
+  if (counters[kCtrGate] == 1)
+    gemm2_resident_body<NKB>(act, act_bytes, w2, s2, dense_tiles, counters, H, y);
+  else
+    gemm2_stream_body<NKB>(act, w2, s2, units, counters, counts, H, NKB * 128, y);
+}
+
+hipError_t launch_gemm2_gated(const GemmArgs& a, hipStream_t st) {
+  const uint32_t act_bytes = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2);
+#define MOE_G2G(NK)                                                                             \
+  hipLaunchKernelGGL(gemm2_gated_kernel<NK>, dim3(kStreamGrid), dim3(kResThreads), 0, st, a.act, \
+                     act_bytes, a.w2, a.s2, a.units16, a.dense_tiles, a.counters, a.counts, a.H, a.y)
+  switch (a.I / 128) {
+    case 1: MOE_G2G(1); break;
+    case 2: MOE_G2G(2); break;
+    default: MOE_G2G(3); break;
+  }
+#undef MOE_G2G
+  return hipGetLastError();
+}
+
+// Persistent grid: `per_cu` blocks per CU, at most one block per item; a
 // multiple of 8 so that every XCD gets the same number of blocks.
 static int tiled_grid(long items, int per_cu) {
   long per = (items + 7) / 8;
@@ -713,21 +746,10 @@ hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Dense GEMM2 for I > 384 (the act tile no longer fits in LDS next to the
+// output staging): the generic tiled kernel, launched after the split-path
+// kernel of the same chain.
 hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st) {
-  if (a.I <= 384) {  // act tile (128 x I bf16) and the weight registers fit
-    const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles), 1);
-    const uint32_t act_bytes = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2);
-#define MOE_G2R(NK)                                                                        \
-  hipLaunchKernelGGL(gemm2_resident_kernel<NK>, dim3(grid), dim3(kResThreads), 0, st,     \
-                     a.act, act_bytes, a.w2, a.s2, a.dense_tiles, a.counters, a.H, a.y)
-    switch (a.I / 128) {
-      case 1: MOE_G2R(1); break;
-      case 2: MOE_G2R(2); break;
-      default: MOE_G2R(3); break;
-    }
-#undef MOE_G2R
-    return hipGetLastError();
-  }
   const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles) * (a.H / 256), 1);
   hipLaunchKernelGGL((gemm_tiled_kernel<false, 2>), dim3(grid), dim3(kTiledThreads), 0, st, a.act,
                      static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I * 2), a.w2, a.s2,
@@ -1034,7 +1056,7 @@ hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
 
 // ---------------------------------------------------------------------------
 // Dense GEMM2 of the W4A8 path, act tile resident in LDS (I <= 512): the
-// structure of gemm2_resident_kernel with the scaled 16x16x128 MFMA. A block
+// structure of gemm2_resident_body with the scaled 16x16x128 MFMA. A block
 // (4 waves) owns a 128-row dense tile: its MXFP8 act rows (128 x I E4M3
 // bytes) and their scales go to LDS once, then it walks all H / 256 output
 // spans. Wave wn takes 64 W2 rows per span as four 16-row tiles against the
@@ -1045,7 +1067,7 @@ hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st) {
 // kernel's. LDS: 128 * I * 33 / 32 + 64 KB.
 // ---------------------------------------------------------------------------
 template <int NKB, bool A4>
-__global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
+__device__ __forceinline__ void gemm2_resident_a8_body(
     const uint8_t* __restrict__ actq, uint32_t actq_bytes, const uint8_t* __restrict__ acts,
     uint32_t acts_bytes, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
     const int32_t* __restrict__ tiles, const int32_t* __restrict__ counters, int H,
@@ -1204,28 +1226,44 @@ __global__ __launch_bounds__(256, 1) void gemm2_resident_a8_kernel(
   }
 }
 
+// GEMM2 of either path in one launch for MX act (I <= 512), as
+// gemm2_gated_kernel does for bf16.
+template <int NKB, bool A4>
+__global__ __launch_bounds__(256, 1) void gemm2_gated_mx_kernel(
+    const uint8_t* __restrict__ actq, uint32_t actq_bytes, const uint8_t* __restrict__ acts,
+    uint32_t acts_bytes, const uint8_t* __restrict__ w2, const uint8_t* __restrict__ s2,
+    const int32_t* __restrict__ units, const int32_t* __restrict__ dense_tiles,
+    const int32_t* __restrict__ counters, const int32_t* __restrict__ counts, int H,
+    uint16_t* __restrict__ y) {
+  if (counters[kCtrGate] == 1)
+    gemm2_resident_a8_body<NKB, A4>(actq, actq_bytes, acts, acts_bytes, w2, s2, dense_tiles, counters,
+                                    H, y);
+  else
+    gemm2_stream_mx_body<NKB, A4>(actq, acts, w2, s2, units, counters, counts, H, NKB * 128, y);
+}
+
 template <bool A4>
-static hipError_t launch_gemm2_resident_mx(const GemmArgs& a, hipStream_t st) {
+static hipError_t launch_gemm2_gated_mx_t(const GemmArgs& a, hipStream_t st) {
   // the MX paths admit I <= 512 only, so the act tile always fits in LDS
-  const int grid = tiled_grid(static_cast<long>(a.dense_grid_tiles), 1);
   const uint8_t* actq = reinterpret_cast<const uint8_t*>(a.act);
   const uint32_t qb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / (A4 ? 2 : 1));
   const uint32_t sb = static_cast<uint32_t>(static_cast<size_t>(a.rows_pad) * a.I / 32);
-#define MOE_G2RA(NK)                                                                           \
-  hipLaunchKernelGGL((gemm2_resident_a8_kernel<NK, A4>), dim3(grid), dim3(256), 0, st, actq, qb, \
-                     a.act_scales, sb, a.w2, a.s2, a.dense_tiles, a.counters, a.H, a.y)
+#define MOE_G2GA(NK)                                                                              \
+  hipLaunchKernelGGL((gemm2_gated_mx_kernel<NK, A4>), dim3(kStreamGrid), dim3(256), 0, st, actq, qb, \
+                     a.act_scales, sb, a.w2, a.s2, a.units16, a.dense_tiles, a.counters, a.counts,  \
+                     a.H, a.y)
   switch (a.I / 128) {
-    case 1: MOE_G2RA(1); break;
-    case 2: MOE_G2RA(2); break;
-    case 3: MOE_G2RA(3); break;
-    default: MOE_G2RA(4); break;
+    case 1: MOE_G2GA(1); break;
+    case 2: MOE_G2GA(2); break;
+    case 3: MOE_G2GA(3); break;
+    default: MOE_G2GA(4); break;
   }
-#undef MOE_G2RA
+#undef MOE_G2GA
   return hipGetLastError();
 }
 
-hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st) {
-  return a.a4 ? launch_gemm2_resident_mx<true>(a, st) : launch_gemm2_resident_mx<false>(a, st);
+hipError_t launch_gemm2_gated_mx(const GemmArgs& a, hipStream_t st) {
+  return a.a4 ? launch_gemm2_gated_mx_t<true>(a, st) : launch_gemm2_gated_mx_t<false>(a, st);
 }
 
 }  // namespace moe

@@ -64,20 +64,22 @@ struct GemmArgs {
 hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st);  // split + dense, gated on device
 // LDS-tiled kernels for many rows per expert (gemm_tiled.hip): GEMM1 over the
-// chunk table (B >= 64), and the dense GEMM2 path over the dense tiles.
+// chunk table (B >= 64); GEMM2 of both paths in one gated launch (bf16 act
+// with I <= kResidentMaxI, or MX act); the generic dense GEMM2 over the dense
+// tiles for bf16 act with larger I.
 hipError_t launch_gemm1_tiled(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm2_gated(const GemmArgs& a, hipStream_t st);
+hipError_t launch_gemm2_gated_mx(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm2_dense_tiled(const GemmArgs& a, hipStream_t st);
 
 // x -> MXFP8 (W4A8 path: xq [T, H] E4M3 codes) or MXFP4 (a4, W4A4 path:
 // xq [T, H/2] E2M1 code pairs), xs [T, H/32] E8M0 scales.
 hipError_t launch_quant_x(const uint16_t* x, int T, int H, uint8_t* xq, uint8_t* xs, bool a4,
                           hipStream_t st);
-// MX-activation kernels, W4A8 or W4A4 by a4 (the launchers above dispatch to
+// MX-activation GEMM1 kernels, W4A8 or W4A4 by a4 (launch_gemm1 dispatches to
 // them when a8 is set).
 hipError_t launch_gemm1_a8(const GemmArgs& a, hipStream_t st);
-hipError_t launch_gemm2_a8(const GemmArgs& a, hipStream_t st);
 hipError_t launch_gemm1_tiled_a8(const GemmArgs& a, hipStream_t st);
-hipError_t launch_gemm2_dense_tiled_a8(const GemmArgs& a, hipStream_t st);
 
 struct FinalizeArgs {
   const uint16_t* y;
