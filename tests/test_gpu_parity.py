@@ -60,6 +60,11 @@ SMALL = [
     LayerShape("prefill_i384_b256", T=2048, E=12, E_g=12, topk=4, H=1024, I=384, B=256, S=1,
                swiglu_limit=6.0),
     LayerShape("prefill_i768_b128", T=1536, E=10, E_g=10, topk=4, H=512, I=768, B=128),
+    # I = 512: the longest K of the split stream (four steps in registers),
+    # with bf16 act outside the one-launch gated GEMM2 (the stream kernel,
+    # then the generic tiled dense kernel); decode and 256-row-tile prefill
+    LayerShape("i512_decode", T=48, E=16, E_g=16, topk=4, H=512, I=512, B=32),
+    LayerShape("i512_prefill_b128", T=1024, E=8, E_g=8, topk=2, H=512, I=512, B=128),
 ]
 
 
@@ -177,6 +182,11 @@ SMALL_A8 = [
                a_dtype="mxfp8"),
     LayerShape("a8_prefill_i384_b256", T=2048, E=12, E_g=12, topk=4, H=1024, I=384, B=256, S=1,
                swiglu_limit=6.0, a_dtype="mxfp8"),
+    # I = 512, the largest the MX paths take: four K steps in the gated
+    # GEMM2's stream and resident bodies, decode and tiled GEMM1
+    LayerShape("a8_i512_decode", T=48, E=16, E_g=16, topk=4, H=512, I=512, B=32, a_dtype="mxfp8"),
+    LayerShape("a8_i512_prefill_b128", T=1024, E=8, E_g=8, topk=2, H=512, I=512, B=128,
+               a_dtype="mxfp8"),
 ]
 
 
