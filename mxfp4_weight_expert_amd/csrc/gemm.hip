@@ -72,11 +72,61 @@ __device__ __forceinline__ XcdItems xcd_items(int nitems) {
 // use buffer loads whose out-of-range offset (lanes past the chunk's last
 // row) returns zero without touching memory.
 // ---------------------------------------------------------------------------
-// Copy `bytes` (a multiple of 16) from global to this wave's LDS block.
-__device__ __forceinline__ void wave_copy_to_lds(uint8_t* lds, const uint8_t* src, int bytes) {
-  for (int off = lane_id() * 16; off < bytes; off += kWave * 16)
-    *reinterpret_cast<uint4*>(lds + off) = ld16(src + off);
+// Copy N blocks of `bytes` each (a multiple of 16, at most MAXB * 4 KB) from
+// global memory to this wave's LDS. The loads of a batch (four 1 KB pieces
+// per block) all go out before its first store, so a batch costs one memory
+// round trip; a load-then-store loop waited for every piece in turn, about
+// eight dependent round trips for the two 3.5 KB scale blocks of a decode
+// GEMM1 item at H = 3584. Straight-line code (batches behind wave-uniform
+// guards, no per-lane branch): lanes past the end load and store the
+// block's last 16 bytes again, the same data at the same place.
+// LDS bytes reserved for a copied block: a direct-to-LDS load instruction
+// writes a whole 1 KB (16 bytes per lane, lane order).
+__host__ __device__ constexpr int lds_block_bytes(int bytes) { return (bytes + 1023) & ~1023; }
+
+// Copy N blocks of `bytes` each (a multiple of 16, at most MAXP KB) from
+// global memory straight into this wave's LDS with 16-byte direct-to-LDS
+// buffer loads: no data registers, every piece in flight at once, so the copy
+// costs one memory round trip and is waited for like any other load. A
+// load-then-store loop waited for every 1 KB piece in turn, about eight
+// dependent round trips for the two 3.5 KB scale blocks of a decode GEMM1
+// item at H = 3584. Piece i of block b comes through a buffer of its own
+// (base + 1024 i, the bytes left), so a lane past the block's end is out of
+// range and reads nothing; it lands in the padding of the block's LDS
+// region, lds_block_bytes(bytes) long. Lane l's 16 bytes go to
+// lds[b] + 1024 i + 16 l.
+template <int N, int MAXP>
+__device__ __forceinline__ void wave_copy_to_lds(uint8_t* const (&lds)[N],
+                                                 const uint8_t* const (&src)[N], int bytes) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const uint32_t l16 = static_cast<uint32_t>(lane_id()) * 16;
+#pragma unroll
+  for (int i = 0; i < MAXP; ++i) {
+    if (i == 0 || i * 1024 < bytes) {  // wave-uniform
+#pragma unroll
+      for (int b = 0; b < N; ++b) {
+        const __amdgpu_buffer_rsrc_t r =
+            make_rsrc(src[b] + i * 1024, static_cast<uint32_t>(bytes - i * 1024));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds[b] + i * 1024), 16, l16, 0, 0, 0);
+      }
+    }
+  }
 }
+// Wait until every load this wave issued has completed, direct-to-LDS loads
+// included (s_waitcnt vmcnt(0); the other counters are left alone). The
+// compiler does not order reads of LDS after direct-to-LDS buffer loads, so
+// the streams below call this after their first ring loads, before their
+// first read of the scale rows wave_copy_to_lds brought in: on MI355X,
+// reads issued ahead of the copy returned the previous item's scales now
+// and then (run-to-run differences at H = 512, I = 640).
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Pieces the callers allow for (the shape check caps H and I at kMaxTiledK):
+// GEMM1 scale blocks of 16 * TP rows x H / 32 bytes (TP <= 2) and the MX
+// GEMM1's 32 rows, at most 8 KB; the split GEMM2's 64 rows x I / 32 bytes,
+// at most 16 KB.
+static_assert(16 * 2 * (kMaxTiledK / 32) <= 8 * 1024, "GEMM1 scale blocks exceed 8 pieces");
+static_assert(64 * (kMaxTiledK / 32) <= 16 * 1024, "split GEMM2 scale blocks exceed 16 pieces");
 
 // acc[s][t] += W_tile_t (16 x K) * B_s^T for NS sub-tiles of 16 token rows.
 // wp: lane's weight-row pointer of tile 0, offset by g*16 bytes; tile t is
@@ -105,6 +155,8 @@ __device__ __forceinline__ void stream_block(const uint8_t* wp, const uint32_t (
     for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
+  wait_all_loads();  // the item's scale rows are in LDS
+  __builtin_amdgcn_sched_barrier(0);
   const int last = nkb - 1;
   // One ring step: multiply slot d (step kb), then refill it with step
   // kb + D (near the end the last step again; those loads are never used).
@@ -190,6 +242,8 @@ __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32
     for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
+  wait_all_loads();  // the item's scale rows are in LDS
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < NS; ++i) *reinterpret_cast<uint4*>(tl + tlds_off(lr + 16 * i, lc)) = tv[0][i];
   __syncthreads();
@@ -274,8 +328,9 @@ __device__ __forceinline__ void gemm1_decode_items(
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
   const int nkb = H >> 7;
   const int blk = 16 * TP * static_cast<int>(srow);  // the group's gate (or up) scale rows
+  const int blkp = lds_block_bytes(blk);
   uint8_t* tl = lds_scales;
-  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<NSMAX>() : 0) + wave_index() * 2 * blk;
+  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<NSMAX>() : 0) + wave_index() * 2 * blkp;
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(T) * H * 2));
   const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
   uint32_t wofs[NT], lofs[NT];
@@ -284,7 +339,7 @@ __device__ __forceinline__ void gemm1_decode_items(
     wofs[2 * p] = static_cast<uint32_t>(16 * p * wrow);
     wofs[2 * p + 1] = static_cast<uint32_t>((I + 16 * p) * wrow);
     lofs[2 * p] = static_cast<uint32_t>(16 * p * srow);
-    lofs[2 * p + 1] = static_cast<uint32_t>(blk + 16 * p * srow);
+    lofs[2 * p + 1] = static_cast<uint32_t>(blkp + 16 * p * srow);
   }
   const XcdItems xi = xcd_items(nitems);
   for (int item = xi.first; item < xi.end; item += xi.step) {
@@ -294,24 +349,34 @@ __device__ __forceinline__ void gemm1_decode_items(
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * 2 * I + f0;
     const uint8_t* sg = s13 + row0 * srow;
-    wave_copy_to_lds(my, sg, blk);
-    wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
+    // the chunk's slot numbers (clamped, unconditional loads) go out with the
+    // scale-row loads: the item setup waits one round trip for both
+    int slot_w[NSMAX], slot_t[NSMAX];
+#pragma unroll
+    for (int s = 0; s < NSMAX; ++s) slot_w[s] = sorted_slot[r0 + min(16 * s + r, nrows - 1)];
+    if (TL) {
+#pragma unroll
+      for (int i = 0; i < NSMAX; ++i) slot_t[i] = sorted_slot[r0 + min(lr + 16 * i, nrows - 1)];
+    }
+    {
+      uint8_t* const dst[2] = {my, my + blkp};
+      const uint8_t* const src[2] = {sg, sg + static_cast<size_t>(I) * srow};
+      wave_copy_to_lds<2, 8>(dst, src, blk);
+    }
     const uint8_t* wp = w13 + row0 * wrow + r * 64 + g * 16;  // packed layout
     const bool once = counts[e] <= 16 * NSMAX;  // the expert's only chunk
     uint32_t boff[NSMAX];
 #pragma unroll
     for (int s = 0; s < NSMAX; ++s) {
       const int rr = 16 * s + r;
-      const int tok = sorted_slot[r0 + min(rr, nrows - 1)] / Kp;
-      boff[s] = rr < nrows ? static_cast<uint32_t>(tok) * H * 2 + g * 64 : kNoRow;
+      boff[s] = rr < nrows ? static_cast<uint32_t>(slot_w[s] / Kp) * H * 2 + g * 64 : kNoRow;
     }
     uint32_t toff[NSMAX];  // this thread's rows of the block's token tile
     if (TL) {
 #pragma unroll
       for (int i = 0; i < NSMAX; ++i) {
         const int rr = lr + 16 * i;
-        const int tok = sorted_slot[r0 + min(rr, nrows - 1)] / Kp;
-        toff[i] = rr < nrows ? static_cast<uint32_t>(tok) * H * 2 + lc * 16 : kNoRow;
+        toff[i] = rr < nrows ? static_cast<uint32_t>(slot_t[i] / Kp) * H * 2 + lc * 16 : kNoRow;
       }
     }
     // rows past the chunk's end fall outside the buffer: stores dropped
@@ -411,7 +476,7 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
   const int nkb = I >> 7;
   const int blk = 64 * static_cast<int>(srow);  // = 2I bytes
   uint8_t* tl = lds_scales;
-  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<NSMAX>() : 0) + wave_index() * blk;
+  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<NSMAX>() : 0) + wave_index() * lds_block_bytes(blk);
   const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
   const uint32_t wofs[4] = {0u, static_cast<uint32_t>(16 * wrow), static_cast<uint32_t>(32 * wrow),
                             static_cast<uint32_t>(48 * wrow)};
@@ -424,7 +489,11 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * H + h0;
-    wave_copy_to_lds(my, s2 + row0 * srow, blk);
+    {
+      uint8_t* const dst[1] = {my};
+      const uint8_t* const src[1] = {s2 + row0 * srow};
+      wave_copy_to_lds<1, 16>(dst, src, blk);
+    }
     const uint8_t* wp = w2 + row0 * wrow + r * 64 + g * 16;  // packed layout
     const bool once = counts[e] <= 16 * NSMAX;  // the expert's only chunk
     // chunk-relative buffers: rows past the chunk's end read 0 / drop stores
@@ -532,6 +601,8 @@ __device__ __forceinline__ void stream_block_a8(const uint8_t* wp, const uint32_
     for (int t = 0; t < 4; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
+  wait_all_loads();  // the item's scale rows are in LDS
+  __builtin_amdgcn_sched_barrier(0);
   const int last = nkb - 1;
   auto step = [&](int kb, int d) {
 #pragma unroll
@@ -617,6 +688,8 @@ __device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uin
     for (int q = 0; q < 4; ++q) w[d][q] = ldw16<NTW>(wp + wofs[q] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
   }
+  wait_all_loads();  // the item's scale rows are in LDS
+  __builtin_amdgcn_sched_barrier(0);
   put(tl, 0);
   __syncthreads();
   const int last = nkb - 1;
@@ -695,16 +768,17 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
   const int nkb = H >> 7;
   const int blk = 32 * static_cast<int>(srow);
-  uint8_t* my = lds_scales + wave_index() * 2 * blk;
+  const int blkp = lds_block_bytes(blk);
+  uint8_t* my = lds_scales + wave_index() * 2 * blkp;
   const uint32_t HB = A4 ? static_cast<uint32_t>(H) / 2 : static_cast<uint32_t>(H);  // x row bytes
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(xq, static_cast<uint32_t>(static_cast<size_t>(T) * HB));
   const __amdgpu_buffer_rsrc_t srs = make_rsrc(xs, static_cast<uint32_t>(static_cast<size_t>(T) * srow));
   const uint32_t wofs[4] = {0u, static_cast<uint32_t>(I * wrow), static_cast<uint32_t>(16 * wrow),
                             static_cast<uint32_t>((I + 16) * wrow)};
-  const uint32_t lofs[4] = {0u, static_cast<uint32_t>(blk), static_cast<uint32_t>(16 * srow),
-                            static_cast<uint32_t>(blk + 16 * srow)};
+  const uint32_t lofs[4] = {0u, static_cast<uint32_t>(blkp), static_cast<uint32_t>(16 * srow),
+                            static_cast<uint32_t>(blkp + 16 * srow)};
   const uint32_t srow_a = static_cast<uint32_t>(I) >> 5;
-  uint8_t* tl = lds_scales + 4 * 2 * blk;
+  uint8_t* tl = lds_scales + 4 * 2 * blkp;
   const int tt = static_cast<int>(threadIdx.x);
   const XcdItems xi = xcd_items(nitems);
   for (int item = xi.first; item < xi.end; item += xi.step) {
@@ -714,11 +788,21 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * 2 * I + f0;
     const uint8_t* sg = s13 + row0 * srow;
-    wave_copy_to_lds(my, sg, blk);
-    wave_copy_to_lds(my + blk, sg + static_cast<size_t>(I) * srow, blk);
+    // the slot numbers go out with the scale-row loads (one round trip): the
+    // lane's row, and the thread's row of the block's token tile (TL: codes
+    // for t < NC, scales for the next 16 threads)
+    const int slot = sorted_slot[r0 + min(r, nrows - 1)];
+    constexpr int NC = tok_mx_code_threads<A4>();
+    const int rr_t = tt < NC ? (A4 ? tt >> 2 : tt >> 3) : tt - NC;
+    const int slot_t = TL ? sorted_slot[r0 + min(rr_t, nrows - 1)] : 0;
+    {
+      uint8_t* const dst[2] = {my, my + blkp};
+      const uint8_t* const src[2] = {sg, sg + static_cast<size_t>(I) * srow};
+      wave_copy_to_lds<2, 8>(dst, src, blk);
+    }
     const uint8_t* wp = w13 + row0 * wrow + r * 64 + g * 16;  // packed layout
     const bool valid = r < nrows;
-    const uint32_t tok = static_cast<uint32_t>(sorted_slot[r0 + min(r, nrows - 1)] / Kp);
+    const uint32_t tok = static_cast<uint32_t>(slot / Kp);
     const uint32_t xoff = valid ? tok * HB + g * 16 : kNoRow;
     const uint32_t soff = valid ? tok * static_cast<uint32_t>(srow) + g : kNoRow;
     f32x4_t acc[4];
@@ -727,10 +811,8 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     auto run = [&](auto ntw) {
       if constexpr (TL) {
         // this thread's row of the block's token tile: codes (t < NC) or scales
-        constexpr int NC = tok_mx_code_threads<A4>();
-        const int rr = tt < NC ? (A4 ? tt >> 2 : tt >> 3) : tt - NC;
-        const uint32_t ttok = static_cast<uint32_t>(sorted_slot[r0 + min(rr, nrows - 1)] / Kp);
-        const bool tv_ok = rr < nrows;
+        const uint32_t ttok = static_cast<uint32_t>(slot_t / Kp);
+        const bool tv_ok = rr_t < nrows;
         const uint32_t toff =
             tt < NC && tv_ok ? ttok * HB + (A4 ? (tt & 3) : (tt & 7)) * 16 : kNoRow;
         const uint32_t tsoff =
@@ -793,8 +875,10 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
     const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / 16));
     const int d = ring_depth(a.H / 128);
     const bool tl = token_tiles_in_lds(a, d);
-    const size_t lds =
-        static_cast<size_t>(4) * 2 * a.H + (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
+    // per wave: the gate and up scale blocks of a 32-feature item (H bytes
+    // each; a 16-feature item's half-size blocks fit in the same space)
+    const size_t lds = static_cast<size_t>(4) * 2 * lds_block_bytes(a.H) +
+                       (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
 #define MOE_G1D(DD, NS, TL)                                                                       \
   hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, TL>), dim3(grid), dim3(kGemmBlock), lds, st,      \
                      a.x, a.w13, a.s13, units, ctr, a.counters, a.counts, a.sorted_slot, a.T, a.H,   \
@@ -824,8 +908,8 @@ hipError_t launch_gemm2(const GemmArgs& a, hipStream_t st) {
     const int gsplit = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.H / 64));
     const int d = ring_depth(a.I / 128);
     const bool tl = token_tiles_in_lds(a, d);
-    const size_t lds2 =
-        static_cast<size_t>(4) * 2 * a.I + (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
+    const size_t lds2 = static_cast<size_t>(4) * lds_block_bytes(2 * a.I) +
+                        (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
 #define MOE_G2D(DD, NS, TL)                                                                     \
   hipLaunchKernelGGL((gemm2_split_kernel<DD, NS, TL>), dim3(gsplit), dim3(kGemmBlock), lds2, st, \
                      a.act, a.w2, a.s2, units, ctr, a.counters, a.counts, a.H, a.I, a.y)
@@ -846,7 +930,8 @@ static hipError_t launch_gemm1_mx(const GemmArgs& a, hipStream_t st) {
   const int grid = grid_for(static_cast<long>(a.max_units16) * (a.I / 32));
   const int ring = ring_depth(a.H / 128) >= 2 ? 2 : 1;
   const bool tl = token_tiles_in_lds(a, ring);
-  const size_t lds = static_cast<size_t>(4) * 2 * a.H + (tl ? 2 * tok_mx_lds_step<A4>() : 0);
+  const size_t lds =
+      static_cast<size_t>(4) * 2 * lds_block_bytes(a.H) + (tl ? 2 * tok_mx_lds_step<A4>() : 0);
   uint8_t* actq = reinterpret_cast<uint8_t*>(a.act);
 #define MOE_G1A(DD, TL)                                                                          \
   hipLaunchKernelGGL((gemm1_decode_a8_kernel<DD, TL, A4>), dim3(grid), dim3(kGemmBlock), lds, st, \
