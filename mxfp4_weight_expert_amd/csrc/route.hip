@@ -58,19 +58,32 @@ __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) { return a <
 // One wave per token. The token's logits become 64-bit keys (ordered logit
 // << 32 | ~id), NPL per lane (E_global <= 64 * NPL); larger key = larger
 // logit, equal logits: lower id. A NaN's key is ~id alone: above the empty
-// key 0 and below every number's. Every lane keeps its four largest keys
-// below a ceiling, sorted. Each of topk rounds finds the wave's largest head
-// key (a 32-bit DPP maximum over the ordered logits, and over the ids only
-// when several lanes tie) and pops it from its lane; a lane whose list runs
-// empty rebuilds it from its keys below the key it gave last. Keys come out
-// in descending order.
+// key 0 and below every number's. The top-k keys are found in three passes
+// over registers and a little LDS:
+//  1. thr: the largest 32-bit ordered logit that at least topk lane maxima
+//     reach (radix select, most significant bit first, one ballot per bit).
+//     At least topk keys have a logit >= thr, so every top-k key does;
+//  2. the candidates (non-empty keys with logit >= thr; typically topk plus
+//     a few) are packed into the wave's LDS row in ballot order;
+//  3. each candidate's rank is the number of larger candidates (all 64 bits:
+//     ties of equal logits rank by id), and the key of rank r goes to lane r.
+// About 400 instructions per token against about 1,300 for topk rounds of a
+// wave-wide maximum. More than 64 candidates (many logits equal at the
+// threshold, or mostly NaN rows) take the round-based selection: every lane
+// keeps its four largest keys below a ceiling, sorted; each of topk rounds
+// finds the wave's largest head key (a 32-bit DPP maximum over the ordered
+// logits, and over the ids only when several lanes tie) and pops it from its
+// lane; a lane whose list runs empty rebuilds it from its keys below the key
+// it gave last. Either way lane r ends with the r-th largest key.
 template <int NPL>
 __global__ __launch_bounds__(256) void route_logits_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ shared_logits, int T, int Eg,
     int topk, int S, int E, int expert_offset, float shared_scale, int32_t* __restrict__ route_ids,
     int32_t* __restrict__ slot_expert, float* __restrict__ slot_w) {
+  __shared__ uint64_t s_key[4][kWave];  // per wave: the candidates, then the selection
   const int lane = lane_id();
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int wv = static_cast<int>(threadIdx.x) >> 6;
+  const int t = blockIdx.x * 4 + wv;
   if (t >= T) return;
   const float* row = logits + static_cast<size_t>(t) * Eg;
   // Unconditional loads (clamped index) so all of them are in flight at once.
@@ -84,43 +97,86 @@ __global__ __launch_bounds__(256) void route_logits_kernel(
     const uint64_t k = (static_cast<uint64_t>(order_bits(lv[j])) << 32) | static_cast<uint32_t>(~idx);
     key[j] = idx < Eg ? k : 0ull;  // 0 is below every real key
   }
-  // the lane's four largest keys below `ceil`, descending (0 = none)
-  uint64_t L[4];
-  auto build = [&](uint64_t ceil) {
+  // 1. the threshold logit
+  uint64_t lmax = 0ull;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) L[i] = 0ull;
+  for (int j = 0; j < NPL; ++j) lmax = max_u64(lmax, key[j]);
+  const uint32_t lhi = static_cast<uint32_t>(lmax >> 32);
+  uint32_t thr = 0u;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = thr | (1u << b);
+    if (__popcll(ballot(lhi >= c)) >= topk) thr = c;
+  }
+  // 2. the candidates
+  uint64_t bal[NPL];
+  int ncand = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    bal[j] = ballot(key[j] != 0ull && static_cast<uint32_t>(key[j] >> 32) >= thr);
+    ncand += __popcll(bal[j]);
+  }
+  uint64_t mine = 0;  // lane r keeps the r-th selected key
+  if (ncand <= kWave) {
+    const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    uint64_t* row_lds = s_key[wv];
+    int base = 0;
 #pragma unroll
     for (int j = 0; j < NPL; ++j) {
-      uint64_t x = key[j] < ceil ? key[j] : 0ull;
+      if ((bal[j] >> lane) & 1ull) row_lds[base + __popcll(bal[j] & lt)] = key[j];
+      base += __popcll(bal[j]);
+    }
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t ck = lane < ncand ? row_lds[lane] : 0ull;
+    // 3. ranks (candidate keys are distinct: the ids differ)
+    int rank = 0;
+    for (int i = 0; i < ncand; ++i) {
+      const uint64_t ki =
+          (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ck >> 32), i))) << 32) |
+          static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(ck), i));
+      rank += ki > ck ? 1 : 0;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (lane < ncand && rank < topk) row_lds[rank] = ck;
+    __builtin_amdgcn_wave_barrier();
+    mine = lane < topk ? row_lds[lane] : 0ull;
+  } else {
+    // the lane's four largest keys below `ceil`, descending (0 = none)
+    uint64_t L[4];
+    auto build = [&](uint64_t ceil) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint64_t hi = max_u64(L[i], x);
-        x = min_u64(L[i], x);
-        L[i] = hi;
+      for (int i = 0; i < 4; ++i) L[i] = 0ull;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        uint64_t x = key[j] < ceil ? key[j] : 0ull;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint64_t hi = max_u64(L[i], x);
+          x = min_u64(L[i], x);
+          L[i] = hi;
+        }
       }
-    }
-  };
-  build(~0ull);
-  uint64_t mine = 0;  // lane r keeps the r-th selected key
-  for (int r = 0; r < topk; ++r) {
-    const uint32_t h0 = static_cast<uint32_t>(L[0] >> 32), l0 = static_cast<uint32_t>(L[0]);
-    const uint32_t mh = wave_max_u32(h0);
-    const bool cand = h0 == mh;
-    const uint64_t bal = ballot(cand);
-    uint32_t ml;
-    if (__popcll(bal) == 1) {
-      ml = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(l0), __builtin_ctzll(bal)));
-    } else {
-      ml = wave_max_u32(cand ? l0 : 0u);
-    }
-    const uint64_t m = (static_cast<uint64_t>(mh) << 32) | ml;
-    if (lane == r) mine = m;
-    if (L[0] == m) {  // the one lane holding the winner (keys are distinct)
-      L[0] = L[1];
-      L[1] = L[2];
-      L[2] = L[3];
-      L[3] = 0ull;
-      if (L[0] == 0ull) build(m);
+    };
+    build(~0ull);
+    for (int r = 0; r < topk; ++r) {
+      const uint32_t h0 = static_cast<uint32_t>(L[0] >> 32), l0 = static_cast<uint32_t>(L[0]);
+      const uint32_t mh = wave_max_u32(h0);
+      const bool cand = h0 == mh;
+      const uint64_t bl = ballot(cand);
+      uint32_t ml;
+      if (__popcll(bl) == 1) {
+        ml = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(l0), __builtin_ctzll(bl)));
+      } else {
+        ml = wave_max_u32(cand ? l0 : 0u);
+      }
+      const uint64_t m = (static_cast<uint64_t>(mh) << 32) | ml;
+      if (lane == r) mine = m;
+      if (L[0] == m) {  // the one lane holding the winner (keys are distinct)
+        L[0] = L[1];
+        L[1] = L[2];
+        L[2] = L[3];
+        L[3] = 0ull;
+        if (L[0] == 0ull) build(m);
+      }
     }
   }
   const bool sel = lane < topk;

@@ -335,6 +335,36 @@ def test_routing_ties_and_signed_zeros(E_g, topk):
     check_maps(s, maps_np(s, ws), ref)
 
 
+@pytest.mark.parametrize("E_g,topk", [(8, 2), (130, 5), (896, 16), (2048, 32)])
+def test_routing_threshold_ties(E_g, topk):
+    """Ties among few candidates: a group of equal logits straddles the top-k
+    boundary while the rest of the row stays distinct (the selection ranks
+    the keys at or above a threshold, ties by lower id); groups spread over
+    ids that fall in different lanes and lane slots; a group tied with the
+    row's own maximum; signed zeros as the top values; rows where many keys
+    tie at the threshold (the round-based selection)."""
+    s = LayerShape(f"thr_ties_{E_g}", T=64, E=min(16, E_g), E_g=E_g, topk=topk, H=512, I=128, B=16)
+    inp = make_inputs(s, 980 + E_g)
+    lg = inp["logits"].copy()
+    rng = np.random.default_rng(E_g + 7)
+    g = min(topk + 3, E_g)
+    for t in range(s.T):
+        ids = rng.choice(E_g, size=g, replace=False)
+        if t % 4 == 0:
+            lg[t, ids] = np.float32(9.0)                         # above every other logit
+        elif t % 4 == 1:
+            lg[t, ids] = lg[t].max()                             # tied with the row's maximum
+        elif t % 4 == 2:
+            lg[t] = -np.abs(lg[t]) - np.float32(1.0)             # all below zero, then
+            lg[t, ids] = np.where(np.arange(g) % 2 == 0, np.float32(0.0), np.float32(-0.0))
+        else:
+            lg[t, : max(E_g // 2, topk)] = np.float32(3.0)        # many equal at the threshold
+    inp["logits"] = lg
+    ref = oracle.reference_forward(s, inp, compute_out=False)
+    out, ws = run(s, to_device(s, inp))
+    check_maps(s, maps_np(s, ws), ref)
+
+
 @pytest.mark.parametrize("E_g,topk", [(130, 5), (896, 16)])
 def test_routing_non_finite_logits(E_g, topk):
     """NaN logits rank below -inf (ties by lower id) and a selected NaN gets
