@@ -26,38 +26,57 @@ namespace moe {
 
 // Block of 1024 threads: from per-expert row counts (LDS), write counts,
 // offsets (exclusive scan, offsets[Ep] = R), the chunk table in expert-major
-// order and the chunk count, and the same table for 16-row units (the decode
-// GEMMs' work list). If next_row is given, it receives offsets[e].
-__device__ void block_scan_experts(const int32_t* s_cnt, int Ep, int B, int32_t* counts,
-                                   int32_t* offsets, int32_t* vinfo, int32_t* units16,
-                                   int32_t* counters, int32_t* next_row) {
-  __shared__ int32_t s_wrows[16], s_wchunks[16], s_wunits[16];
+// order and the chunk count, the same table for 16-row units (the decode
+// GEMMs' work list), and the GEMM2 gate: rows R and touched experts U, Dense
+// iff R >= kGateTau * U (or forced); on Dense the per-expert 128-row tile
+// list, experts in order. Gate word: {path, U, R, dense tiles (0 on Split)}.
+// One pass over the experts and one barrier for all of it. If next_row is
+// given, it receives offsets[e]. Every thread of the block must call it.
+__device__ void block_scan_and_gate(const int32_t* s_cnt, int Ep, int B, int force_path,
+                                    int32_t* counts, int32_t* offsets, int32_t* vinfo,
+                                    int32_t* units16, int32_t* counters, int32_t* dense_tiles,
+                                    int32_t* next_row) {
+  __shared__ int32_t s_w[5][16];  // per wave: rows, chunks, units, dense tiles, touched experts
   const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
   const int per = (Ep + 1023) / 1024;
   const int e0 = tid * per;
-  int rows = 0, chunks = 0, units = 0;
+  int rows = 0, chunks = 0, units = 0, tiles = 0, touched = 0;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e < Ep) {
-      rows += s_cnt[e];
-      chunks += (s_cnt[e] + B - 1) / B;
-      units += (s_cnt[e] + 15) / 16;
+      const int n = s_cnt[e];
+      rows += n;
+      chunks += (n + B - 1) / B;
+      units += (n + 15) / 16;
+      tiles += (n + kDenseMT - 1) / kDenseMT;
+      touched += n > 0;
     }
   }
   const int rin = wave_incl_scan(rows), cin = wave_incl_scan(chunks), uin = wave_incl_scan(units);
+  const int tin = wave_incl_scan(tiles), gin = wave_incl_scan(touched);
   if (lane == kWave - 1) {
-    s_wrows[w] = rin;
-    s_wchunks[w] = cin;
-    s_wunits[w] = uin;
+    s_w[0][w] = rin;
+    s_w[1][w] = cin;
+    s_w[2][w] = uin;
+    s_w[3][w] = tin;
+    s_w[4][w] = gin;
   }
   __syncthreads();
-  int rbase = 0, cbase = 0, ubase = 0;
-  for (int j = 0; j < w; ++j) {
-    rbase += s_wrows[j];
-    cbase += s_wchunks[j];
-    ubase += s_wunits[j];
+  int rbase = 0, cbase = 0, ubase = 0, tbase = 0, Rt = 0, Ut = 0, ttot = 0;
+  for (int j = 0; j < 16; ++j) {
+    const bool before = j < w;
+    rbase += before ? s_w[0][j] : 0;
+    cbase += before ? s_w[1][j] : 0;
+    ubase += before ? s_w[2][j] : 0;
+    tbase += before ? s_w[3][j] : 0;
+    Rt += s_w[0][j];
+    ttot += s_w[3][j];
+    Ut += s_w[4][j];
   }
+  int path = (Ut > 0 && Rt >= kGateTau * Ut) ? 1 : 0;
+  if (force_path == 0 || force_path == 1) path = force_path;
   int row = rbase + rin - rows, chunk = cbase + cin - chunks, unit = ubase + uin - units;
+  int tile = tbase + tin - tiles;
   for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= Ep) break;
@@ -81,66 +100,25 @@ __device__ void block_scan_experts(const int32_t* s_cnt, int Ep, int B, int32_t*
       v.w = c;
       reinterpret_cast<int4*>(units16)[unit + c] = v;
     }
+    if (path == 1) {
+      for (int m = 0; m * kDenseMT < n; ++m) {
+        int4 v;
+        v.x = e;
+        v.y = row + m * kDenseMT;
+        v.z = min(kDenseMT, n - m * kDenseMT);
+        v.w = m;
+        reinterpret_cast<int4*>(dense_tiles)[tile + m] = v;
+      }
+    }
     row += n;
     chunk += (n + B - 1) / B;
     unit += (n + 15) / 16;
+    tile += (n + kDenseMT - 1) / kDenseMT;
   }
   if (tid == 1023) {
     offsets[Ep] = row;  // thread 1023 owns the last experts (or none): row = R
     counters[kCtrNumV] = chunk;
     counters[kCtrNumU] = unit;
-  }
-}
-
-// Whole block (1024 threads): rows R and touched experts U from the counts
-// (LDS); Dense iff R >= kGateTau * U (or forced). On Dense it writes the
-// per-expert 128-row tile list, experts in order. Gate word: {path, U, R,
-// dense tiles (0 on Split)}. Every thread of the block must call it.
-__device__ void block_gate(const int32_t* s_cnt, const int32_t* s_off, int Ep, int force_path,
-                           int32_t* counters, int32_t* dense_tiles) {
-  __shared__ int32_t s_u[16], s_r[16], s_t[16];
-  const int tid = threadIdx.x, lane = lane_id(), w = tid >> 6;
-  const int per = (Ep + 1023) / 1024;
-  const int e0 = tid * per;
-  int U = 0, R = 0, nt = 0;
-  for (int i = 0; i < per; ++i) {
-    const int e = e0 + i;
-    const int n = e < Ep ? s_cnt[e] : 0;
-    U += n > 0;
-    R += n;
-    nt += (n + kDenseMT - 1) / kDenseMT;
-  }
-  const int uw = wave_sum(U), rw = wave_sum(R), tin = wave_incl_scan(nt);
-  if (lane == kWave - 1) {
-    s_u[w] = uw;
-    s_r[w] = rw;
-    s_t[w] = tin;
-  }
-  __syncthreads();
-  int Ut = 0, Rt = 0, tbase = 0, ttot = 0;
-  for (int j = 0; j < 16; ++j) {
-    Ut += s_u[j];
-    Rt += s_r[j];
-    tbase += j < w ? s_t[j] : 0;
-    ttot += s_t[j];
-  }
-  int path = (Ut > 0 && Rt >= kGateTau * Ut) ? 1 : 0;
-  if (force_path == 0 || force_path == 1) path = force_path;
-  if (path == 1) {
-    int tile = tbase + tin - nt;
-    for (int i = 0; i < per; ++i) {
-      const int e = e0 + i;
-      if (e >= Ep) break;
-      const int n = s_cnt[e];
-      for (int m = 0; m * kDenseMT < n; ++m) {
-        int4 v;
-        v.x = e;
-        v.y = s_off[e] + m * kDenseMT;
-        v.z = min(kDenseMT, n - m * kDenseMT);
-        v.w = m;
-        reinterpret_cast<int4*>(dense_tiles)[tile++] = v;
-      }
-    }
   }
   if (tid == 0) {
     int4 g;
@@ -230,10 +208,13 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(
   }
   __syncthreads();
   uint16_t* h = s_wcnt + w * Ep;
+  uint64_t mm[kSmallGroups];  // each lane's equal-expert mask per group, kept for the placement
 #pragma unroll
   for (int gi = 0; gi < kSmallGroups; ++gi) {
+    mm[gi] = 0ull;
     if (gi * kWave < rw) {
       const uint64_t match = match_mask(ex[gi] >= 0 ? ex[gi] : Ep, key_bits);
+      mm[gi] = match;
       if (ex[gi] >= 0 && __popcll(match & lt) == 0)
         h[ex[gi]] = static_cast<uint16_t>(h[ex[gi]] + __popcll(match));
       __builtin_amdgcn_wave_barrier();
@@ -252,7 +233,8 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(
     s_cnt[e] = run;
   }
   __syncthreads();
-  block_scan_experts(s_cnt, Ep, B, counts, offsets, vinfo, units16, counters, s_off);
+  block_scan_and_gate(s_cnt, Ep, B, force_path, counts, offsets, vinfo, units16, counters,
+                      dense_tiles, s_off);
   __syncthreads();
   // placement of this wave's slots
 #pragma unroll
@@ -261,7 +243,7 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(
       const int s = s0 + gi * kWave + lane;
       const int e = ex[gi];
       const bool valid = e >= 0;
-      const uint64_t match = match_mask(valid ? e : Ep, key_bits);
+      const uint64_t match = mm[gi];
       const int rank = __popcll(match & lt);
       int base = 0;
       if (valid) base = h[e];
@@ -277,7 +259,6 @@ __global__ __launch_bounds__(1024) void sort_small_kernel(
       __builtin_amdgcn_wave_barrier();
     }
   }
-  block_gate(s_cnt, s_off, Ep, force_path, counters, dense_tiles);
 }
 
 // ------------------------------------------------------------ large shapes
@@ -365,15 +346,13 @@ __global__ __launch_bounds__(1024) void sort_scan_kernel(int Ep, int B, int forc
                                                          int32_t* __restrict__ counters,
                                                          int32_t* __restrict__ dense_tiles) {
   __shared__ int32_t s_cnt[kMaxExperts];
-  __shared__ int32_t s_off[kMaxExperts];
   const int tid = threadIdx.x;
   // 1) the per-expert totals
   for (int e = tid; e < Ep; e += 1024) s_cnt[e] = counts[e];
   __syncthreads();
-  // 2) expert offsets and the chunk table, then the gate
-  block_scan_experts(s_cnt, Ep, B, counts, offsets, vinfo, units16, counters, s_off);
-  __syncthreads();
-  block_gate(s_cnt, s_off, Ep, force_path, counters, dense_tiles);
+  // 2) expert offsets, the chunk tables and the gate
+  block_scan_and_gate(s_cnt, Ep, B, force_path, counts, offsets, vinfo, units16, counters,
+                      dense_tiles, nullptr);
 }
 
 __global__ __launch_bounds__(64) void sort_scatter_kernel(
