@@ -286,7 +286,7 @@ def test_w4a4_config_parity(name):
     if name == "prefill":
         toks = covering_tokens(ref, s.Kp, s.B, 128)
         want = oracle_rows(s, inp, toks)
-    elif name == "decode_ep":  # every token: the oracle finishes it in seconds
+    elif name in ("decode", "decode_ep"):  # every token: the oracle finishes these in seconds
         toks = np.arange(s.T)
         want = oracle.sampled_forward(s, inp, toks)
     else:
@@ -311,7 +311,7 @@ def test_w4a8_config_parity(name):
     if name == "prefill":
         toks = covering_tokens(ref, s.Kp, s.B, 128)
         want = oracle_rows(s, inp, toks)
-    elif name == "decode_ep":  # every token: the oracle finishes it in seconds
+    elif name in ("decode", "decode_ep"):  # every token: the oracle finishes these in seconds
         toks = np.arange(s.T)
         want = oracle.sampled_forward(s, inp, toks)
     else:
