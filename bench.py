@@ -8,9 +8,15 @@ SwiGLU, GEMM2, finalize) on one batch of seeded synthetic inputs that are
 resident in HBM before timing starts. Steps are replayed from captured
 graphs that cycle through enough copies of the weights that no step finds
 the weights it reads in L2 or the 256 MB Infinity Cache (cold weights, as
-the decode page measures). The K timed replays are bracketed by one pair
-of HIP events and a synchronisation on both sides; K more replays, each
-between its own pair of events, give the distribution of single steps.
+the decode page measures). One graph holds CHAIN_STEPS or more steps in
+turn, cycling the copies, as a model's decode graph holds all of its MoE
+layers: a graph launch is paid once per replay, not once per layer. The K
+timed steps (whole replays of that graph, then single-step graphs for the
+remainder) follow SETTLE_S seconds of replays (clocks settle after idle)
+and the W warmup steps, and are bracketed by one pair of HIP events and a
+synchronisation on both sides; more replays, each between its own pair of
+events, give the distribution of the per-step time. The mean of K
+single-step graph replays is reported beside it (`single_step_graph_us`).
 Prints one JSON line.
 
 The headline is the 64-token decode layer (T=64, E=896, top-16, H=3584,
@@ -19,7 +25,7 @@ also carries, under "configs", the same measurement for the EP decode, the
 shared-expert + clamp layer and the 32k-token prefill in bf16 and W4A8
 (skip with --no-sweep). For every workload:
   * layer time: the mean over the K timed steps, and the median, p10 and
-    p90 of single steps;
+    p90 over replays of the per-step time;
   * layer_roofline: the whole layer's algorithmic HBM bytes (decode shapes:
     touched experts' weights and scales, x, out, router logits) or FLOPs
     (prefill: 6 R H I) over the median replay time, against 8 TB/s HBM or
@@ -50,6 +56,12 @@ METRIC = "MoE layer tokens/s and µs/layer; achieved HBM GB/s (decode), MFMA % (
 # the other copies' touched weights between two uses of one copy exceed
 # twice that.
 MALL_FLUSH_BYTES = 512 << 20
+# Steps per replayed graph (at least; a whole number of weight-copy cycles).
+CHAIN_STEPS = 10
+# After idle time (input generation, the CPU baseline) the GPU's clocks and
+# power state take tens of milliseconds of work to settle: every workload
+# replays its graph this long before its warmup steps.
+SETTLE_S = 1.0
 SWEEP = [("decode_ep", "bf16"), ("shared_clamp", "bf16"), ("prefill", "bf16"), ("prefill", "mxfp8"),
          ("prefill", "mxfp4")]
 
@@ -217,6 +229,9 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
     for i in range(1, nsets):
         step(i)
     torch.cuda.synchronize()
+    # one single-step graph per weight copy, and one graph of `chain` steps
+    # that cycles through the copies (whole cycles, so that two uses of a
+    # copy stay nsets - 1 steps apart across replays too)
     graphs = []
     cap = torch.cuda.Stream()
     for i in range(nsets):
@@ -224,37 +239,58 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
         with torch.cuda.graph(g, stream=cap):
             step(i)
         graphs.append(g)
-    torch.cuda.synchronize()
-    for i in range(args.warmup):
-        graphs[i % nsets].replay()
+    chain = nsets * -(-CHAIN_STEPS // nsets)
+    chain_g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(chain_g, stream=cap):
+        for i in range(chain):
+            step(i)
     torch.cuda.synchronize()
 
-    # The K timed steps: graph replays back to back, bracketed by one event
-    # pair and a synchronisation on both sides.
-    log(f"[bench] {name}/{a_dtype}: timing {args.steps} steps ({nsets} weight sets)")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    def run_steps(n):  # n layer steps: whole chain replays, then single-step graphs
+        for _ in range(n // chain):
+            chain_g.replay()
+        for i in range(n % chain):
+            graphs[i % nsets].replay()
+
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    t_end = time.perf_counter() + SETTLE_S
+    while time.perf_counter() < t_end:
+        chain_g.replay()
+        torch.cuda.synchronize()
+    run_steps(max(args.warmup, 1))
     torch.cuda.synchronize()
+
+    # The K timed steps, bracketed by one event pair and a synchronisation on
+    # both sides.
+    log(f"[bench] {name}/{a_dtype}: timing {args.steps} steps ({nsets} weight sets, "
+        f"{chain} steps per graph)")
     t0 = time.perf_counter()
-    e0.record()
-    for i in range(args.steps):
-        graphs[i % nsets].replay()
-    e1.record()
-    torch.cuda.synchronize()
+    ms_per_step = timed(lambda: run_steps(args.steps)) / args.steps
     wall = time.perf_counter() - t0
-    ms_per_step = e0.elapsed_time(e1) / args.steps
-    # The distribution of single steps: another K replays, each between its
-    # own pair of events (the event records add a little to each step).
+    # the same K steps as single-step graph replays (a graph launch per step)
+    single_ms = timed(lambda: [graphs[i % nsets].replay() for i in range(args.steps)]) / args.steps
+    # The distribution of the per-step time: chain replays, each between its
+    # own pair of events.
+    nrep = max(10, args.steps // chain)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps)]
-    for i in range(args.steps):
+          for _ in range(nrep)]
+    for i in range(nrep):
         ev[i][0].record()
-        graphs[i % nsets].replay()
+        chain_g.replay()
         ev[i][1].record()
     torch.cuda.synchronize()
-    rep_us = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    rep_us = [a.elapsed_time(b) * 1e3 / chain for a, b in ev]
     med = pct(rep_us, 50)
     log(f"[bench] {name}/{a_dtype}: {ms_per_step * 1e3:.1f} us/step mean, median {med:.1f} us "
-        f"(wall {wall / args.steps * 1e6:.1f} us/step)")
+        f"(wall {wall / args.steps * 1e6:.1f} us/step; single-step graphs {single_ms * 1e3:.1f} us/step)")
 
     # Stage kernels: the same chain with the library's per-stage HIP events
     # on its stream (eager calls, same weight rotation).
@@ -322,7 +358,7 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
                                           kname))
         kernels[label] = r
     layer = roof(layer_bytes, layer_flops, med, compute_bound)
-    layer["basis"] = "median replay time of the whole layer"
+    layer["basis"] = "median per-step time of the whole layer"
 
     res = {
         "workload": workload_name(s),
@@ -332,13 +368,15 @@ def measure(name: str, a_dtype: str, args, activation=None, cpu_seconds=None) ->
         "tokens_per_s": round(s.T / (ms_per_step * 1e-3), 1),
         "ms_per_step": round(ms_per_step, 4),
         "layer_us": {"median": round(med, 2), "p10": round(pct(rep_us, 10), 2),
-                     "p90": round(pct(rep_us, 90), 2), "mean": round(ms_per_step * 1e3, 2)},
+                     "p90": round(pct(rep_us, 90), 2), "mean": round(ms_per_step * 1e3, 2),
+                     "basis": f"steps run {chain} to a graph"},
+        "single_step_graph_us": round(single_ms * 1e3, 2),
         "stage_us": stages,
         "weight_sets": nsets,
         "layer_roofline": layer,
         "kernels": kernels,
     }
-    del graphs, sets, ws, out, x, logits, shared
+    del graphs, chain_g, sets, ws, out, x, logits, shared
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline and cpu_seconds:
@@ -372,9 +410,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    # The sweep runs first: on a fresh box the first layer calls run slower
-    # (clocks and power state settle over the first second or so of work), and
-    # the headline is measured on a warm GPU like the others.
+    # The sweep runs first, then the headline (each workload settles the
+    # clocks itself before its warmup steps).
     sweep = {}
     if not args.no_sweep:
         for name, adt in SWEEP:
