@@ -21,6 +21,11 @@
 #include "kernels.h"
 #include "gemm2_stream.h"
 
+#include <map>
+#include <mutex>
+#include <utility>
+
+
 namespace moe {
 
 namespace {
@@ -223,21 +228,24 @@ __device__ __forceinline__ uint32_t tlds_off(int rr, int c) {
 // (i < NS) from trs at toff[i] (out of range past the chunk's end, which
 // reads zero), D = 2 steps ahead like the weights, and stores it to the
 // other LDS buffer one step before it is read.
-template <bool NTW, int NS, int NT = 4>
+// NL >= NS: the tile holds NL 16-row sub-tiles (NL = 2, NS = 1 for the
+// K-halves items, whose second sub-tile is the same rows half the K range
+// further on) and the wave reads sub-tiles sub0 .. sub0 + NS - 1.
+template <bool NTW, int NS, int NT = 4, int NL = NS>
 __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32_t (&wofs)[NT],
                                                  const uint8_t* ls, const uint32_t (&lofs)[NT],
                                                  int nkb, __amdgpu_buffer_rsrc_t trs,
-                                                 const uint32_t (&toff)[NS], uint8_t* tl,
-                                                 f32x4_t (&acc)[NS][NT]) {
+                                                 const uint32_t (&toff)[NL], uint8_t* tl,
+                                                 f32x4_t (&acc)[NS][NT], int sub0 = 0) {
   constexpr int D = 2;
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
-  uint4 w[D][NT], tv[D][NS];
+  uint4 w[D][NT], tv[D][NL];
 #pragma unroll
   for (int d = 0; d < D; ++d) {
 #pragma unroll
-    for (int i = 0; i < NS; ++i) tv[d][i] = bld16(trs, toff[i] + d * 256);
+    for (int i = 0; i < NL; ++i) tv[d][i] = bld16(trs, toff[i] + d * 256);
 #pragma unroll
     for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + d * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
@@ -245,17 +253,17 @@ __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32
   wait_all_loads();  // the item's scale rows are in LDS
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < NS; ++i) *reinterpret_cast<uint4*>(tl + tlds_off(lr + 16 * i, lc)) = tv[0][i];
+  for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(tl + tlds_off(lr + 16 * i, lc)) = tv[0][i];
   __syncthreads();
   const int last = nkb - 1;
   auto step = [&](int kb, int d) {
-    const uint8_t* tb = tl + (kb & 1) * tok_lds_step<NS>();
+    const uint8_t* tb = tl + (kb & 1) * tok_lds_step<NL>();
     uint4 xb[NS][4];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xb[s][j] = *reinterpret_cast<const uint4*>(tb + tlds_off(16 * s + r, 4 * g + j));
+        xb[s][j] = *reinterpret_cast<const uint4*>(tb + tlds_off(16 * (s + sub0) + r, 4 * g + j));
     float sc[NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) sc[t] = e8m0_scale_operand(ls[lofs[t] + kb * 4]);
@@ -272,12 +280,12 @@ __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32
     __builtin_amdgcn_sched_barrier(0);
     // step kb + 1's tile (loaded one step ago) into the buffer read in step
     // kb - 1, which every wave left before the last barrier
-    uint8_t* nb = tl + ((kb + 1) & 1) * tok_lds_step<NS>();
+    uint8_t* nb = tl + ((kb + 1) & 1) * tok_lds_step<NL>();
 #pragma unroll
-    for (int i = 0; i < NS; ++i) *reinterpret_cast<uint4*>(nb + tlds_off(lr + 16 * i, lc)) = tv[(d + 1) % D][i];
+    for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(nb + tlds_off(lr + 16 * i, lc)) = tv[(d + 1) % D][i];
     const int nk = min(kb + D, last);
 #pragma unroll
-    for (int i = 0; i < NS; ++i) tv[d][i] = bld16(trs, toff[i] + nk * 256);
+    for (int i = 0; i < NL; ++i) tv[d][i] = bld16(trs, toff[i] + nk * 256);
 #pragma unroll
     for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + nk * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
@@ -313,24 +321,33 @@ inline int ring_depth(int nkb) {
 // TL: token tiles shared through LDS (stream_block_lds, D = 2); the dynamic
 // LDS then starts with the two token buffers. The four waves of a block
 // always hold items of the same chunk (groups is a multiple of 4).
-template <int D, int NSMAX, int TP, bool TL>
+// KH (K halves; TL, one 16-row sub-tile, H a multiple of 512): every
+// (chunk, feature group) pair is two items, the first and the second half
+// of K, taken by neighbouring waves of one block (item 2 * pair + half).
+// Both halves' token rows share the block's LDS tile (two sub-tiles), the
+// second-half wave hands its fp32 sums to the first through LDS after the
+// stream, and the first adds them (first half + second half, always in that
+// order) and stores act. `xi` gives the items each wave takes.
+template <int D, int NSMAX, int TP, bool TL, bool KH = false>
 __device__ __forceinline__ void gemm1_decode_items(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ sorted_slot, int T, int H,
-    int I, int Kp, ActArgs actf, uint16_t* __restrict__ act, uint8_t* lds_scales) {
+    int I, int Kp, ActArgs actf, uint16_t* __restrict__ act, uint8_t* lds_scales, XcdItems xi) {
+  static_assert(!KH || (TL && NSMAX == 1), "K halves share a one-sub-tile LDS token tile");
   constexpr int NT = 2 * TP;
+  constexpr int TNS = KH ? 2 : NSMAX;  // 16-row sub-tiles of the block's token tile
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int groups = I / (16 * TP);
-  const int nitems = counters[ctr] * groups;
+  const int ipc = KH ? 2 * groups : groups;  // items per chunk
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
-  const int nkb = H >> 7;
+  const int nkb = KH ? H >> 8 : H >> 7;  // K steps per item
   const int blk = 16 * TP * static_cast<int>(srow);  // the group's gate (or up) scale rows
   const int blkp = lds_block_bytes(blk);
   uint8_t* tl = lds_scales;
-  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<NSMAX>() : 0) + wave_index() * 2 * blkp;
+  uint8_t* my = lds_scales + (TL ? 2 * tok_lds_step<TNS>() : 0) + wave_index() * 2 * blkp;
   const __amdgpu_buffer_rsrc_t xrs = make_rsrc(x, static_cast<uint32_t>(static_cast<size_t>(T) * H * 2));
   const int lr = static_cast<int>(threadIdx.x) >> 4, lc = static_cast<int>(threadIdx.x) & 15;
   uint32_t wofs[NT], lofs[NT];
@@ -341,10 +358,11 @@ __device__ __forceinline__ void gemm1_decode_items(
     lofs[2 * p] = static_cast<uint32_t>(16 * p * srow);
     lofs[2 * p + 1] = static_cast<uint32_t>(blkp + 16 * p * srow);
   }
-  const XcdItems xi = xcd_items(nitems);
   for (int item = xi.first; item < xi.end; item += xi.step) {
-    const int u = item / groups;
-    const int f0 = (item - u * groups) * 16 * TP;
+    const int u = item / ipc;
+    const int ig = item - u * ipc;
+    const int kh = KH ? ig & 1 : 0;  // which half of K
+    const int f0 = (KH ? ig >> 1 : ig) * 16 * TP;
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * 2 * I + f0;
@@ -401,15 +419,43 @@ __device__ __forceinline__ void gemm1_decode_items(
       const uint32_t b1[1] = {boff[0]};
       const uint32_t t1[1] = {toff[0]};
       auto run = [&](auto ntw) {
-        if constexpr (TL)
+        if constexpr (KH) {
+          // sub-tile 1: the same rows, the second half of K
+          const uint32_t t2[2] = {toff[0], toff[0] + static_cast<uint32_t>(nkb) * 256u};
+          stream_block_lds<decltype(ntw)::value, 1, NT, 2>(
+              wp + static_cast<size_t>(kh) * nkb * kPkBlock, wofs, my + r * srow + g + kh * nkb * 4,
+              lofs, nkb, xrs, t2, tl, acc, kh);
+        } else if constexpr (TL) {
           stream_block_lds<decltype(ntw)::value, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, t1,
                                                         tl, acc);
-        else
+        } else {
           stream_block<decltype(ntw)::value, D, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1,
                                                        acc);
+        }
       };
       if (once) run(BoolC<true>{}); else run(BoolC<false>{});
-      store(acc[0], 0);
+      if constexpr (KH) {
+        // the second half's sums go to the first half's wave through the
+        // token buffers, free after the stream's last barrier
+        float* part = reinterpret_cast<float*>(tl) + (wave_index() >> 1) * NT * 4 * kWave;
+        if (kh) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[(t * 4 + i) * kWave + lane] = acc[0][t][i];
+        }
+        __syncthreads();
+        if (!kh) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[0][t][i] += part[(t * 4 + i) * kWave + lane];
+          store(acc[0], 0);
+        }
+        __syncthreads();  // the next item's first token tile overwrites the sums
+      } else {
+        store(acc[0], 0);
+      }
     } else {
       f32x4_t acc[NSMAX][NT];
 #pragma unroll
@@ -446,14 +492,50 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     const uint8_t* __restrict__ s13, const int32_t* __restrict__ units, int ctr,
     const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ sorted_slot, int T, int H, int I, int Kp, ActArgs actf,
-    uint16_t* __restrict__ act) {
+    uint16_t* __restrict__ act, int res_xcd) {
   extern __shared__ uint8_t lds_scales[];
-  if (counters[ctr] * (I / 32) < kNarrowItemsBelow)
+  const int nch = counters[ctr];
+  if (nch * (I / 32) < kNarrowItemsBelow) {
+    const int P = nch * (I / 16);  // (chunk, 16-feature group) pairs
+    if constexpr (TL && NSMAX == 1) {
+      // A short last round (res_xcd: the blocks one XCD holds at once, from
+      // the host; 0 turns this off): the XCD's first res_xcd blocks take
+      // four pairs each, and the pairs left over go two to a block as K
+      // halves (half as many steps each), so they end sooner after the
+      // first round does. Each pair is computed once either way. At the
+      // Zipf-routed T256 EP decode 4,632 pairs meet 4,096 wave slots; the
+      // 536 left over had run as a late second round of whole items (GEMM1
+      // 43 -> 40 us on MI355X).
+      const int per = (((P + 7) >> 3) + 3) & ~3;  // pairs per XCD, as xcd_items
+      const int left = per - 4 * res_xcd;
+      const int gx = static_cast<int>(gridDim.x) >> 3;
+      if ((H & 511) == 0 && res_xcd > 0 && left > 0 && left <= 2 * res_xcd &&
+          left / 2 <= gx - res_xcd) {
+        const int xcd = static_cast<int>(blockIdx.x) & 7, lb = static_cast<int>(blockIdx.x) >> 3;
+        const int lo = xcd * per, endp = min(lo + per, P);
+        XcdItems xi;
+        xi.step = 1 << 30;  // one item per wave
+        if (lb < res_xcd) {
+          xi.first = lo + 4 * lb + wave_index();
+          xi.end = endp;
+          gemm1_decode_items<D, NSMAX, 1, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot,
+                                              T, H, I, Kp, actf, act, lds_scales, xi);
+        } else {  // K-half items are numbered 2 * pair + half
+          xi.first = 2 * (lo + 4 * res_xcd + 2 * (lb - res_xcd)) + wave_index();
+          xi.end = 2 * endp;
+          gemm1_decode_items<D, NSMAX, 1, TL, true>(x, w13, s13, units, ctr, counters, counts,
+                                                    sorted_slot, T, H, I, Kp, actf, act, lds_scales,
+                                                    xi);
+        }
+        return;
+      }
+    }
     gemm1_decode_items<D, NSMAX, 1, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
-                                        I, Kp, actf, act, lds_scales);
-  else
+                                        I, Kp, actf, act, lds_scales, xcd_items(P));
+  } else {
     gemm1_decode_items<D, NSMAX, 2, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
-                                        I, Kp, actf, act, lds_scales);
+                                        I, Kp, actf, act, lds_scales, xcd_items(nch * (I / 32)));
+  }
 }
 
 // GEMM2 split path, decode shape, long K. Item = (chunk of at most
@@ -855,6 +937,26 @@ static bool token_tiles_in_lds(const GemmArgs& a, int ring) {
   return ring == 2 && static_cast<long>(a.T) * a.Kp >= 2L * a.Ep;
 }
 
+// Blocks of a kernel that one XCD holds at once (an eighth of the chip),
+// from the occupancy the runtime reports for its registers and LDS; 0 if
+// the query fails. Cached per (kernel, LDS bytes).
+static int resident_blocks_per_xcd(const void* kernel, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, size_t>, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto key = std::make_pair(kernel, lds);
+  const auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int per_cu = 0, dev = 0, cus = 0;
+  int res = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kGemmBlock, lds) == hipSuccess &&
+      hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+    res = per_cu * cus / 8;
+  cache.emplace(key, res);
+  return res;
+}
+
 // One block per four items, at most kMaxGrid, a multiple of 8 (xcd_items).
 static int grid_for(long items) {
   long blocks = (items + 3) / 4;
@@ -871,18 +973,25 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
     const bool c32 = a.B == 32;
     const int32_t* units = c32 ? a.vinfo : a.units16;
     const int ctr = c32 ? kCtrNumV : kCtrNumU;
-    // grid for the 16-feature items (the larger count); LDS for the 32-feature ones
-    const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / 16));
     const int d = ring_depth(a.H / 128);
     const bool tl = token_tiles_in_lds(a, d);
+    const bool kh = tl && !c32 && a.H % 512 == 0;  // K-half items possible
+    // grid for the 16-feature items (the larger count)
+    const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / 16));
     // per wave: the gate and up scale blocks of a 32-feature item (H bytes
     // each; a 16-feature item's half-size blocks fit in the same space)
-    const size_t lds = static_cast<size_t>(4) * 2 * lds_block_bytes(a.H) +
-                       (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
+    size_t lds = static_cast<size_t>(4) * 2 * lds_block_bytes(a.H) +
+                 (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
+    if (kh) {  // two token sub-tiles and 16-feature scale blocks
+      const size_t lds_kh = static_cast<size_t>(4) * 2 * lds_block_bytes(a.H / 2) + 2 * tok_lds_step<2>();
+      if (lds_kh > lds) lds = lds_kh;
+    }
 #define MOE_G1D(DD, NS, TL)                                                                       \
   hipLaunchKernelGGL((gemm1_decode_kernel<DD, NS, TL>), dim3(grid), dim3(kGemmBlock), lds, st,      \
                      a.x, a.w13, a.s13, units, ctr, a.counters, a.counts, a.sorted_slot, a.T, a.H,   \
-                     a.I, a.Kp, a.act_fn, a.act)
+                     a.I, a.Kp, a.act_fn, a.act,                                                   \
+                     kh ? resident_blocks_per_xcd(reinterpret_cast<const void*>(                     \
+                              gemm1_decode_kernel<DD, NS, TL>), lds) : 0)
     if (c32) {
       if (tl) MOE_G1D(2, 2, true); else if (d == 2) MOE_G1D(2, 2, false); else MOE_G1D(1, 2, false);
     } else {
