@@ -65,7 +65,18 @@ __global__ __launch_bounds__(kFinBlock) void finalize_kernel(const uint16_t* __r
 #pragma unroll
     for (int u = 0; u < 8; ++u) add(v[u], s_w[k + u]);
   }
-  for (; k < n; ++k) add(ldw16<true>(yc + static_cast<size_t>(s_row[k]) * H), s_w[k]);
+  // the last 1..7 columns: all loads issued before the first add (one load
+  // at a time, each waiting for the one before, had cost the Zipf-routed
+  // EP decode, whose tokens keep 0..16 local columns, about 1 us)
+  if (k < n) {
+    uint4 v[7];
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      if (k + u < n) v[u] = ldw16<true>(yc + static_cast<size_t>(s_row[k + u]) * H);
+#pragma unroll
+    for (int u = 0; u < 7; ++u)
+      if (k + u < n) add(v[u], s_w[k + u]);
+  }
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);
   o.y = pack_bf16x2(acc[2], acc[3]);
