@@ -65,6 +65,11 @@ SMALL = [
     # then the generic tiled dense kernel); decode and 256-row-tile prefill
     LayerShape("i512_decode", T=48, E=16, E_g=16, topk=4, H=512, I=512, B=32),
     LayerShape("i512_prefill_b128", T=1024, E=8, E_g=8, topk=2, H=512, I=512, B=128),
+    # decode GEMM1 with LDS token tiles and 16-feature items whose (chunk,
+    # feature group) pairs overfill one resident round a little (about 4,600
+    # pairs against the 4,096 wave slots of MI355X): the pairs left over run
+    # as K halves joined through LDS
+    LayerShape("gemm1_leftover_halves", T=512, E=64, E_g=64, topk=8, H=512, I=256, B=16),
 ]
 
 
