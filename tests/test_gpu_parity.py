@@ -126,6 +126,23 @@ def test_config_parity(name):
     torch.cuda.empty_cache()
 
 
+# The decode GEMM1's (chunk, 16-feature group) pairs against one resident
+# round (4,096 wave slots on MI355X, 512 pairs per XCD): exactly one round
+# (T = 452), a few pairs left over (456), nearly half a round left over (704,
+# the most that runs as K halves) and just past it (720, the plain mapping);
+# at 456 the last XCD's range is cut short.
+@pytest.mark.parametrize("T", [452, 456, 704, 720])
+def test_gemm1_leftover_edges(T):
+    s = LayerShape(f"gemm1_leftover_T{T}", T=T, E=64, E_g=64, topk=8, H=512, I=256, B=16)
+    say(f"[leftover] T={T}")
+    inp = make_inputs(s, 900 + T)
+    ref = oracle.reference_forward(s, inp)
+    dev = to_device(s, inp)
+    out, ws = run(s, dev, "auto")
+    check_maps(s, maps_np(s, ws, "auto"), ref)
+    check_out(out_np(out), ref["out"], s.name)
+
+
 def test_situ_kimi_decode_shape():
     """The K3.1 TP8 decode shape with its own activation, SiTU(4, 25)."""
     s = CONFIGS["decode"].replace(activation="situ", name="decode_situ")
