@@ -23,8 +23,7 @@
 
 #include <map>
 #include <mutex>
-#include <utility>
-
+#include <tuple>
 
 namespace moe {
 
@@ -939,18 +938,19 @@ static bool token_tiles_in_lds(const GemmArgs& a, int ring) {
 
 // Blocks of a kernel that one XCD holds at once (an eighth of the chip),
 // from the occupancy the runtime reports for its registers and LDS; 0 if
-// the query fails. Cached per (kernel, LDS bytes).
+// a query fails. Cached per (device, kernel, LDS bytes).
 static int resident_blocks_per_xcd(const void* kernel, size_t lds) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
   static std::mutex mu;
-  static std::map<std::pair<const void*, size_t>, int> cache;
+  static std::map<std::tuple<int, const void*, size_t>, int> cache;
   std::lock_guard<std::mutex> lock(mu);
-  const auto key = std::make_pair(kernel, lds);
+  const auto key = std::make_tuple(dev, kernel, lds);
   const auto it = cache.find(key);
   if (it != cache.end()) return it->second;
-  int per_cu = 0, dev = 0, cus = 0;
+  int per_cu = 0, cus = 0;
   int res = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kGemmBlock, lds) == hipSuccess &&
-      hipGetDevice(&dev) == hipSuccess &&
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
     res = per_cu * cus / 8;
   cache.emplace(key, res);
