@@ -29,6 +29,11 @@ namespace moe {
 
 namespace {
 constexpr int kGemmBlock = 256;  // 4 waves, one item each at a time
+// A compile-time int carried as a value (for generic lambdas).
+template <int N>
+struct IntC {
+  static constexpr int value = N;
+};
 // Grid cap of the item-strided decode kernels: one block per four items up
 // to 16 blocks per CU, more than can be resident, so blocks start as others
 // finish and waves end within about one item of each other. Against a cap
@@ -320,13 +325,14 @@ inline int ring_depth(int nkb) {
 // TL: token tiles shared through LDS (stream_block_lds, D = 2); the dynamic
 // LDS then starts with the two token buffers. The four waves of a block
 // always hold items of the same chunk (groups is a multiple of 4).
-// KH (K halves; TL, one 16-row sub-tile, H a multiple of 512): every
-// (chunk, feature group) pair is two items, the first and the second half
-// of K, taken by neighbouring waves of one block (item 2 * pair + half).
-// Both halves' token rows share the block's LDS tile (two sub-tiles), the
-// second-half wave hands its fp32 sums to the first through LDS after the
-// stream, and the first adds them (first half + second half, always in that
-// order) and stores act. `xi` gives the items each wave takes.
+// KH (K halves; H a multiple of 512, and with TL one 16-row sub-tile):
+// every (chunk, feature group) pair is two items, the first and the second
+// half of K, taken by neighbouring waves of one block (item 2 * pair +
+// half). With TL both halves' token rows share the block's LDS tile (two
+// sub-tiles). After the stream the second-half wave hands its fp32 sums to
+// the first through LDS, and the first adds them (first half + second half,
+// always in that order) and stores act. `xi` gives the items each wave
+// takes.
 template <int D, int NSMAX, int TP, bool TL, bool KH = false>
 __device__ __forceinline__ void gemm1_decode_items(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13,
@@ -334,9 +340,9 @@ __device__ __forceinline__ void gemm1_decode_items(
     const int32_t* __restrict__ counters, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ sorted_slot, int T, int H,
     int I, int Kp, ActArgs actf, uint16_t* __restrict__ act, uint8_t* lds_scales, XcdItems xi) {
-  static_assert(!KH || (TL && NSMAX == 1), "K halves share a one-sub-tile LDS token tile");
+  static_assert(!KH || !TL || NSMAX == 1, "K halves share a one-sub-tile LDS token tile");
   constexpr int NT = 2 * TP;
-  constexpr int TNS = KH ? 2 : NSMAX;  // 16-row sub-tiles of the block's token tile
+  constexpr int TNS = (KH && TL) ? 2 : NSMAX;  // 16-row sub-tiles of the block's token tile
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int groups = I / (16 * TP);
@@ -411,14 +417,46 @@ __device__ __forceinline__ void gemm1_decode_items(
         bst8(ars, aoff + p * 32, pk);
       }
     };
+    // K halves: the second-half wave's fp32 sums go to the first-half wave
+    // through LDS (with TL the token buffers, else the second wave's own
+    // scale block, both free after the stream), then the first adds them
+    // (first half + second half) and stores act.
+    auto join_store = [&](auto& acc, auto ns) {
+      constexpr int NS = decltype(ns)::value;
+      float* part = TL ? reinterpret_cast<float*>(tl) + (wave_index() >> 1) * NS * NT * 4 * kWave
+                       : reinterpret_cast<float*>(lds_scales + (wave_index() | 1) * 2 * blkp);
+      if (kh) {
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2)
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[((s2 * NT + t) * 4 + i) * kWave + lane] = acc[s2][t][i];
+      }
+      __syncthreads();
+      if (!kh) {
+#pragma unroll
+        for (int s2 = 0; s2 < NS; ++s2) {
+#pragma unroll
+          for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[s2][t][i] += part[((s2 * NT + t) * 4 + i) * kWave + lane];
+          store(acc[s2], s2);
+        }
+      }
+      __syncthreads();  // the next item overwrites the sums
+    };
+    const size_t kwo = KH ? static_cast<size_t>(kh) * nkb * kPkBlock : 0;  // this half's K offsets
+    const int kso = KH ? kh * nkb * 4 : 0;
+    const uint32_t kto = KH ? static_cast<uint32_t>(kh * nkb) * 256u : 0u;
     if (NSMAX == 1 || nrows <= 16) {
       f32x4_t acc[1][NT];
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[0][t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const uint32_t b1[1] = {boff[0]};
+      const uint32_t b1[1] = {boff[0] + kto};
       const uint32_t t1[1] = {toff[0]};
       auto run = [&](auto ntw) {
-        if constexpr (KH) {
+        if constexpr (KH && TL) {
           // sub-tile 1: the same rows, the second half of K
           const uint32_t t2[2] = {toff[0], toff[0] + static_cast<uint32_t>(nkb) * 256u};
           stream_block_lds<decltype(ntw)::value, 1, NT, 2>(
@@ -428,12 +466,14 @@ __device__ __forceinline__ void gemm1_decode_items(
           stream_block_lds<decltype(ntw)::value, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, t1,
                                                         tl, acc);
         } else {
-          stream_block<decltype(ntw)::value, D, 1, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, b1,
-                                                       acc);
+          stream_block<decltype(ntw)::value, D, 1, NT>(wp + kwo, wofs, my + r * srow + g + kso, lofs, nkb,
+                                                       xrs, b1, acc);
         }
       };
       if (once) run(BoolC<true>{}); else run(BoolC<false>{});
-      if constexpr (KH) {
+      if constexpr (KH && !TL) {
+        join_store(acc, IntC<1>{});
+      } else if constexpr (KH) {
         // the second half's sums go to the first half's wave through the
         // token buffers, free after the stream's last barrier
         float* part = reinterpret_cast<float*>(tl) + (wave_index() >> 1) * NT * 4 * kWave;
@@ -465,13 +505,21 @@ __device__ __forceinline__ void gemm1_decode_items(
         if constexpr (TL)
           stream_block_lds<decltype(ntw)::value, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs,
                                                             toff, tl, acc);
-        else
-          stream_block<decltype(ntw)::value, D, NSMAX, NT>(wp, wofs, my + r * srow + g, lofs, nkb, xrs,
-                                                           boff, acc);
+        else {
+          uint32_t bk[NSMAX];
+#pragma unroll
+          for (int s2 = 0; s2 < NSMAX; ++s2) bk[s2] = boff[s2] + kto;
+          stream_block<decltype(ntw)::value, D, NSMAX, NT>(wp + kwo, wofs, my + r * srow + g + kso, lofs,
+                                                           nkb, xrs, bk, acc);
+        }
       };
       if (once) run(BoolC<true>{}); else run(BoolC<false>{});
+      if constexpr (KH && !TL) {
+        join_store(acc, IntC<NSMAX>{});
+      } else {
 #pragma unroll
-      for (int s = 0; s < NSMAX; ++s) store(acc[s], s);
+        for (int s = 0; s < NSMAX; ++s) store(acc[s], s);
+      }
     }
   }
 }
@@ -494,47 +542,62 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_kernel(
     uint16_t* __restrict__ act, int res_xcd) {
   extern __shared__ uint8_t lds_scales[];
   const int nch = counters[ctr];
-  if (nch * (I / 32) < kNarrowItemsBelow) {
-    const int P = nch * (I / 16);  // (chunk, 16-feature group) pairs
-    if constexpr (TL && NSMAX == 1) {
-      // A short last round (res_xcd: the blocks one XCD holds at once, from
-      // the host; 0 turns this off): the XCD's first res_xcd blocks take
-      // four pairs each, and the pairs left over go two to a block as K
-      // halves (half as many steps each), so they end sooner after the
-      // first round does. Each pair is computed once either way. At the
-      // Zipf-routed T256 EP decode 4,632 pairs meet 4,096 wave slots; the
-      // 536 left over had run as a late second round of whole items (GEMM1
-      // 43 -> 40 us on MI355X).
-      const int per = (((P + 7) >> 3) + 3) & ~3;  // pairs per XCD, as xcd_items
-      const int left = per - 4 * res_xcd;
-      const int gx = static_cast<int>(gridDim.x) >> 3;
-      if ((H & 511) == 0 && res_xcd > 0 && left > 0 && left <= 2 * res_xcd &&
-          left / 2 <= gx - res_xcd) {
-        const int xcd = static_cast<int>(blockIdx.x) & 7, lb = static_cast<int>(blockIdx.x) >> 3;
-        const int lo = xcd * per, endp = min(lo + per, P);
-        XcdItems xi;
-        xi.step = 1 << 30;  // one item per wave
-        if (lb < res_xcd) {
-          xi.first = lo + 4 * lb + wave_index();
-          xi.end = endp;
+  const bool narrow = nch * (I / 32) < kNarrowItemsBelow;
+  const int P = nch * (narrow ? I / 16 : I / 32);  // (chunk, feature group) pairs
+  // A partial last round (res_xcd: the blocks one XCD holds at once, from
+  // the host; 0 turns this off): the blocks of whole rounds take four pairs
+  // each, and the pairs left over go two to a block as K halves (half as
+  // many steps each), so the last items end closer together. Each pair is
+  // computed once either way. Zipf-routed T256 EP decode: 4,632 pairs on
+  // 4,096 wave slots, GEMM1 43 -> 40 us; T64 decode: 7,284 pairs on 2,048
+  // slots, GEMM1 142 -> 138 us (MI355X).
+  if ((H & 511) == 0 && res_xcd > 0) {
+    const int per = (((P + 7) >> 3) + 3) & ~3;  // pairs per XCD, as xcd_items
+    const int nfull = ((per >> 2) / res_xcd) * res_xcd;  // blocks of whole rounds
+    const int left = per - 4 * nfull;
+    const int gx = static_cast<int>(gridDim.x) >> 3;
+    const int srow = H >> 5;
+    // without TL the sums pass through the second wave's scale block
+    const bool fits = TL ? (NSMAX == 1 && narrow)
+                         : 2 * lds_block_bytes(16 * (narrow ? 1 : 2) * srow) >=
+                               NSMAX * 2 * (narrow ? 1 : 2) * 4 * kWave * 4;
+    if (fits && nfull > 0 && left > 0 && left / 2 <= gx - nfull) {
+      const int xcd = static_cast<int>(blockIdx.x) & 7, lb = static_cast<int>(blockIdx.x) >> 3;
+      const int lo = xcd * per, endp = min(lo + per, P);
+      XcdItems xi;
+      xi.step = 1 << 30;  // one item per wave
+      const bool whole = lb < nfull;
+      if (whole) {
+        xi.first = lo + 4 * lb + wave_index();
+        xi.end = endp;
+      } else {  // K-half items are numbered 2 * pair + half
+        xi.first = 2 * (lo + 4 * nfull + 2 * (lb - nfull)) + wave_index();
+        xi.end = 2 * endp;
+      }
+      if (narrow) {
+        if (whole)
           gemm1_decode_items<D, NSMAX, 1, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot,
                                               T, H, I, Kp, actf, act, lds_scales, xi);
-        } else {  // K-half items are numbered 2 * pair + half
-          xi.first = 2 * (lo + 4 * res_xcd + 2 * (lb - res_xcd)) + wave_index();
-          xi.end = 2 * endp;
+        else if constexpr (!TL || NSMAX == 1)
           gemm1_decode_items<D, NSMAX, 1, TL, true>(x, w13, s13, units, ctr, counters, counts,
-                                                    sorted_slot, T, H, I, Kp, actf, act, lds_scales,
-                                                    xi);
-        }
-        return;
+                                                    sorted_slot, T, H, I, Kp, actf, act, lds_scales, xi);
+      } else if constexpr (!TL) {
+        if (whole)
+          gemm1_decode_items<D, NSMAX, 2, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot,
+                                              T, H, I, Kp, actf, act, lds_scales, xi);
+        else
+          gemm1_decode_items<D, NSMAX, 2, TL, true>(x, w13, s13, units, ctr, counters, counts,
+                                                    sorted_slot, T, H, I, Kp, actf, act, lds_scales, xi);
       }
+      return;
     }
+  }
+  if (narrow)
     gemm1_decode_items<D, NSMAX, 1, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
                                         I, Kp, actf, act, lds_scales, xcd_items(P));
-  } else {
+  else
     gemm1_decode_items<D, NSMAX, 2, TL>(x, w13, s13, units, ctr, counters, counts, sorted_slot, T, H,
-                                        I, Kp, actf, act, lds_scales, xcd_items(nch * (I / 32)));
-  }
+                                        I, Kp, actf, act, lds_scales, xcd_items(P));
 }
 
 // GEMM2 split path, decode shape, long K. Item = (chunk of at most
@@ -975,14 +1038,14 @@ hipError_t launch_gemm1(const GemmArgs& a, hipStream_t st) {
     const int ctr = c32 ? kCtrNumV : kCtrNumU;
     const int d = ring_depth(a.H / 128);
     const bool tl = token_tiles_in_lds(a, d);
-    const bool kh = tl && !c32 && a.H % 512 == 0;  // K-half items possible
+    const bool kh = a.H % 512 == 0;  // K-half items possible
     // grid for the 16-feature items (the larger count)
     const int grid = grid_for(static_cast<long>(c32 ? a.kmax_v : a.max_units16) * (a.I / 16));
     // per wave: the gate and up scale blocks of a 32-feature item (H bytes
     // each; a 16-feature item's half-size blocks fit in the same space)
     size_t lds = static_cast<size_t>(4) * 2 * lds_block_bytes(a.H) +
                  (tl ? 2 * (c32 ? tok_lds_step<2>() : tok_lds_step<1>()) : 0);
-    if (kh) {  // two token sub-tiles and 16-feature scale blocks
+    if (kh && tl && !c32) {  // two token sub-tiles and 16-feature scale blocks
       const size_t lds_kh = static_cast<size_t>(4) * 2 * lds_block_bytes(a.H / 2) + 2 * tok_lds_step<2>();
       if (lds_kh > lds) lds = lds_kh;
     }

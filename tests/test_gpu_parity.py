@@ -70,6 +70,10 @@ SMALL = [
     # pairs against the 4,096 wave slots of MI355X): the pairs left over run
     # as K halves joined through LDS
     LayerShape("gemm1_leftover_halves", T=512, E=64, E_g=64, topk=8, H=512, I=256, B=16),
+    # the same with per-wave token loads (about one row per expert): about
+    # 5,150 pairs against one round of 3,072 wave slots, the second round
+    # run as K halves whose sums meet in the second wave's scale block
+    LayerShape("gemm1_leftover_sparse", T=64, E=512, E_g=512, topk=8, H=512, I=256, B=16),
 ]
 
 
