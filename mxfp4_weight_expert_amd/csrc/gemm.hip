@@ -897,20 +897,23 @@ __device__ __forceinline__ void quant_store_act(const float (&a)[8], __amdgpu_bu
 // Items and LDS as in gemm1_decode_kernel; the 32-feature group of an item
 // is exactly one MX block of act. TL: token tiles through LDS
 // (stream_block_a8_lds, D = 2), after the scale blocks in the dynamic LDS.
-template <int D, bool TL, bool A4>
-__global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
+// KH (per-wave token loads only): K halves as in gemm1_decode_items; the
+// second-half wave's sums reach the first through its own scale block.
+template <int D, bool TL, bool A4, bool KH = false>
+__device__ __forceinline__ void gemm1_decode_a8_items(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
     const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
     const int32_t* __restrict__ units, const int32_t* __restrict__ counters,
     const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slot, int T, int H,
-    int I, int Kp, ActArgs actf, uint8_t* __restrict__ actq, uint8_t* __restrict__ acts) {
-  extern __shared__ uint8_t lds_scales[];
+    int I, int Kp, ActArgs actf, uint8_t* __restrict__ actq, uint8_t* __restrict__ acts,
+    uint8_t* lds_scales, XcdItems xi) {
+  static_assert(!KH || !TL, "K halves of the MX stream use per-wave token loads");
   const int lane = lane_id();
   const int r = lane & 15, g = lane >> 4;
   const int groups = I >> 5;
-  const int nitems = counters[kCtrNumU] * groups;
+  const int ipc = KH ? 2 * groups : groups;  // items per unit
   const size_t wrow = static_cast<size_t>(H) >> 1, srow = static_cast<size_t>(H) >> 5;
-  const int nkb = H >> 7;
+  const int nkb = KH ? H >> 8 : H >> 7;  // K steps per item
   const int blk = 32 * static_cast<int>(srow);
   const int blkp = lds_block_bytes(blk);
   uint8_t* my = lds_scales + wave_index() * 2 * blkp;
@@ -924,10 +927,11 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
   const uint32_t srow_a = static_cast<uint32_t>(I) >> 5;
   uint8_t* tl = lds_scales + 4 * 2 * blkp;
   const int tt = static_cast<int>(threadIdx.x);
-  const XcdItems xi = xcd_items(nitems);
   for (int item = xi.first; item < xi.end; item += xi.step) {
-    const int u = item / groups;
-    const int f0 = (item - u * groups) * 32;
+    const int u = item / ipc;
+    const int ig = item - u * ipc;
+    const int kh = KH ? ig & 1 : 0;  // which half of K
+    const int f0 = (KH ? ig >> 1 : ig) * 32;
     const int4 ui = reinterpret_cast<const int4*>(units)[u];
     const int e = ui.x, r0 = ui.y, nrows = ui.z;
     const size_t row0 = static_cast<size_t>(e) * 2 * I + f0;
@@ -964,12 +968,35 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
         stream_block_a8_lds<decltype(ntw)::value, A4>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, toff,
                                                       srs, tsoff, tl, acc);
       } else {
-        stream_block_a8<decltype(ntw)::value, D, A4>(wp, wofs, my + r * srow + g, lofs, nkb, xrs, xoff,
-                                                     srs, soff, acc);
+        const int kk = kh * nkb;  // this half's first K step
+        stream_block_a8<decltype(ntw)::value, D, A4>(
+            wp + static_cast<size_t>(kk) * kPkBlock, wofs, my + r * srow + g + kk * 4, lofs, nkb, xrs,
+            xoff + static_cast<uint32_t>(kk) * tok_step_bytes<A4>(), srs,
+            soff + static_cast<uint32_t>(kk) * 4u, acc);
       }
     };
     // weights read once in this call (the expert's only unit): non-temporal
     if (counts[e] <= 16) run(BoolC<true>{}); else run(BoolC<false>{});
+    if constexpr (KH) {
+      // the second half's sums to the first-half wave, through the second
+      // wave's scale block (free after its stream); first half + second half
+      float* part = reinterpret_cast<float*>(lds_scales + (wave_index() | 1) * 2 * blkp);
+      if (kh) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) part[(t * 4 + i) * kWave + lane] = acc[t][i];
+      }
+      __syncthreads();
+      if (!kh) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][i] += part[(t * 4 + i) * kWave + lane];
+      }
+      __syncthreads();  // the next item's scale copy overwrites the sums
+      if (kh) continue;
+    }
     // lane (r, g): features f0 + 16h + 4g + v of token row r0 + r
     float a[8];
 #pragma unroll
@@ -987,6 +1014,53 @@ __global__ __launch_bounds__(kGemmBlock) void gemm1_decode_a8_kernel(
     quant_store_act<A4>(a, qrs, o0, o0 + (A4 ? 8 : 16), ars,
                         g == 0 ? static_cast<uint32_t>(r) * srow_a + (f0 >> 5) : kNoRow);
   }
+}
+
+// Four blocks per CU (four waves per SIMD) for the per-wave token path at
+// ring depth <= 2: its K-half instance would otherwise take the kernel to
+// 133 registers a lane, one wave per SIMD fewer.
+template <int D, bool TL, bool A4>
+__global__ __launch_bounds__(kGemmBlock, (TL || D > 2) ? 1 : 4) void gemm1_decode_a8_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs,
+    const uint8_t* __restrict__ w13, const uint8_t* __restrict__ s13,
+    const int32_t* __restrict__ units, const int32_t* __restrict__ counters,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ sorted_slot, int T, int H,
+    int I, int Kp, ActArgs actf, uint8_t* __restrict__ actq, uint8_t* __restrict__ acts,
+    int res_xcd) {
+  extern __shared__ uint8_t lds_scales[];
+  const int P = counters[kCtrNumU] * (I >> 5);  // (unit, 32-feature group) pairs
+  if constexpr (!TL) {
+    // a partial last round as K halves, as in gemm1_decode_kernel (the sums
+    // of 16 floats a lane fit the second wave's two scale blocks)
+    if ((H & 511) == 0 && (H >> 8) % D == 0 && res_xcd > 0 &&
+        2 * lds_block_bytes(H) >= 16 * kWave * 4) {
+      const int per = (((P + 7) >> 3) + 3) & ~3;  // pairs per XCD, as xcd_items
+      const int nfull = ((per >> 2) / res_xcd) * res_xcd;  // blocks of whole rounds
+      const int left = per - 4 * nfull;
+      const int gx = static_cast<int>(gridDim.x) >> 3;
+      if (nfull > 0 && left > 0 && left / 2 <= gx - nfull) {
+        const int xcd = static_cast<int>(blockIdx.x) & 7, lb = static_cast<int>(blockIdx.x) >> 3;
+        const int lo = xcd * per, endp = min(lo + per, P);
+        XcdItems xi;
+        xi.step = 1 << 30;  // one item per wave
+        if (lb < nfull) {
+          xi.first = lo + 4 * lb + wave_index();
+          xi.end = endp;
+          gemm1_decode_a8_items<D, TL, A4>(xq, xs, w13, s13, units, counters, counts, sorted_slot, T,
+                                           H, I, Kp, actf, actq, acts, lds_scales, xi);
+        } else {  // K-half items are numbered 2 * pair + half
+          xi.first = 2 * (lo + 4 * nfull + 2 * (lb - nfull)) + wave_index();
+          xi.end = 2 * endp;
+          gemm1_decode_a8_items<D, TL, A4, true>(xq, xs, w13, s13, units, counters, counts,
+                                                 sorted_slot, T, H, I, Kp, actf, actq, acts,
+                                                 lds_scales, xi);
+        }
+        return;
+      }
+    }
+  }
+  gemm1_decode_a8_items<D, TL, A4>(xq, xs, w13, s13, units, counters, counts, sorted_slot, T, H, I,
+                                   Kp, actf, actq, acts, lds_scales, xcd_items(P));
 }
 
 // Token tiles through LDS (stream_block_lds) pay off once chunks carry
@@ -1108,7 +1182,11 @@ static hipError_t launch_gemm1_mx(const GemmArgs& a, hipStream_t st) {
 #define MOE_G1A(DD, TL)                                                                          \
   hipLaunchKernelGGL((gemm1_decode_a8_kernel<DD, TL, A4>), dim3(grid), dim3(kGemmBlock), lds, st, \
                      a.xq, a.xs, a.w13, a.s13, a.units16, a.counters, a.counts, a.sorted_slot, a.T,  \
-                     a.H, a.I, a.Kp, a.act_fn, actq, a.act_scales)
+                     a.H, a.I, a.Kp, a.act_fn, actq, a.act_scales,                                \
+                     (!(TL) && a.H % 512 == 0)                                                    \
+                         ? resident_blocks_per_xcd(                                                \
+                               reinterpret_cast<const void*>(gemm1_decode_a8_kernel<DD, TL, A4>), lds) \
+                         : 0)
   if (tl) {
     MOE_G1A(2, true);
   } else {
