@@ -22,8 +22,8 @@ Prints one JSON line.
 The headline is the 64-token decode layer (T=64, E=896, top-16, H=3584,
 I=384, BlockN=32): `value` is its tokens/s over the K timed steps. The line
 also carries, under "configs", the same measurement for the EP decode, the
-shared-expert + clamp layer and the 32k-token prefill in bf16 and W4A8
-(skip with --no-sweep). For every workload:
+64-token decode in W4A8, the shared-expert + clamp layer and the 32k-token
+prefill in bf16, W4A8 and W4A4 (skip with --no-sweep). For every workload:
   * layer time: the mean over the K timed steps, and the median, p10 and
     p90 over replays of the per-step time;
   * layer_roofline: the whole layer's algorithmic HBM bytes (decode shapes:
@@ -62,8 +62,8 @@ CHAIN_STEPS = 10
 # power state take tens of milliseconds of work to settle: every workload
 # replays its graph this long before its warmup steps.
 SETTLE_S = 1.0
-SWEEP = [("decode_ep", "bf16"), ("shared_clamp", "bf16"), ("prefill", "bf16"), ("prefill", "mxfp8"),
-         ("prefill", "mxfp4")]
+SWEEP = [("decode_ep", "bf16"), ("decode", "mxfp8"), ("shared_clamp", "bf16"), ("prefill", "bf16"),
+         ("prefill", "mxfp8"), ("prefill", "mxfp4")]
 
 
 def parse():
