@@ -43,6 +43,12 @@ INV = [
     LayerShape("inv_prefill_w4a8", T=512, E=8, E_g=8, topk=2, H=512, I=128, B=128, a_dtype="mxfp8"),
     LayerShape("inv_decode_w4a4", T=64, E=64, E_g=64, topk=8, H=512, I=256, B=32, a_dtype="mxfp4"),
     LayerShape("inv_prefill_w4a4", T=512, E=8, E_g=8, topk=2, H=512, I=384, B=128, a_dtype="mxfp4"),
+    # decode GEMM1 pairs past one resident round run as K halves: LDS token
+    # tiles, per-wave tokens, and the W4A8 kernel
+    LayerShape("inv_leftover_tl", T=512, E=64, E_g=64, topk=8, H=512, I=256, B=16),
+    LayerShape("inv_leftover_sparse", T=64, E=512, E_g=512, topk=8, H=512, I=256, B=16),
+    LayerShape("inv_leftover_w4a8", T=64, E=1024, E_g=1024, topk=16, H=2048, I=256, B=16,
+               a_dtype="mxfp8"),
 ]
 FORCES = ["auto", "split", "dense"]
 SEED = 4242
