@@ -42,8 +42,11 @@ constexpr uint32_t tok_step_bytes() {
 }
 
 // bf16 act. The work unit is a 16-row tile of one 16-row unit's output over
-// the full K. Waves own equal contiguous ranges of the unit-major tile list,
-// so the last wave ends at most one tile after the first. Within the part of
+// the full K. Waves own equal contiguous ranges of the unit-major tile list
+// in whole batches of kStreamAhead tiles, so ranges differ by at most one
+// batch. A batch's outputs are regrouped across lanes and leave as two
+// 16-byte stores a lane, aligned 64-byte pieces of 16 Y rows (four 8-byte
+// stores of 32-byte pieces were 1-3 us slower a call). Within the part of
 // its range that falls in one unit, a wave keeps the unit's activation
 // fragments in registers and streams tiles through a ring kStreamAhead tiles
 // deep; each tile's scales come in with one load of exactly the row's I/32
@@ -51,10 +54,31 @@ constexpr uint32_t tok_step_bytes() {
 // recompute the last tile and their stores fall outside the unit's output
 // buffer, so the hardware drops them (no branches in the stream). The caller
 // checks the gate word: this runs only on the Split path.
-#ifndef MOE_STREAM_AHEAD
-#define MOE_STREAM_AHEAD 4
-#endif
-constexpr int kStreamAhead = MOE_STREAM_AHEAD;
+constexpr int kStreamAhead = 4;  // also the Y store regroup's batch (below)
+
+// A batch's four bf16 output pieces, regrouped for whole 64-byte row stores.
+// Before: lane r + 16 g holds, in piece a, features 16 a + 4 g .. + 3 of row r
+// (the 16x16 MFMA output layout, one tile per piece). After: lane r + 16 h
+// holds features 32 k + 8 h .. + 7 of row r in pieces 2 k and 2 k + 1. As a
+// 4 x 4 array over (lane group bits g1 g0, piece bits a1 a0) that moves a0 to
+// g1, g1 to g0 and g0 to a0: an exchange of g1 with a0 (lanes 32 apart) and
+// then one of g0 with a0 (lanes 16 apart).
+__device__ __forceinline__ void y_regroup(uint2 (&p)[4]) {
+#pragma unroll
+  for (int a = 0; a < 4; a += 2) {
+    auto x = __builtin_amdgcn_permlane32_swap(p[a].x, p[a + 1].x, false, false);
+    auto y = __builtin_amdgcn_permlane32_swap(p[a].y, p[a + 1].y, false, false);
+    p[a].x = x[0]; p[a + 1].x = x[1];
+    p[a].y = y[0]; p[a + 1].y = y[1];
+  }
+#pragma unroll
+  for (int a = 0; a < 4; a += 2) {
+    auto x = __builtin_amdgcn_permlane16_swap(p[a].x, p[a + 1].x, false, false);
+    auto y = __builtin_amdgcn_permlane16_swap(p[a].y, p[a + 1].y, false, false);
+    p[a].x = x[0]; p[a + 1].x = x[1];
+    p[a].y = y[0]; p[a + 1].y = y[1];
+  }
+}
 
 template <int NKB>
 __device__ __forceinline__ void gemm2_stream_body(
@@ -68,8 +92,11 @@ __device__ __forceinline__ void gemm2_stream_body(
   const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
   const int64_t wid = xcd_wave_id();
-  int64_t t = total * wid / nwaves;
-  const int64_t t_end = total * (wid + 1) / nwaves;
+  // ranges start on whole batches (H % 512 == 0 makes a unit's tile count a
+  // multiple of the batch), so a batch's four tiles are 128 aligned bytes of
+  // each Y row
+  int64_t t = total / kStreamAhead * wid / nwaves * kStreamAhead;
+  const int64_t t_end = total / kStreamAhead * (wid + 1) / nwaves * kStreamAhead;
   const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
   const uint32_t tstride = static_cast<uint32_t>(16 * wrow);
   const uint32_t sstride = static_cast<uint32_t>(16 * srow);
@@ -132,9 +159,11 @@ __device__ __forceinline__ void gemm2_stream_body(
           res[a].y = pack_bf16x2(acc[2], acc[3]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        y_regroup(res);
   #pragma unroll
-        for (int a = 0; a < kStreamAhead; ++a)
-          bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
+        for (int k = 0; k < 2; ++k)
+          bst16(yrs, i0 + 2 * k + (g >> 1) < nt ? yrow + 8 * g + i0 * 32 + 64 * k : 0xfffffff0u,
+                uint4{res[2 * k].x, res[2 * k].y, res[2 * k + 1].x, res[2 * k + 1].y});
       }
     };
     if (counts[e] <= 16) seg(BoolC<true>{}); else seg(BoolC<false>{});
@@ -157,8 +186,11 @@ __device__ __forceinline__ void gemm2_stream_mx_body(
   const int64_t total = static_cast<int64_t>(counters[kCtrNumU]) * tpu;
   const int64_t nwaves = static_cast<int64_t>(gridDim.x) * 4;
   const int64_t wid = xcd_wave_id();
-  int64_t t = total * wid / nwaves;
-  const int64_t t_end = total * (wid + 1) / nwaves;
+  // ranges start on whole batches (H % 512 == 0 makes a unit's tile count a
+  // multiple of the batch), so a batch's four tiles are 128 aligned bytes of
+  // each Y row
+  int64_t t = total / kStreamAhead * wid / nwaves * kStreamAhead;
+  const int64_t t_end = total / kStreamAhead * (wid + 1) / nwaves * kStreamAhead;
   const size_t wrow = static_cast<size_t>(I) >> 1, srow = static_cast<size_t>(I) >> 5;
   const uint32_t tstride = static_cast<uint32_t>(16 * wrow);
   const uint32_t sstride = static_cast<uint32_t>(16 * srow);
@@ -223,9 +255,11 @@ __device__ __forceinline__ void gemm2_stream_mx_body(
           res[a].y = pack_bf16x2(acc[2], acc[3]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        y_regroup(res);
   #pragma unroll
-        for (int a = 0; a < kStreamAhead; ++a)
-          bst8(yrs, i0 + a < nt ? yrow + (i0 + a) * 32 : 0xfffffff0u, res[a]);
+        for (int k = 0; k < 2; ++k)
+          bst16(yrs, i0 + 2 * k + (g >> 1) < nt ? yrow + 8 * g + i0 * 32 + 64 * k : 0xfffffff0u,
+                uint4{res[2 * k].x, res[2 * k].y, res[2 * k + 1].x, res[2 * k + 1].y});
       }
     };
     if (counts[e] <= 16) seg(BoolC<true>{}); else seg(BoolC<false>{});
