@@ -651,15 +651,20 @@ __global__ __launch_bounds__(kGemmBlock) void gemm2_split_kernel(
     uint32_t toff[NSMAX];  // this thread's rows of the block's act tile (zero past nrows)
 #pragma unroll
     for (int i = 0; i < NSMAX; ++i) toff[i] = static_cast<uint32_t>(lr + 16 * i) * I * 2 + lc * 16;
+    // the four 16-feature tiles regrouped across lanes: two 16-byte stores a
+    // lane, aligned 64-byte pieces of 16 Y rows (h0 is a multiple of 64)
     auto store = [&](const f32x4_t (&acc)[4], int s) {
-      const uint32_t yoff = static_cast<uint32_t>(16 * s + r) * H * 2 + (h0 + g * 4) * 2;
+      uint2 pk[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        uint2 pk;
-        pk.x = pack_bf16x2(acc[t][0], acc[t][1]);
-        pk.y = pack_bf16x2(acc[t][2], acc[t][3]);
-        bst8(yrs, yoff + t * 32, pk);
+        pk[t].x = pack_bf16x2(acc[t][0], acc[t][1]);
+        pk[t].y = pack_bf16x2(acc[t][2], acc[t][3]);
       }
+      y_regroup(pk);
+      const uint32_t yoff = static_cast<uint32_t>(16 * s + r) * H * 2 + h0 * 2 + 16 * g;
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+        bst16(yrs, yoff + 64 * k, uint4{pk[2 * k].x, pk[2 * k].y, pk[2 * k + 1].x, pk[2 * k + 1].y});
     };
     if (NSMAX == 1 || nrows <= 16) {
       f32x4_t acc[1][4];

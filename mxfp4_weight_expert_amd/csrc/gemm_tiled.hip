@@ -439,17 +439,20 @@ __global__ __launch_bounds__(kTiledThreads, 2) void gemm_tiled_kernel(
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
           const f32x16_t& c = acc[m][n];
+          uint2 pk[2];
 #pragma unroll
           for (int b4 = 0; b4 < 2; ++b4) {
-            uint2 pk;
-            pk.x = pack_bf16x2(act_apply(c[4 * b4 + 0], c[4 * b4 + 8], actf),
-                               act_apply(c[4 * b4 + 1], c[4 * b4 + 9], actf));
-            pk.y = pack_bf16x2(act_apply(c[4 * b4 + 2], c[4 * b4 + 10], actf),
-                               act_apply(c[4 * b4 + 3], c[4 * b4 + 11], actf));
-            const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * I * 2 +
-                                 (fbase + 8 * b4 + 4 * h) * 2;
-            bst8(ors, off, pk);
+            pk[b4].x = pack_bf16x2(act_apply(c[4 * b4 + 0], c[4 * b4 + 8], actf),
+                                   act_apply(c[4 * b4 + 1], c[4 * b4 + 9], actf));
+            pk[b4].y = pack_bf16x2(act_apply(c[4 * b4 + 2], c[4 * b4 + 10], actf),
+                                   act_apply(c[4 * b4 + 3], c[4 * b4 + 11], actf));
           }
+          // lane (r, h) holds features 8 b4 + 4 h .. + 3 in piece b4; one
+          // exchange of h with b4 leaves it features 8 h .. + 7 (16 bytes)
+          auto x = __builtin_amdgcn_permlane32_swap(pk[0].x, pk[1].x, false, false);
+          auto y = __builtin_amdgcn_permlane32_swap(pk[0].y, pk[1].y, false, false);
+          const uint32_t off = static_cast<uint32_t>(wm * 64 + n * 32 + r) * I * 2 + (fbase + 8 * h) * 2;
+          bst16(ors, off, uint4{x[0], y[0], x[1], y[1]});
         }
       }
     } else {
