@@ -261,6 +261,12 @@ __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32
   __syncthreads();
   const int last = nkb - 1;
   auto step = [&](int kb, int d) {
+    // step kb + 2's token rows, issued first: tv[d] held step kb's rows,
+    // which went to LDS in step kb - 1
+    const int nk = min(kb + D, last);
+#pragma unroll
+    for (int i = 0; i < NL; ++i) tv[d][i] = bld16(trs, toff[i] + nk * 256);
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* tb = tl + (kb & 1) * tok_lds_step<NL>();
     uint4 xb[NS][4];
 #pragma unroll
@@ -287,9 +293,6 @@ __device__ __forceinline__ void stream_block_lds(const uint8_t* wp, const uint32
     uint8_t* nb = tl + ((kb + 1) & 1) * tok_lds_step<NL>();
 #pragma unroll
     for (int i = 0; i < NL; ++i) *reinterpret_cast<uint4*>(nb + tlds_off(lr + 16 * i, lc)) = tv[(d + 1) % D][i];
-    const int nk = min(kb + D, last);
-#pragma unroll
-    for (int i = 0; i < NL; ++i) tv[d][i] = bld16(trs, toff[i] + nk * 256);
 #pragma unroll
     for (int t = 0; t < NT; ++t) w[d][t] = ldw16<NTW>(wp + wofs[t] + nk * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
