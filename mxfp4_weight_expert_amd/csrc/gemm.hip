@@ -846,6 +846,12 @@ __device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uin
   __syncthreads();
   const int last = nkb - 1;
   auto step = [&](int kb, int d) {
+    // step kb + 2's token codes and scales, issued first: slot d held step
+    // kb's, which went to LDS in step kb - 1
+    const int nk = min(kb + D, last);
+    tv[d] = bld16(xrs, toff + nk * XS);
+    ts[d] = bld4(srs, tsoff + nk * 4);
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t* tb = tl + (kb & 1) * STEP;
     uint4 x0, x1;
     x0 = *reinterpret_cast<const uint4*>(tb + tmx_lds_off<A4>(r, g));
@@ -855,9 +861,6 @@ __device__ __forceinline__ void stream_block_a8_lds(const uint8_t* wp, const uin
     for (int q = 0; q < 4; ++q) acc[q] = mfma_f4xa<A4>(w[d][q], ls[lofs[q] + kb * 4], x0, x1, xsb, acc[q]);
     __builtin_amdgcn_sched_barrier(0);
     put(tl + ((kb + 1) & 1) * STEP, (d + 1) % D);
-    const int nk = min(kb + D, last);
-    tv[d] = bld16(xrs, toff + nk * XS);
-    ts[d] = bld4(srs, tsoff + nk * 4);
 #pragma unroll
     for (int q = 0; q < 4; ++q) w[d][q] = ldw16<NTW>(wp + wofs[q] + nk * kPkBlock);
     __builtin_amdgcn_sched_barrier(0);
